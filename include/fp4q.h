@@ -1,0 +1,203 @@
+/*
+ * fp4q.h -- C ABI of the MI355X (gfx950) microscaling FP4 quantization library.
+ *
+ * The library quantizes row-major matrices to 4-bit E2M1 codes in blocks of b
+ * consecutive elements along each row, each block sharing one 8-bit scale:
+ *
+ *   MXFP4  b = 32, E8M0 power-of-two scale (a shared 8-bit exponent).
+ *          Source: "Diagnosing FP4 inference: a layer-wise and block-wise
+ *          sensitivity analysis of NVFP4 and MXFP4", technical summary section 2
+ *          (32-element blocks, shared 8-bit exponent, E2M1 elements);
+ *          "Bridging the Gap Between Promise and Performance for Microscaling
+ *          FP4 Quantization", Sommario tecnico section 1 (E8M0 power-of-two
+ *          scales, round-to-nearest).
+ *   NVFP4  b = 16, unsigned E4M3 (UE4M3) scale under an FP32 per-tensor scale g.
+ *          Same pages: 16-element blocks, dynamic "max" scaling, E4M3 scales;
+ *          "Is finer better? Limits of micro-scaling formats in LLMs",
+ *          Framework Teorico (UE4M3, smallest non-zero scale 2^-9) and
+ *          Risultati (UE4M3-S: UE4M3 with per-tensor scaling).
+ *   UE4M3 / UE5M3 at b in {8, 16, 32, 64, 128, 256}: the block-size sweep and
+ *          the UE5M3 scale (smallest non-zero scale 2^-17, no per-tensor scale)
+ *          of "Is finer better?", Metodologia and Contributi Chiave item 3.
+ *
+ * An optional block-diagonal Hadamard rotation of size 16 or 32 (equal to the
+ * block) precedes quantization ("Bridging the Gap...", Sommario tecnico
+ * section 3 item 1 and section 2).  The error of each block is split into the
+ * three sources of "Is finer better?", Framework Teorico: non-maximum elements,
+ * the block maximum, and zero-rounding of a whole block.
+ *
+ * Rules the pages leave open, as this library implements them:
+ *   - E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}: nearest value, an exact tie
+ *     goes to the even 3-bit code, past 6 saturates to 6; the code's sign bit is
+ *     the input's sign (so -0 and small negatives give 0x8).
+ *   - MXFP4 scale exponent E = floor(log2 m) - 2, clamped to [-127, 127], where
+ *     m is the block's largest magnitude; byte = E + 127 (0x00 for an all-zero
+ *     block); codes are those of x * 2^-E.
+ *   - UE4M3 scale: D = RN32(6 g); s = RN32(m / D); the byte is s rounded to
+ *     the nearest UE4M3 value (ties to even, saturating at 448, E4M3 bit
+ *     pattern with a clear sign bit); d = RN32(s_hat * g); codes are those of
+ *     RN32(x / d), or sign-only zeros when s_hat = 0.  UE5M3 is the same with
+ *     bias 15, values down to 2^-17 and up to 61440, and g = 1.
+ *   - Dynamic per-tensor scale: g = RN32(amax / 2688) over the (rotated)
+ *     tensor, g = 1 when that is 0.
+ *   - Rotation: normalised Sylvester Walsh-Hadamard transform in binary32,
+ *     butterfly stages h = 1, 2, 4, ... in that order, then one multiply by
+ *     RN32(n^-1/2).  Quantization, amax and errors act on rotated values.
+ *   - Packing: byte j of a row's codes holds element 2j in its low nibble and
+ *     element 2j+1 in its high nibble.  Scales are one byte per block, row-major
+ *     (rows x cols/b).  Per-block MSE is one float per block, same layout.
+ *   - Errors: e = x - x_hat; block SSE; m = max |x|, i* = the lowest index
+ *     attaining m.  A zero-rounded block has m > 0 and every x_hat = 0: its SSE
+ *     is the zero-rounding term.  Otherwise e_{i*}^2 is the max-element term
+ *     and the rest of the SSE the non-max term.  Per-block MSE is SSE/b (ABS)
+ *     or SSE/sum(x^2) (REL, 0 when sum(x^2) = 0).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers marked "device" are device memory owned by the caller; the
+ *     library allocates nothing.  Inputs and outputs are contiguous row-major.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  Every
+ *     call is asynchronous; outputs are valid once the stream has reached the
+ *     call.  Calls may be captured into a HIP graph.
+ *   - A call returns a status at once.  Arguments are checked before anything is
+ *     launched: on an error nothing is launched or written, and fp4q_last_error()
+ *     (thread-local) holds a description.  No C++ exception crosses the ABI.
+ *   - rows * cols == 0 is valid: codes/scales/block_mse are untouched, *stats
+ *     is set to zeros and, in the dynamic mode, *g to 1.
+ *   - NaN and infinite inputs are outside the contract: codes are unspecified
+ *     for them; nothing faults.  With rotation, inputs must also keep the
+ *     binary32 butterfly finite, which |x| < 2^100 guarantees.
+ *   - Workspace: calls that take `ws` need fp4q_workspace_bytes() bytes of
+ *     device memory (256-byte aligned, any initial contents).  One workspace
+ *     serves any number of calls in stream order, but only one call at a time:
+ *     calls that overlap on one workspace race.
+ *   - Results are deterministic: the same inputs give bit-identical outputs,
+ *     including the floating-point sums in fp4q_stats.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4Q_ABI_VERSION 1
+
+typedef enum {
+    FP4Q_OK = 0,
+    FP4Q_ERR_ARG = 1,       /* a required pointer is NULL or an enum is out of range */
+    FP4Q_ERR_SHAPE = 2,     /* negative size, cols % block != 0, bad block/rotation */
+    FP4Q_ERR_ALIGN = 3,     /* a pointer violates the alignment stated below */
+    FP4Q_ERR_WORKSPACE = 4, /* ws missing or smaller than fp4q_workspace_bytes() */
+    FP4Q_ERR_HIP = 5        /* the HIP runtime reported an error at launch */
+} fp4q_status;
+
+typedef enum { FP4Q_BF16 = 0, FP4Q_F32 = 1 } fp4q_dtype;
+
+typedef enum {
+    FP4Q_FMT_MXFP4 = 0, /* E8M0 scales, block 32 */
+    FP4Q_FMT_UE4M3 = 1, /* UE4M3 scales (NVFP4 at block 16), with per-tensor g */
+    FP4Q_FMT_UE5M3 = 2  /* UE5M3 scales, no per-tensor scale (g = 1) */
+} fp4q_format;
+
+typedef enum {
+    FP4Q_G_NONE = 0,    /* g = 1 */
+    FP4Q_G_DYNAMIC = 1, /* g = RN32(amax / 2688), written to *g (device) */
+    FP4Q_G_GIVEN = 2    /* g read from *g (device); must be positive and finite */
+} fp4q_gmode;
+
+typedef enum { FP4Q_MSE_ABS = 0, FP4Q_MSE_REL = 1 } fp4q_mse_kind;
+
+/* Tensor-level error terms (device memory, written by the call). */
+typedef struct {
+    double sse_nonmax;     /* sum of squared errors of non-maximum elements */
+    double sse_max;        /* sum of squared errors of the block maxima */
+    double sse_zero;       /* squared error of zero-rounded blocks (whole blocks) */
+    double sum_x2;         /* sum of x^2 (rotated values when rotating) */
+    int64_t n_blocks;      /* rows * cols / block */
+    int64_t n_zero_blocks; /* number of zero-rounded blocks */
+} fp4q_stats;
+
+/*
+ * MXFP4 quantization (block 32, E8M0 scales), fused with dequantization and the
+ * error split.
+ *   x          device, rows x cols, dtype xt (FP4Q_BF16 or FP4Q_F32); 16-byte aligned
+ *   rotate     0 or 32 (block Hadamard before quantization)
+ *   codes      device out, rows x cols/2 bytes; 16-byte aligned
+ *   scales     device out, rows x cols/32 bytes (E8M0 byte = E + 127)
+ *   block_mse  device out or NULL, rows x cols/32 floats (kind mse_kind); 4-byte aligned
+ *   stats      device out or NULL; 8-byte aligned
+ *   ws         device workspace (see Conventions); needed when stats != NULL
+ * cols must be a multiple of 32.  With block_mse and stats both NULL only codes
+ * and scales are produced.
+ */
+fp4q_status mxfp4_quantize(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t rotate,
+                           uint8_t* codes, uint8_t* scales, float* block_mse, int32_t mse_kind,
+                           fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * UE4M3 / UE5M3 block quantization (NVFP4 at block 16), fused as above.
+ *   block      8, 16, 32, 64, 128 or 256; cols must be a multiple of it
+ *   scale_fmt  FP4Q_FMT_UE4M3 or FP4Q_FMT_UE5M3 (UE5M3 requires gmode NONE)
+ *   gmode      fp4q_gmode; g is a device pointer to one float, written in the
+ *              dynamic mode and read in the given mode (may be NULL for NONE)
+ *   rotate     0, or equal to block when block is 16 or 32
+ *   ws         needed when stats != NULL or gmode == DYNAMIC
+ * Other arguments as for mxfp4_quantize; scales are rows x cols/block bytes.
+ */
+fp4q_status nvfp4_quantize(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t block,
+                           int32_t scale_fmt, int32_t gmode, float* g, int32_t rotate,
+                           uint8_t* codes, uint8_t* scales, float* block_mse, int32_t mse_kind,
+                           fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dequantization of stored codes and scales ("Diagnosing FP4 inference",
+ * section 2: weights are dequantized for the compute).  x_hat = v * 2^E (MXFP4,
+ * exact) or RN32(v * d) with d = RN32(s_hat * g); with rotate the block
+ * Hadamard is applied to x_hat, returning to the original domain.
+ *   codes, scales  device, as written by the quantize calls; codes 4-byte aligned
+ *   fmt, block     FP4Q_FMT_MXFP4 (block 32) / UE4M3 / UE5M3 (block 8..256)
+ *   g              device pointer to g for UE4M3 (NULL means g = 1); ignored otherwise
+ *   out            device out, rows x cols of dtype ot (F32, or BF16 rounded to
+ *                  nearest even); 16-byte aligned
+ */
+fp4q_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales, int32_t fmt, int32_t block,
+                           const float* g, int64_t rows, int64_t cols, int32_t rotate, void* out,
+                           int32_t ot, void* stream);
+
+/*
+ * Error split of stored codes against x (rotated first when rotate != 0):
+ * block MSE and tensor terms exactly as the fused quantize calls report them.
+ * The max-element term uses the lowest index attaining the block maximum, so
+ * codes need not come from this library.  ws is needed when stats != NULL.
+ */
+fp4q_status fp4_block_mse(const void* x, int32_t xt, const uint8_t* codes, const uint8_t* scales,
+                          int32_t fmt, int32_t block, const float* g, int64_t rows, int64_t cols,
+                          int32_t rotate, float* block_mse, int32_t mse_kind, fp4q_stats* stats,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Block-diagonal normalised Hadamard rotation ("Bridging the Gap...", Sommario
+ * tecnico section 3 item 1), n = 16 or 32, cols % n == 0.  out is device
+ * binary32, 16-byte aligned.  The transform is its own inverse up to rounding.
+ */
+fp4q_status hadamard_block_rotate(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t n,
+                                  float* out, void* stream);
+
+/* Workspace size in bytes for any call on a rows x cols tensor (a constant
+ * upper bound in this version). */
+size_t fp4q_workspace_bytes(int64_t rows, int64_t cols, int32_t block);
+
+/* Description of the last error returned on the calling thread ("" if none). */
+const char* fp4q_last_error(void);
+
+/* FP4Q_ABI_VERSION of the loaded library. */
+int32_t fp4q_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4Q_H */

@@ -1,0 +1,241 @@
+"""Python binding of libfp4q.so, the gfx950 microscaling FP4 quantization library.
+
+The functions here carry the C ABI's names (include/fp4q.h) and only marshal
+arguments: they check tensor shapes, allocate outputs with torch when the caller
+does not pass them, and hand device pointers and torch's current HIP stream to
+the library.  Every step of the computation runs in the library's kernels.
+There is no fallback: if libfp4q.so is missing, importing the functions works but
+every call raises.
+
+Layouts (row-major, blocks of b consecutive elements along a row):
+  codes      uint8 rows x cols/2; byte j holds element 2j (low nibble) and 2j+1
+  scales     uint8 rows x cols/b; E8M0 (MXFP4) or UE4M3/UE5M3 bytes
+  block_mse  float32 rows x cols/b
+  stats      float64[6] device tensor laid out as the C struct fp4q_stats
+             (sse_nonmax, sse_max, sse_zero, sum_x2, then two int64 counts);
+             read it with stats_dict().
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp4q.so")
+
+BF16, F32 = 0, 1
+FMT_MXFP4, FMT_UE4M3, FMT_UE5M3 = 0, 1, 2
+G_NONE, G_DYNAMIC, G_GIVEN = 0, 1, 2
+MSE_ABS, MSE_REL = 0, 1
+STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
+
+EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "fp4_dequantize", "fp4_block_mse",
+           "hadamard_block_rotate", "fp4q_workspace_bytes", "fp4q_last_error",
+           "fp4q_abi_version")
+
+
+class Fp4qError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libfp4q.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise Fp4qError(5, f"{LIB_PATH} is missing; build it with "
+                               "`python -m microscaling_fp4_quantization_amd.build`")
+        _lib = _bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _bind(l):
+    c = ctypes
+    P, i32, i64, sz = c.c_void_p, c.c_int32, c.c_int64, c.c_size_t
+    l.mxfp4_quantize.argtypes = [P, i32, i64, i64, i32, P, P, P, i32, P, P, sz, P]
+    l.nvfp4_quantize.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, P, P, P, i32, P, P, sz, P]
+    l.fp4_dequantize.argtypes = [P, P, i32, i32, P, i64, i64, i32, P, i32, P]
+    l.fp4_block_mse.argtypes = [P, i32, P, P, i32, i32, P, i64, i64, i32, P, i32, P, P, sz, P]
+    l.hadamard_block_rotate.argtypes = [P, i32, i64, i64, i32, P, P]
+    for name in ("mxfp4_quantize", "nvfp4_quantize", "fp4_dequantize", "fp4_block_mse",
+                 "hadamard_block_rotate"):
+        getattr(l, name).restype = c.c_int
+    l.fp4q_workspace_bytes.argtypes = [i64, i64, i32]
+    l.fp4q_workspace_bytes.restype = sz
+    l.fp4q_last_error.argtypes = []
+    l.fp4q_last_error.restype = c.c_char_p
+    l.fp4q_abi_version.argtypes = []
+    l.fp4q_abi_version.restype = c.c_int32
+    return l
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise Fp4qError(rc, lib().fp4q_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _matrix(x: torch.Tensor, what: str = "x") -> torch.Tensor:
+    if x.dim() != 2:
+        raise ValueError(f"{what} must be 2-D (rows x cols)")
+    if not x.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if not x.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    return x
+
+
+_workspaces = {}
+
+
+def workspace_bytes(rows: int = 0, cols: int = 0, block: int = 32) -> int:
+    return int(lib().fp4q_workspace_bytes(rows, cols, block))
+
+
+def workspace(device) -> torch.Tensor:
+    """A zero-filled workspace for `device`, shared by calls made on one stream."""
+    key = torch.device(device).index
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = torch.zeros(workspace_bytes(), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def new_stats(device) -> torch.Tensor:
+    return torch.zeros(6, dtype=torch.float64, device=device)
+
+
+def stats_dict(stats: torch.Tensor) -> dict:
+    """Copy an fp4q_stats tensor to the host (synchronises)."""
+    h = stats.detach().cpu()
+    f = h[:4].tolist()
+    i = h.view(torch.int64)[4:6].tolist()
+    return {"sse_nonmax": f[0], "sse_max": f[1], "sse_zero": f[2], "sum_x2": f[3],
+            "n_blocks": i[0], "n_zero_blocks": i[1]}
+
+
+@dataclass
+class Quantized:
+    codes: torch.Tensor
+    scales: torch.Tensor
+    block_mse: Optional[torch.Tensor]
+    stats: Optional[torch.Tensor]
+    g: Optional[torch.Tensor]
+
+
+def _outputs(x, block, codes, scales, block_mse, stats):
+    rows, cols = x.shape
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, cols // block), dtype=torch.uint8, device=dev)
+    if block_mse is True:
+        block_mse = torch.empty((rows, cols // block), dtype=torch.float32, device=dev)
+    elif block_mse is False:
+        block_mse = None
+    if stats is True:
+        stats = new_stats(dev)
+    elif stats is False:
+        stats = None
+    return codes, scales, block_mse, stats
+
+
+def mxfp4_quantize(x: torch.Tensor, rotate: int = 0, *, codes=None, scales=None,
+                   block_mse=True, mse_kind: int = MSE_ABS, stats=True,
+                   ws: Optional[torch.Tensor] = None) -> Quantized:
+    """MXFP4 (block 32, E8M0) quantize + pack + dequantize + error split.
+
+    ``block_mse`` / ``stats``: True to allocate, False to skip, or a tensor to fill.
+    """
+    x = _matrix(x)
+    codes, scales, block_mse, stats = _outputs(x, 32, codes, scales, block_mse, stats)
+    ws = ws if ws is not None else (workspace(x.device) if stats is not None else None)
+    _check(lib().mxfp4_quantize(_ptr(x), _dtype_code(x), x.shape[0], x.shape[1], rotate,
+                                _ptr(codes), _ptr(scales), _ptr(block_mse), mse_kind,
+                                _ptr(stats), _ptr(ws), 0 if ws is None else ws.numel(),
+                                _stream(x.device)))
+    return Quantized(codes, scales, block_mse, stats, None)
+
+
+def nvfp4_quantize(x: torch.Tensor, block: int = 16, scale_fmt: int = FMT_UE4M3,
+                   gmode: int = G_DYNAMIC, g: Optional[torch.Tensor] = None, rotate: int = 0, *,
+                   codes=None, scales=None, block_mse=True, mse_kind: int = MSE_ABS, stats=True,
+                   ws: Optional[torch.Tensor] = None) -> Quantized:
+    """UE4M3/UE5M3 block quantize (NVFP4 at block 16) + pack + dequantize + error split.
+
+    ``g``: one-element float32 device tensor; written in the dynamic mode (allocated
+    when not given), read in the given mode.
+    """
+    x = _matrix(x)
+    codes, scales, block_mse, stats = _outputs(x, block, codes, scales, block_mse, stats)
+    if gmode != G_NONE and g is None:
+        g = torch.empty(1, dtype=torch.float32, device=x.device)
+    need_ws = stats is not None or gmode == G_DYNAMIC
+    ws = ws if ws is not None else (workspace(x.device) if need_ws else None)
+    _check(lib().nvfp4_quantize(_ptr(x), _dtype_code(x), x.shape[0], x.shape[1], block,
+                                scale_fmt, gmode, _ptr(g), rotate, _ptr(codes), _ptr(scales),
+                                _ptr(block_mse), mse_kind, _ptr(stats), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(x.device)))
+    return Quantized(codes, scales, block_mse, stats, g)
+
+
+def fp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, fmt: int, block: int,
+                   g: Optional[torch.Tensor] = None, rotate: int = 0,
+                   out_dtype=torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    codes = _matrix(codes, "codes")
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
+    _check(lib().fp4_dequantize(_ptr(codes), _ptr(scales), fmt, block, _ptr(g), rows, cols,
+                                rotate, _ptr(out), _dtype_code(out), _stream(codes.device)))
+    return out
+
+
+def fp4_block_mse(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, fmt: int,
+                  block: int, g: Optional[torch.Tensor] = None, rotate: int = 0, *,
+                  block_mse=True, mse_kind: int = MSE_ABS, stats=True,
+                  ws: Optional[torch.Tensor] = None):
+    """Error split of stored codes against x; returns (block_mse, stats)."""
+    x = _matrix(x)
+    _, _, block_mse, stats = _outputs(x, block, codes, scales, block_mse, stats)
+    ws = ws if ws is not None else (workspace(x.device) if stats is not None else None)
+    _check(lib().fp4_block_mse(_ptr(x), _dtype_code(x), _ptr(codes), _ptr(scales), fmt, block,
+                               _ptr(g), x.shape[0], x.shape[1], rotate, _ptr(block_mse),
+                               mse_kind, _ptr(stats), _ptr(ws), 0 if ws is None else ws.numel(),
+                               _stream(x.device)))
+    return block_mse, stats
+
+
+def hadamard_block_rotate(x: torch.Tensor, n: int, out: Optional[torch.Tensor] = None):
+    x = _matrix(x)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _check(lib().hadamard_block_rotate(_ptr(x), _dtype_code(x), x.shape[0], x.shape[1], n,
+                                       _ptr(out), _stream(x.device)))
+    return out

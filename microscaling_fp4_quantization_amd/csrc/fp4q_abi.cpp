@@ -1,0 +1,217 @@
+// fp4q_abi.cpp -- the extern "C" entry points declared in include/fp4q.h.
+//
+// Every entry point validates its arguments completely before anything is
+// launched, so an error status means nothing was enqueued and no output was
+// touched.  Launching is delegated to fp4q_kernels.hip.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/fp4q.h"
+#include "fp4q_launch.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+fp4q_status fail(fp4q_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+fp4q_status ok() {
+    g_err[0] = '\0';
+    return FP4Q_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_block(int32_t b) { return b == 8 || b == 16 || b == 32 || b == 64 || b == 128 || b == 256; }
+
+// Shape rules shared by all calls.
+fp4q_status check_shape(const char* fn, int64_t rows, int64_t cols, int32_t block, int32_t rotate) {
+    if (rows < 0 || cols < 0) return fail(FP4Q_ERR_SHAPE, "%s: negative size %lld x %lld", fn, (long long)rows, (long long)cols);
+    if (rows > 0 && cols > INT64_MAX / rows) return fail(FP4Q_ERR_SHAPE, "%s: rows * cols overflows", fn);
+    if (!valid_block(block)) return fail(FP4Q_ERR_SHAPE, "%s: block %d is not one of 8, 16, 32, 64, 128, 256", fn, block);
+    if (cols % block != 0) return fail(FP4Q_ERR_SHAPE, "%s: cols %lld is not a multiple of the block %d", fn, (long long)cols, block);
+    if (rotate != 0) {
+        if (rotate != 16 && rotate != 32) return fail(FP4Q_ERR_SHAPE, "%s: rotate %d is not 0, 16 or 32", fn, rotate);
+        if (rotate != block) return fail(FP4Q_ERR_SHAPE, "%s: rotate %d must equal the block %d", fn, rotate, block);
+    }
+    return FP4Q_OK;
+}
+
+fp4q_status check_dtype(const char* fn, int32_t t) {
+    if (t != FP4Q_BF16 && t != FP4Q_F32) return fail(FP4Q_ERR_ARG, "%s: dtype %d is not BF16 (0) or F32 (1)", fn, t);
+    return FP4Q_OK;
+}
+
+fp4q_status check_mse(const char* fn, const float* block_mse, int32_t kind) {
+    if (kind != FP4Q_MSE_ABS && kind != FP4Q_MSE_REL) return fail(FP4Q_ERR_ARG, "%s: mse_kind %d is not ABS (0) or REL (1)", fn, kind);
+    if (block_mse && !aligned(block_mse, 4)) return fail(FP4Q_ERR_ALIGN, "%s: block_mse is not 4-byte aligned", fn);
+    return FP4Q_OK;
+}
+
+fp4q_status check_ws(const char* fn, bool needed, void* ws, size_t ws_bytes) {
+    if (!needed) return FP4Q_OK;
+    if (!ws) return fail(FP4Q_ERR_WORKSPACE, "%s: a workspace is needed (stats or dynamic scale) but ws is NULL", fn);
+    if (!aligned(ws, 256)) return fail(FP4Q_ERR_ALIGN, "%s: ws is not 256-byte aligned", fn);
+    if (ws_bytes < fp4q::kWsBytes) return fail(FP4Q_ERR_WORKSPACE, "%s: ws has %zu bytes, needs %zu", fn, ws_bytes, fp4q::kWsBytes);
+    return FP4Q_OK;
+}
+
+fp4q_status launched(int rc, const char* msg) {
+    if (rc) return fail(FP4Q_ERR_HIP, "%s", msg);
+    return ok();
+}
+
+#define TRY(expr)                          \
+    do {                                   \
+        fp4q_status st_ = (expr);          \
+        if (st_ != FP4Q_OK) return st_;    \
+    } while (0)
+
+fp4q_status quantize_common(const char* fn, const void* x, int32_t xt, int64_t rows, int64_t cols,
+                            int32_t block, int32_t fmt, int32_t gmode, float* g, int32_t rotate,
+                            uint8_t* codes, uint8_t* scales, float* block_mse, int32_t mse_kind,
+                            fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_dtype(fn, xt));
+    TRY(check_shape(fn, rows, cols, block, rotate));
+    TRY(check_mse(fn, block_mse, mse_kind));
+    if (gmode != FP4Q_G_NONE && gmode != FP4Q_G_DYNAMIC && gmode != FP4Q_G_GIVEN)
+        return fail(FP4Q_ERR_ARG, "%s: gmode %d is not NONE (0), DYNAMIC (1) or GIVEN (2)", fn, gmode);
+    if (fmt == FP4Q_FMT_UE5M3 && gmode != FP4Q_G_NONE)
+        return fail(FP4Q_ERR_ARG, "%s: UE5M3 scales take no per-tensor scale (gmode must be NONE)", fn);
+    if (gmode != FP4Q_G_NONE && !g) return fail(FP4Q_ERR_ARG, "%s: gmode %d needs a g pointer", fn, gmode);
+    if (g && !aligned(g, 4)) return fail(FP4Q_ERR_ALIGN, "%s: g is not 4-byte aligned", fn);
+    const int64_t n = rows * cols;
+    if (n > 0) {
+        if (!x || !codes || !scales) return fail(FP4Q_ERR_ARG, "%s: x, codes and scales must not be NULL", fn);
+        if (!aligned(x, 16)) return fail(FP4Q_ERR_ALIGN, "%s: x is not 16-byte aligned", fn);
+        if (!aligned(codes, 16)) return fail(FP4Q_ERR_ALIGN, "%s: codes is not 16-byte aligned", fn);
+    }
+    if (stats && !aligned(stats, 8)) return fail(FP4Q_ERR_ALIGN, "%s: stats is not 8-byte aligned", fn);
+    TRY(check_ws(fn, stats != nullptr || gmode == FP4Q_G_DYNAMIC, ws, ws_bytes));
+    fp4q::QuantJob j{};
+    j.x = x;
+    j.xt = xt;
+    j.n = n;
+    j.block = block;
+    j.fmt = fmt;
+    j.gmode = gmode;
+    j.g = g;
+    j.rotate = rotate;
+    j.codes = codes;
+    j.scales = scales;
+    j.block_mse = block_mse;
+    j.mse_kind = mse_kind;
+    j.stats = stats;
+    j.ws = ws;
+    j.stream = stream;
+    char msg[256] = {0};
+    return launched(fp4q::launch_quantize(j, msg, sizeof msg), msg);
+}
+
+fp4q_status check_fmt_block(const char* fn, int32_t fmt, int32_t block) {
+    if (fmt != FP4Q_FMT_MXFP4 && fmt != FP4Q_FMT_UE4M3 && fmt != FP4Q_FMT_UE5M3)
+        return fail(FP4Q_ERR_ARG, "%s: fmt %d is not MXFP4 (0), UE4M3 (1) or UE5M3 (2)", fn, fmt);
+    if (fmt == FP4Q_FMT_MXFP4 && block != 32) return fail(FP4Q_ERR_SHAPE, "%s: MXFP4 blocks are 32, not %d", fn, block);
+    return FP4Q_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fp4q_status mxfp4_quantize(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t rotate,
+                           uint8_t* codes, uint8_t* scales, float* block_mse, int32_t mse_kind,
+                           fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+    if (rotate != 0 && rotate != 32) return fail(FP4Q_ERR_SHAPE, "mxfp4_quantize: rotate %d is not 0 or 32", rotate);
+    return quantize_common("mxfp4_quantize", x, xt, rows, cols, 32, FP4Q_FMT_MXFP4, FP4Q_G_NONE, nullptr,
+                           rotate, codes, scales, block_mse, mse_kind, stats, ws, ws_bytes, stream);
+}
+
+fp4q_status nvfp4_quantize(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t block,
+                           int32_t scale_fmt, int32_t gmode, float* g, int32_t rotate,
+                           uint8_t* codes, uint8_t* scales, float* block_mse, int32_t mse_kind,
+                           fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+    if (scale_fmt != FP4Q_FMT_UE4M3 && scale_fmt != FP4Q_FMT_UE5M3)
+        return fail(FP4Q_ERR_ARG, "nvfp4_quantize: scale_fmt %d is not UE4M3 (1) or UE5M3 (2)", scale_fmt);
+    return quantize_common("nvfp4_quantize", x, xt, rows, cols, block, scale_fmt, gmode, g, rotate,
+                           codes, scales, block_mse, mse_kind, stats, ws, ws_bytes, stream);
+}
+
+fp4q_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales, int32_t fmt, int32_t block,
+                           const float* g, int64_t rows, int64_t cols, int32_t rotate, void* out,
+                           int32_t ot, void* stream) {
+    const char* fn = "fp4_dequantize";
+    TRY(check_fmt_block(fn, fmt, block));
+    TRY(check_shape(fn, rows, cols, block, rotate));
+    TRY(check_dtype(fn, ot));
+    if (g && !aligned(g, 4)) return fail(FP4Q_ERR_ALIGN, "%s: g is not 4-byte aligned", fn);
+    const int64_t n = rows * cols;
+    if (n > 0) {
+        if (!codes || !scales || !out) return fail(FP4Q_ERR_ARG, "%s: codes, scales and out must not be NULL", fn);
+        if (!aligned(codes, 4)) return fail(FP4Q_ERR_ALIGN, "%s: codes is not 4-byte aligned", fn);
+        if (!aligned(out, 16)) return fail(FP4Q_ERR_ALIGN, "%s: out is not 16-byte aligned", fn);
+    }
+    fp4q::DequantJob j{codes, scales, fmt, block, fmt == FP4Q_FMT_UE4M3 ? g : nullptr, n, rotate, out, ot, stream};
+    char msg[256] = {0};
+    return launched(fp4q::launch_dequantize(j, msg, sizeof msg), msg);
+}
+
+fp4q_status fp4_block_mse(const void* x, int32_t xt, const uint8_t* codes, const uint8_t* scales,
+                          int32_t fmt, int32_t block, const float* g, int64_t rows, int64_t cols,
+                          int32_t rotate, float* block_mse, int32_t mse_kind, fp4q_stats* stats,
+                          void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "fp4_block_mse";
+    TRY(check_fmt_block(fn, fmt, block));
+    TRY(check_dtype(fn, xt));
+    TRY(check_shape(fn, rows, cols, block, rotate));
+    TRY(check_mse(fn, block_mse, mse_kind));
+    if (g && !aligned(g, 4)) return fail(FP4Q_ERR_ALIGN, "%s: g is not 4-byte aligned", fn);
+    const int64_t n = rows * cols;
+    if (n > 0) {
+        if (!x || !codes || !scales) return fail(FP4Q_ERR_ARG, "%s: x, codes and scales must not be NULL", fn);
+        if (!aligned(x, 16)) return fail(FP4Q_ERR_ALIGN, "%s: x is not 16-byte aligned", fn);
+        if (!aligned(codes, 4)) return fail(FP4Q_ERR_ALIGN, "%s: codes is not 4-byte aligned", fn);
+    }
+    if (stats && !aligned(stats, 8)) return fail(FP4Q_ERR_ALIGN, "%s: stats is not 8-byte aligned", fn);
+    TRY(check_ws(fn, stats != nullptr, ws, ws_bytes));
+    fp4q::MseJob j{x, xt, codes, scales, fmt, block, fmt == FP4Q_FMT_UE4M3 ? g : nullptr, n, rotate,
+                   block_mse, mse_kind, stats, ws, stream};
+    char msg[256] = {0};
+    return launched(fp4q::launch_block_mse(j, msg, sizeof msg), msg);
+}
+
+fp4q_status hadamard_block_rotate(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t n_rot,
+                                  float* out, void* stream) {
+    const char* fn = "hadamard_block_rotate";
+    TRY(check_dtype(fn, xt));
+    if (n_rot != 16 && n_rot != 32) return fail(FP4Q_ERR_SHAPE, "%s: n %d is not 16 or 32", fn, n_rot);
+    TRY(check_shape(fn, rows, cols, n_rot, n_rot));
+    const int64_t n = rows * cols;
+    if (n > 0) {
+        if (!x || !out) return fail(FP4Q_ERR_ARG, "%s: x and out must not be NULL", fn);
+        if (!aligned(x, 16) || !aligned(out, 16)) return fail(FP4Q_ERR_ALIGN, "%s: x and out must be 16-byte aligned", fn);
+    }
+    fp4q::RotateJob j{x, xt, n, n_rot, out, stream};
+    char msg[256] = {0};
+    return launched(fp4q::launch_rotate(j, msg, sizeof msg), msg);
+}
+
+size_t fp4q_workspace_bytes(int64_t rows, int64_t cols, int32_t block) {
+    (void)rows;
+    (void)cols;
+    (void)block;
+    return fp4q::kWsBytes;
+}
+
+const char* fp4q_last_error(void) { return g_err; }
+
+int32_t fp4q_abi_version(void) { return FP4Q_ABI_VERSION; }
+
+}  // extern "C"

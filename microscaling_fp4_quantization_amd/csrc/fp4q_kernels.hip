@@ -1,0 +1,1097 @@
+// fp4q_kernels.hip -- gfx950 kernels for block-wise microscaling FP4 quantization.
+//
+// Work layout.  A tensor of n = rows * cols elements is a flat run of n / b
+// blocks (blocks never cross a row because cols % b == 0).  Each lane owns 8
+// consecutive elements (one 16-byte load of bf16, two of fp32), so a block of b
+// spans L = b / 8 lanes of one wavefront and a 64-lane wave covers a 512-element
+// chunk with perfectly coalesced loads and 4-byte code stores.  Block maxima and
+// error sums are reduced across the L lanes with DPP quad permutes and row
+// mirrors; nothing goes through LDS on the hot path.  A wave takes kUnroll
+// chunks per iteration (all loads issued before any use); the 4 waves of a
+// workgroup walk adjacent tiles of one contiguous slice of the tensor, and the
+// slices are laid out so that each XCD streams one contiguous eighth.
+//
+// Arithmetic (the rules the pages leave open are stated in include/fp4q.h):
+//   MXFP4: the E8M0 byte is the block maximum's binary32 exponent field minus 2
+//   (clamped at 0); codes come from v_cvt_scalef32_pk_fp4_{bf16,f32}, which
+//   divide by the scale's power of two exactly and round to nearest-even onto
+//   E2M1 with saturation and a kept sign; dequantization (exact) from
+//   v_cvt_scalef32_pk_f32_fp4.
+//   UE4M3/UE5M3: s = m / D and the reciprocal r = 1 / d are correctly rounded
+//   divisions once per block; the element quotient RN32(x / d) uses the
+//   FMA-corrected reciprocal product of Markstein (IBM J. Res. Dev. 34(1), 1990):
+//   q = x r, rem = fma(-q, d, x), y = fma(rem, r, q), which returns the
+//   correctly rounded quotient when r = RN(1/d) and no intermediate leaves the
+//   normal range; blocks whose d or x / d leave the safe range use a plain
+//   division.  y is then coded with the same cvt instruction at scale 1.
+//   Errors: e = x - x_hat in binary32 (exact for MXFP4 and for unsaturated
+//   UE4M3 blocks), squared and summed in binary64.  The max-element term is
+//   computed from the block maximum m itself (every element attaining m has
+//   the same error), the non-max term as block SSE minus it.
+//   Tensor terms: per-workgroup binary64 partials, summed in a fixed order by
+//   the last workgroup to finish, so results are bit-reproducible.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "fp4q_launch.h"
+
+namespace fp4q {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kLaneElems = 8;
+constexpr int kChunk = kWave * kLaneElems;  // 512 elements per wave per chunk
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kUnroll = 4;                  // chunks per wave iteration
+constexpr int kTile = kChunk * kUnroll;     // elements per wave iteration
+constexpr int kGroupsPerCU = 8;
+
+constexpr int kFmtMx = 0;
+constexpr int kFmtUe4m3 = 1;
+constexpr int kMseRel = 1;
+
+// DPP controls (GFX9 encoding).
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i within 16
+
+constexpr uint32_t kRsqrt32Bits = 0x3E3504F3u;  // RN32(2^-2.5)
+
+// ------------------------------------------------------------ lane helpers
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    uint64_t u = (uint64_t)__double_as_longlong(v);
+    uint32_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Max over the L lanes of an aligned lane group; every lane gets the result.
+template <int L>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+    if constexpr (L >= 2) v = max(v, dpp_u32<kQuadXor1>(v));
+    if constexpr (L >= 4) v = max(v, dpp_u32<kQuadXor2>(v));
+    if constexpr (L >= 8) v = max(v, dpp_u32<kRowHalfMirror>(v));
+    if constexpr (L >= 16) v = max(v, dpp_u32<kRowMirror>(v));
+    if constexpr (L >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+    return v;
+}
+
+// Sum over the lane group.  Each step adds two equal-sized partial sums, so
+// every lane ends with bit-identical totals.
+template <int L>
+__device__ __forceinline__ double group_sum(double v) {
+    if constexpr (L >= 2) v = v + dpp_f64<kQuadXor1>(v);
+    if constexpr (L >= 4) v = v + dpp_f64<kQuadXor2>(v);
+    if constexpr (L >= 8) v = v + dpp_f64<kRowHalfMirror>(v);
+    if constexpr (L >= 16) v = v + dpp_f64<kRowMirror>(v);
+    if constexpr (L >= 32) v = v + __shfl_xor(v, 16);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+    for (int s = 32; s >= 1; s >>= 1) v = v + __shfl_xor(v, s);
+    return v;
+}
+
+__device__ __forceinline__ long long wave_sum_i64(long long v) {
+    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+    for (int s = 32; s >= 1; s >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, s));
+    return v;
+}
+
+// Logical slice index for workgroup `bid` of `G`: workgroups are dispatched
+// round-robin over the 8 XCDs, so XCD x receives bids x, x+8, ...; giving those
+// consecutive slices keeps each XCD on one contiguous eighth of the tensor.
+__device__ __forceinline__ int xcd_slice(int bid, int G) {
+    const int q = G / 8, r = G % 8, x = bid % 8, k = bid / 8;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
+}
+
+// ------------------------------------------------------------ input chunks
+template <int XT>
+struct Raw;
+template <>
+struct Raw<0> {  // 8 bf16
+    uint4 w;
+};
+template <>
+struct Raw<1> {  // 8 fp32
+    uint4 a, b;
+};
+
+template <int XT>
+__device__ __forceinline__ Raw<XT> load_chunk(const void* x, int64_t base, int64_t n) {
+    Raw<XT> r;
+    if constexpr (XT == 0) {
+        r.w = make_uint4(0, 0, 0, 0);
+        if (base < n) r.w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + base);
+    } else {
+        r.a = make_uint4(0, 0, 0, 0);
+        r.b = r.a;
+        if (base < n) {
+            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + base);
+            r.a = p[0];
+            r.b = p[1];
+        }
+    }
+    return r;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int XT>
+__device__ __forceinline__ void unpack(const Raw<XT>& r, float (&v)[8]) {
+    if constexpr (XT == 0) {
+        v[0] = bf16_lo(r.w.x); v[1] = bf16_hi(r.w.x);
+        v[2] = bf16_lo(r.w.y); v[3] = bf16_hi(r.w.y);
+        v[4] = bf16_lo(r.w.z); v[5] = bf16_hi(r.w.z);
+        v[6] = bf16_lo(r.w.w); v[7] = bf16_hi(r.w.w);
+    } else {
+        v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y);
+        v[2] = __uint_as_float(r.a.z); v[3] = __uint_as_float(r.a.w);
+        v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+        v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+    }
+}
+
+// ------------------------------------------------------------ rotation
+// Normalised Sylvester Walsh-Hadamard transform of a block of ROT = 16 or 32
+// values spread over ROT/8 lanes (gl = lane index within the block): stages
+// h = 1, 2, 4 inside the lane, h = 8 and 16 across lanes, then the multiply by
+// RN32(ROT^-1/2).  Across lanes the upper partner forms (partner - own) as
+// fma(own, -1, partner), a single rounding of the same difference.
+template <int ROT>
+__device__ __forceinline__ void rotate8(float (&v)[8], int gl) {
+#pragma unroll
+    for (int h = 1; h < 8; h *= 2) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i & h) continue;
+            const float a = v[i], b = v[i + h];
+            v[i] = a + b;
+            v[i + h] = a - b;
+        }
+    }
+    const float s1 = (gl & 1) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = fmaf(v[i], s1, dpp_f32<kQuadXor1>(v[i]));
+    if constexpr (ROT == 32) {
+        const float s2 = (gl & 2) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = fmaf(v[i], s2, dpp_f32<kQuadXor2>(v[i]));
+    }
+    const float c = (ROT == 16) ? 0.25f : __uint_as_float(kRsqrt32Bits);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = v[i] * c;
+}
+
+// ------------------------------------------------------------ scale codes
+// Round s >= 0 to the nearest UE4M3 (fmt 1) or UE5M3 (fmt 2) value, ties to
+// the even code, saturating at the largest finite value.  Above the smallest
+// normal value the binary32 significand is rounded to 3 bits in place (the
+// rounded bits then read directly as the byte, after removing the exponent
+// bias difference); below it the value is a multiple of the subnormal step.
+__device__ __forceinline__ uint32_t ue_encode(float s, int fmt) {
+    const bool e4 = (fmt == kFmtUe4m3);
+    const uint32_t b = __float_as_uint(s);
+    const uint32_t normal = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (e4 ? 960u : 896u);
+    const uint32_t sub = (uint32_t)__builtin_rintf(s * (e4 ? 0x1p9f : 0x1p17f));
+    const uint32_t byte = s < (e4 ? 0x1p-6f : 0x1p-14f) ? sub : normal;
+    return min(byte, e4 ? 0x7Eu : 0xF7u);
+}
+
+__device__ __forceinline__ float ue_decode(uint32_t byte, int fmt) {
+    const bool e4 = (fmt == kFmtUe4m3);
+    if (byte < 8u) return (float)byte * (e4 ? 0x1p-9f : 0x1p-17f);
+    return __uint_as_float((byte + (e4 ? 960u : 896u)) << 20);
+}
+
+// Correctly rounded x / d from r = RN(1/d) (Markstein's FMA correction),
+// written with the negated remainder n = q d - x so that x = -0 gives -0.
+// Exact whenever d is in [2^-96, 2^100] and |x / d| <= 4096 (and for d = 0
+// with r = 0, where it yields a zero of x's sign).
+__device__ __forceinline__ float div_rn(float x, float d, float r) {
+    const float q = x * r;
+    const float n = fmaf(q, d, -x);
+    return fmaf(-n, r, q);
+}
+
+// Per-workgroup table of decode scales: for every scale byte c, d_c =
+// RN32(s_hat_c * g) and r_c = RN32(1 / d_c) (0 when d_c = 0).
+constexpr int kUeCodes = 256;  // covers UE4M3 (127 codes) and UE5M3 (248)
+
+__device__ __forceinline__ void build_scale_table(float2* tab, float g, int fmt) {
+    const int n_codes = (fmt == kFmtUe4m3) ? 0x7F : 0xF8;
+    for (int c = threadIdx.x; c < n_codes; c += kThreads) {
+        const float d = ue_decode((uint32_t)c, fmt) * g;
+        tab[c] = make_float2(d, d > 0.0f ? 1.0f / d : 0.0f);
+    }
+    __syncthreads();
+}
+
+// Per-block UE scale state.
+struct UeScale {
+    uint32_t byte;
+    float d, r;
+    bool fast;  // the FMA-corrected quotient is exact for every element
+};
+
+// s = RN32(m / D): the corrected quotient when it is in its exact range (D in
+// [2^-96, 2^100] and m / D <= 4096, which covers every unsaturated block),
+// else a plain division.
+__device__ __forceinline__ UeScale ue_scale(float m, float D, float rD, bool d_fast,
+                                            const float2* tab, int fmt) {
+    UeScale st;
+    float s = div_rn(m, D, rD);
+    if (!(d_fast && s <= 4096.0f)) s = m / D;
+    st.byte = ue_encode(s, fmt);
+    const float2 dr = tab[st.byte];
+    st.d = dr.x;
+    st.r = dr.y;
+    st.fast = (st.d == 0.0f) || (st.d >= 0x1p-96f && st.d <= 0x1p100f && m <= st.d * 4096.0f);
+    return st;
+}
+
+// Eight fp32 values -> one word of 8 codes (element 2k in byte k's low nibble).
+__device__ __forceinline__ uint32_t code_word_f32(const float (&y)[8], float sc) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], sc, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], sc, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], sc, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], sc, 3);
+    return w;
+}
+
+__device__ __forceinline__ uint32_t code_word_bf16(const uint4& w4, float sc) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2_t, w4.x), sc, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2_t, w4.y), sc, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2_t, w4.z), sc, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2_t, w4.w), sc, 3);
+    return w;
+}
+
+// One word of 8 codes -> 8 values v * 2^exponent(sc).
+__device__ __forceinline__ void decode_word(uint32_t w, float sc, float (&o)[8]) {
+    float2_t t;
+    t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0); o[0] = t[0]; o[1] = t[1];
+    t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1); o[2] = t[0]; o[3] = t[1];
+    t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2); o[4] = t[0]; o[5] = t[1];
+    t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3); o[6] = t[0]; o[7] = t[1];
+}
+
+// Dequantized value of a single magnitude m under the block's scale.
+__device__ __forceinline__ float requant_mx(float m, float sc) {
+    const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, m, m, sc, 0);
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, sc, 0)[0];
+}
+
+__device__ __forceinline__ float requant_ue(float m, const UeScale& s) {
+    const float y = s.fast ? div_rn(m, s.d, s.r) : m / s.d;
+    const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y, y, 1.0f, 0);
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0)[0] * s.d;
+}
+
+// ------------------------------------------------------------ tensor terms
+struct Acc {
+    double nonmax = 0.0, max = 0.0, zero = 0.0, sumsq = 0.0;
+    long long nzero = 0;
+};
+
+// Each workgroup writes its binary64 partial terms to partials[blockIdx.x]; a
+// separate one-workgroup kernel (k_finalize) sums them in index order.  The
+// kernel boundary is what makes the partials visible across XCDs, so no
+// device-scope fence (an L2 write-back per workgroup) is needed here.
+__device__ void write_partial(const Acc& a, double* partials) {
+    __shared__ double s_acc[kWaves][4];
+    __shared__ long long s_cnt[kWaves];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const double t0 = wave_sum(a.nonmax), t1 = wave_sum(a.max), t2 = wave_sum(a.zero),
+                 t3 = wave_sum(a.sumsq);
+    const long long tc = wave_sum_i64(a.nzero);
+    if (lane == 0) {
+        s_acc[wave][0] = t0; s_acc[wave][1] = t1; s_acc[wave][2] = t2; s_acc[wave][3] = t3;
+        s_cnt[wave] = tc;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double* p = partials + 5 * (size_t)blockIdx.x;
+        for (int k = 0; k < 4; ++k) {
+            double s = 0.0;
+            for (int w = 0; w < kWaves; ++w) s += s_acc[w][k];
+            p[k] = s;
+        }
+        long long c = 0;
+        for (int w = 0; w < kWaves; ++w) c += s_cnt[w];
+        reinterpret_cast<long long*>(p)[4] = c;
+    }
+}
+
+// Fixed-order sum of G workgroup partials into the fp4q_stats struct
+// (one workgroup of kThreads threads).
+__global__ __launch_bounds__(kThreads) void k_finalize(const double* partials, int G, void* stats,
+                                                       long long n_blocks) {
+    __shared__ double s_red[kThreads];
+    __shared__ long long s_redc[kThreads];
+    double* out = static_cast<double*>(stats);
+    for (int k = 0; k < 5; ++k) {
+        double s = 0.0;
+        long long c = 0;
+        for (int i = threadIdx.x; i < G; i += kThreads) {
+            if (k < 4) s += partials[5 * (size_t)i + k];
+            else c += reinterpret_cast<const long long*>(partials + 5 * (size_t)i)[4];
+        }
+        s_red[threadIdx.x] = s;
+        s_redc[threadIdx.x] = c;
+        __syncthreads();
+        for (int w = kThreads / 2; w > 0; w >>= 1) {
+            if (threadIdx.x < w) {
+                s_red[threadIdx.x] = s_red[threadIdx.x] + s_red[threadIdx.x + w];
+                s_redc[threadIdx.x] += s_redc[threadIdx.x + w];
+            }
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) {
+            if (k < 4) out[k] = s_red[0];
+            else {
+                reinterpret_cast<long long*>(out)[4] = n_blocks;
+                reinterpret_cast<long long*>(out)[5] = s_redc[0];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------ quantize
+struct QParams {
+    const void* x;
+    int64_t n, n_tiles, n_blocks;
+    uint8_t* codes;
+    uint8_t* scales;
+    float* block_mse;
+    int mse_kind;
+    int fmt;   // UE kernels: 1 UE4M3, 2 UE5M3
+    int gsrc;  // 0: g = 1, 1: g = *g_in, 2: g from the amax partials
+    const float* g_in;
+    float* g_out;
+    const uint32_t* amax_part;
+    int n_amax;
+    double* partials;
+    void* stats;
+};
+
+// Per-tensor scale from the amax pre-pass partials: g = RN32(amax / 2688),
+// 1 when that is not positive.
+__device__ float dynamic_g(const uint32_t* part, int n_part, float* g_out) {
+    __shared__ uint32_t s_m[kWaves];
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < n_part; i += kThreads) m = max(m, part[i]);
+    m = wave_max(m);
+    if (threadIdx.x % kWave == 0) s_m[threadIdx.x / kWave] = m;
+    __syncthreads();
+    uint32_t mm = s_m[0];
+    for (int w = 1; w < kWaves; ++w) mm = max(mm, s_m[w]);
+    float g = __uint_as_float(mm) / 2688.0f;
+    if (!(g > 0.0f)) g = 1.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && g_out) *g_out = g;
+    return g;
+}
+
+// Per-kernel UE scale context: g, D = RN32(6 g), rD = RN32(1 / D), whether the
+// corrected quotient m / D is usable, and the workgroup's decode-scale table.
+struct UeCtx {
+    float g, D, rD;
+    bool d_fast;
+    const float2* tab;
+};
+
+template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ>
+__device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int64_t base, const QParams& p,
+                                               const UeCtx& ue, int gl, Acc& acc) {
+    constexpr int L = B / kLaneElems;
+    constexpr bool kPackedBf16 = (XT == 0) && (ROT == 0);
+    const bool valid = base < p.n;
+    float v[8];
+    uint32_t lane_max;
+    if constexpr (kPackedBf16) {
+        // |x| of bf16 orders like its integer bits: max with packed u16 ops
+        const u16x2_t a0 = __builtin_bit_cast(u16x2_t, raw.w.x & 0x7FFF7FFFu);
+        const u16x2_t a1 = __builtin_bit_cast(u16x2_t, raw.w.y & 0x7FFF7FFFu);
+        const u16x2_t a2 = __builtin_bit_cast(u16x2_t, raw.w.z & 0x7FFF7FFFu);
+        const u16x2_t a3 = __builtin_bit_cast(u16x2_t, raw.w.w & 0x7FFF7FFFu);
+        const u16x2_t mm = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1),
+                                                     __builtin_elementwise_max(a2, a3));
+        lane_max = (uint32_t)max(mm[0], mm[1]) << 16;
+        if constexpr (ERR || FMT != kFmtMx) unpack<XT>(raw, v);
+    } else {
+        unpack<XT>(raw, v);
+        if constexpr (ROT != 0) rotate8<ROT>(v, gl);
+        float mf = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
+                         fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
+        lane_max = __float_as_uint(mf);
+    }
+    const uint32_t mbits = group_max<L>(lane_max);
+    const float m = __uint_as_float(mbits);
+
+    uint32_t cw, sbyte;
+    float xh[8];
+    float xh_m = 0.0f;
+    if constexpr (FMT == kFmtMx) {
+        const uint32_t F = mbits >> 23;
+        sbyte = F > 2u ? F - 2u : 0u;
+        const float sc = __uint_as_float(sbyte << 23);
+        if constexpr (kPackedBf16) cw = code_word_bf16(raw.w, sc);
+        else cw = code_word_f32(v, sc);
+        if constexpr (ERR) {
+            decode_word(cw, sc, xh);
+            xh_m = requant_mx(m, sc);
+        }
+    } else {
+        const UeScale s = ue_scale(m, ue.D, ue.rD, ue.d_fast, ue.tab, p.fmt);
+        sbyte = s.byte;
+        float y[8];
+        if (s.fast) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] = div_rn(v[i], s.d, s.r);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] = v[i] / s.d;
+        }
+        cw = code_word_f32(y, 1.0f);
+        if constexpr (ERR) {
+            decode_word(cw, 1.0f, xh);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xh[i] = xh[i] * s.d;
+            xh_m = requant_ue(m, s);
+        }
+    }
+    if (valid) {
+        *reinterpret_cast<uint32_t*>(p.codes + base / 2) = cw;
+        if (gl == 0) p.scales[base / B] = (uint8_t)sbyte;
+    }
+    if constexpr (ERR) {
+        double sse = 0.0, ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double e = (double)(v[i] - xh[i]);
+            sse = fma(e, e, sse);
+            if constexpr (SUMSQ) {
+                const double xv = (double)v[i];
+                ss = fma(xv, xv, ss);
+            }
+        }
+        sse = group_sum<L>(sse);
+        if constexpr (SUMSQ) ss = group_sum<L>(ss);
+        if (valid && gl == 0) {
+            const double em = (double)(m - xh_m);
+            const double mterm = em * em;
+            const bool zero = (m > 0.0f) && (xh_m == 0.0f);
+            if (p.block_mse) {
+                float o;
+                if (p.mse_kind == kMseRel) o = ss > 0.0 ? (float)(sse / ss) : 0.0f;
+                else o = (float)(sse * (1.0 / B));
+                p.block_mse[base / B] = o;
+            }
+            if (zero) {
+                acc.zero += sse;
+                acc.nzero += 1;
+            } else {
+                acc.max += mterm;
+                acc.nonmax += sse - mterm;
+            }
+            acc.sumsq += ss;
+        }
+    }
+}
+
+template <int XT>
+__device__ __forceinline__ void load_tile(Raw<XT> (&raw)[kUnroll], const void* x, int64_t t,
+                                          int lane, int64_t n) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+        raw[u] = load_chunk<XT>(x, t * kTile + u * kChunk + lane * kLaneElems, n);
+}
+
+template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ>
+__global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
+    constexpr int L = B / kLaneElems;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int gl = lane & (L - 1);
+    UeCtx ue{1.0f, 6.0f, 0.0f, true, nullptr};
+    if constexpr (FMT != kFmtMx) {
+        __shared__ float2 s_tab[kUeCodes];
+        float g = 1.0f;
+        if (p.gsrc == 1) g = *p.g_in;
+        else if (p.gsrc == 2) g = dynamic_g(p.amax_part, p.n_amax, p.g_out);
+        build_scale_table(s_tab, g, p.fmt);
+        ue.g = g;
+        ue.D = 6.0f * g;
+        ue.rD = 1.0f / ue.D;
+        ue.d_fast = ue.D >= 0x1p-96f && ue.D <= 0x1p100f;
+        ue.tab = s_tab;
+    }
+    const int G = gridDim.x;
+    const int sl = xcd_slice(blockIdx.x, G);
+    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
+    Acc acc;
+    // Software pipeline: the next tile's loads are in flight while this one is
+    // processed.  Loads never go past this wave's own range.
+    Raw<XT> cur[kUnroll];
+    int64_t t = t0 + wave;
+    if (t < t1) load_tile<XT>(cur, p.x, t, lane, p.n);
+    for (; t < t1; t += kWaves) {
+        Raw<XT> nxt[kUnroll];
+        const bool more = t + kWaves < t1;
+        if (more) load_tile<XT>(nxt, p.x, t + kWaves, lane, p.n);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ>(
+                cur[u], t * kTile + u * kChunk + lane * kLaneElems, p, ue, gl, acc);
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+        }
+    }
+    if (p.stats) write_partial(acc, p.partials);
+}
+
+// ------------------------------------------------------------ amax pre-pass
+struct AParams {
+    const void* x;
+    int64_t n, n_tiles;
+    uint32_t* part;
+};
+
+template <int XT, int ROT>
+__device__ __forceinline__ uint32_t chunk_absmax_bits(const Raw<XT>& raw, int gl) {
+    if constexpr (XT == 0 && ROT == 0) {
+        const u16x2_t a0 = __builtin_bit_cast(u16x2_t, raw.w.x & 0x7FFF7FFFu);
+        const u16x2_t a1 = __builtin_bit_cast(u16x2_t, raw.w.y & 0x7FFF7FFFu);
+        const u16x2_t a2 = __builtin_bit_cast(u16x2_t, raw.w.z & 0x7FFF7FFFu);
+        const u16x2_t a3 = __builtin_bit_cast(u16x2_t, raw.w.w & 0x7FFF7FFFu);
+        const u16x2_t mm = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1),
+                                                     __builtin_elementwise_max(a2, a3));
+        return (uint32_t)max(mm[0], mm[1]) << 16;
+    } else {
+        float v[8];
+        unpack<XT>(raw, v);
+        if constexpr (ROT != 0) rotate8<ROT>(v, gl);
+        float mf = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
+                         fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
+        return __float_as_uint(mf);
+    }
+}
+
+template <int XT, int ROT>
+__global__ __launch_bounds__(kThreads) void k_amax(AParams p) {
+    __shared__ uint32_t s_m[kWaves];
+    constexpr int L = ROT ? ROT / kLaneElems : 1;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int gl = lane & (L - 1);
+    const int G = gridDim.x;
+    const int sl = xcd_slice(blockIdx.x, G);
+    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
+    uint32_t mx = 0;
+    Raw<XT> cur[kUnroll];
+    int64_t t = t0 + wave;
+    if (t < t1) load_tile<XT>(cur, p.x, t, lane, p.n);
+    for (; t < t1; t += kWaves) {
+        Raw<XT> nxt[kUnroll];
+        const bool more = t + kWaves < t1;
+        if (more) load_tile<XT>(nxt, p.x, t + kWaves, lane, p.n);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) mx = max(mx, chunk_absmax_bits<XT, ROT>(cur[u], gl));
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+        }
+    }
+    mx = wave_max(mx);
+    if (lane == 0) s_m[wave] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t m = s_m[0];
+        for (int w = 1; w < kWaves; ++w) m = max(m, s_m[w]);
+        p.part[blockIdx.x] = m;
+    }
+}
+
+// ------------------------------------------------------------ dequantize
+struct DParams {
+    const uint8_t* codes;
+    const uint8_t* scales;
+    const float* g;
+    int fmt;
+    int64_t n, n_tiles;
+    void* out;
+};
+
+template <int FMT, int B, int ROT, int OT>
+__global__ __launch_bounds__(kThreads) void k_dequant(DParams p) {
+    constexpr int L = B / kLaneElems;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int gl = lane & (L - 1);
+    const float g = (FMT != kFmtMx && p.g) ? *p.g : 1.0f;
+    const int G = gridDim.x;
+    const int sl = xcd_slice(blockIdx.x, G);
+    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
+    for (int64_t t = t0 + wave; t < t1; t += kWaves) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t base = (t * kUnroll + u) * kChunk + lane * kLaneElems;
+            const bool valid = base < p.n;
+            uint32_t cw = 0, sbyte = 0;
+            if (valid) {
+                cw = *reinterpret_cast<const uint32_t*>(p.codes + base / 2);
+                sbyte = p.scales[base / B];
+            }
+            float xh[8];
+            if constexpr (FMT == kFmtMx) {
+                decode_word(cw, __uint_as_float(sbyte << 23), xh);
+            } else {
+                const float d = ue_decode(sbyte, p.fmt) * g;
+                decode_word(cw, 1.0f, xh);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xh[i] = xh[i] * d;
+            }
+            if constexpr (ROT != 0) rotate8<ROT>(xh, gl);
+            if (!valid) continue;
+            if constexpr (OT == 1) {
+                uint4* o = reinterpret_cast<uint4*>(static_cast<float*>(p.out) + base);
+                o[0] = make_uint4(__float_as_uint(xh[0]), __float_as_uint(xh[1]),
+                                  __float_as_uint(xh[2]), __float_as_uint(xh[3]));
+                o[1] = make_uint4(__float_as_uint(xh[4]), __float_as_uint(xh[5]),
+                                  __float_as_uint(xh[6]), __float_as_uint(xh[7]));
+            } else {
+                uint32_t h[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t b = __float_as_uint(xh[i]);
+                    h[i] = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;  // nearest, ties to even
+                }
+                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + base) =
+                    make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                               h[6] | (h[7] << 16));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ block MSE of stored codes
+struct MParams {
+    const void* x;
+    const uint8_t* codes;
+    const uint8_t* scales;
+    const float* g;
+    int fmt;
+    int64_t n, n_tiles, n_blocks;
+    float* block_mse;
+    int mse_kind;
+    double* partials;
+    void* stats;
+};
+
+template <int XT, int FMT, int B, int ROT, bool SUMSQ>
+__global__ __launch_bounds__(kThreads) void k_block_mse(MParams p) {
+    constexpr int L = B / kLaneElems;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int gl = lane & (L - 1);
+    const float g = (FMT != kFmtMx && p.g) ? *p.g : 1.0f;
+    const int G = gridDim.x;
+    const int sl = xcd_slice(blockIdx.x, G);
+    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
+    Acc acc;
+    for (int64_t t = t0 + wave; t < t1; t += kWaves) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t base = (t * kUnroll + u) * kChunk + lane * kLaneElems;
+            const bool valid = base < p.n;
+            const Raw<XT> raw = load_chunk<XT>(p.x, base, p.n);
+            uint32_t cw = 0, sbyte = 0;
+            if (valid) {
+                cw = *reinterpret_cast<const uint32_t*>(p.codes + base / 2);
+                sbyte = p.scales[base / B];
+            }
+            float v[8], xh[8];
+            unpack<XT>(raw, v);
+            if constexpr (ROT != 0) rotate8<ROT>(v, gl);
+            if constexpr (FMT == kFmtMx) {
+                decode_word(cw, __uint_as_float(sbyte << 23), xh);
+            } else {
+                const float d = ue_decode(sbyte, p.fmt) * g;
+                decode_word(cw, 1.0f, xh);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xh[i] = xh[i] * d;
+            }
+            float mf = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mf = fmaxf(mf, fabsf(v[i]));
+            const float m = __uint_as_float(group_max<L>(__float_as_uint(mf)));
+            double sse = 0.0, ss = 0.0;
+            uint32_t key = 0xFFu;  // lowest in-block index attaining m
+            float e_key = 0.0f;
+            uint32_t any_nz = 0;
+#pragma unroll
+            for (int i = 7; i >= 0; --i) {
+                const float e = v[i] - xh[i];
+                if (fabsf(v[i]) == m) {
+                    key = (uint32_t)(gl * 8 + i);
+                    e_key = e;
+                }
+                any_nz |= (xh[i] != 0.0f) ? 1u : 0u;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double e = (double)(v[i] - xh[i]);
+                sse = fma(e, e, sse);
+                if constexpr (SUMSQ) ss = fma((double)v[i], (double)v[i], ss);
+            }
+            sse = group_sum<L>(sse);
+            if constexpr (SUMSQ) ss = group_sum<L>(ss);
+            any_nz = group_max<L>(any_nz);
+#pragma unroll
+            for (int s = 1; s < L; s <<= 1) {
+                const uint32_t ok = (uint32_t)__shfl_xor((int)key, s);
+                const float oe = __shfl_xor(e_key, s);
+                if (ok < key) {
+                    key = ok;
+                    e_key = oe;
+                }
+            }
+            if (valid && gl == 0) {
+                const double mterm = (double)e_key * (double)e_key;
+                const bool zero = (m > 0.0f) && !any_nz;
+                if (p.block_mse) {
+                    float o;
+                    if (p.mse_kind == kMseRel) o = ss > 0.0 ? (float)(sse / ss) : 0.0f;
+                    else o = (float)(sse * (1.0 / B));
+                    p.block_mse[base / B] = o;
+                }
+                if (zero) {
+                    acc.zero += sse;
+                    acc.nzero += 1;
+                } else {
+                    acc.max += mterm;
+                    acc.nonmax += sse - mterm;
+                }
+                acc.sumsq += ss;
+            }
+        }
+    }
+    if (p.stats) write_partial(acc, p.partials);
+}
+
+// ------------------------------------------------------------ rotation only
+struct RParams {
+    const void* x;
+    int64_t n, n_tiles;
+    float* out;
+};
+
+template <int XT, int ROT>
+__global__ __launch_bounds__(kThreads) void k_rotate(RParams p) {
+    constexpr int L = ROT / kLaneElems;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int gl = lane & (L - 1);
+    const int G = gridDim.x;
+    const int sl = xcd_slice(blockIdx.x, G);
+    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
+    for (int64_t t = t0 + wave; t < t1; t += kWaves) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t base = (t * kUnroll + u) * kChunk + lane * kLaneElems;
+            const Raw<XT> raw = load_chunk<XT>(p.x, base, p.n);
+            float v[8];
+            unpack<XT>(raw, v);
+            rotate8<ROT>(v, gl);
+            if (base < p.n) {
+                uint4* o = reinterpret_cast<uint4*>(p.out + base);
+                o[0] = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                  __float_as_uint(v[2]), __float_as_uint(v[3]));
+                o[1] = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                  __float_as_uint(v[6]), __float_as_uint(v[7]));
+            }
+        }
+    }
+}
+
+// Empty tensors: zero the stats and/or set g = 1.
+__global__ void k_empty(void* stats, float* g_out) {
+    if (threadIdx.x != 0) return;
+    if (stats) {
+        double* s = static_cast<double*>(stats);
+        s[0] = s[1] = s[2] = s[3] = 0.0;
+        reinterpret_cast<long long*>(s)[4] = 0;
+        reinterpret_cast<long long*>(s)[5] = 0;
+    }
+    if (g_out) *g_out = 1.0f;
+}
+
+// ------------------------------------------------------------ host side
+int num_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    static int cache[64] = {0};
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    if (dev >= 0 && dev < 64) cache[dev] = cus;
+    return cus;
+}
+
+int64_t tiles_of(int64_t n) { return (n + kTile - 1) / kTile; }
+
+int grid_for(int64_t tiles) {
+    int64_t want = (tiles + kWaves - 1) / kWaves;
+    int64_t cap = (int64_t)num_cus() * kGroupsPerCU;
+    if (cap > kMaxGroups) cap = kMaxGroups;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    return (int)want;
+}
+
+int report(hipError_t e, const char* what, char* msg, size_t len) {
+    if (e == hipSuccess) return 0;
+    snprintf(msg, len, "%s: %s", what, hipGetErrorString(e));
+    return (int)e;
+}
+
+typedef void (*QuantKernel)(QParams);
+
+template <int XT, int FMT, int B, int ROT>
+QuantKernel pick_quant(bool err, bool sumsq) {
+    if (!err) return k_quantize<XT, FMT, B, ROT, false, false>;
+    if (!sumsq) return k_quantize<XT, FMT, B, ROT, true, false>;
+    return k_quantize<XT, FMT, B, ROT, true, true>;
+}
+
+template <int XT, int FMT>
+QuantKernel pick_quant_block(int block, int rotate, bool err, bool sumsq) {
+    if constexpr (FMT == kFmtMx) {
+        return rotate ? pick_quant<XT, FMT, 32, 32>(err, sumsq) : pick_quant<XT, FMT, 32, 0>(err, sumsq);
+    } else {
+        switch (block) {
+            case 8: return pick_quant<XT, FMT, 8, 0>(err, sumsq);
+            case 16: return rotate ? pick_quant<XT, FMT, 16, 16>(err, sumsq)
+                                   : pick_quant<XT, FMT, 16, 0>(err, sumsq);
+            case 32: return rotate ? pick_quant<XT, FMT, 32, 32>(err, sumsq)
+                                   : pick_quant<XT, FMT, 32, 0>(err, sumsq);
+            case 64: return pick_quant<XT, FMT, 64, 0>(err, sumsq);
+            case 128: return pick_quant<XT, FMT, 128, 0>(err, sumsq);
+            default: return pick_quant<XT, FMT, 256, 0>(err, sumsq);
+        }
+    }
+}
+
+typedef void (*AmaxKernel)(AParams);
+
+AmaxKernel pick_amax(int xt, int rotate) {
+    if (xt == 0) {
+        if (rotate == 16) return k_amax<0, 16>;
+        if (rotate == 32) return k_amax<0, 32>;
+        return k_amax<0, 0>;
+    }
+    if (rotate == 16) return k_amax<1, 16>;
+    if (rotate == 32) return k_amax<1, 32>;
+    return k_amax<1, 0>;
+}
+
+typedef void (*DequantKernel)(DParams);
+
+template <int FMT, int OT>
+DequantKernel pick_dequant_block(int block, int rotate) {
+    if constexpr (FMT == kFmtMx) {
+        return rotate ? k_dequant<FMT, 32, 32, OT> : k_dequant<FMT, 32, 0, OT>;
+    } else {
+        switch (block) {
+            case 8: return k_dequant<FMT, 8, 0, OT>;
+            case 16: return rotate ? k_dequant<FMT, 16, 16, OT> : k_dequant<FMT, 16, 0, OT>;
+            case 32: return rotate ? k_dequant<FMT, 32, 32, OT> : k_dequant<FMT, 32, 0, OT>;
+            case 64: return k_dequant<FMT, 64, 0, OT>;
+            case 128: return k_dequant<FMT, 128, 0, OT>;
+            default: return k_dequant<FMT, 256, 0, OT>;
+        }
+    }
+}
+
+typedef void (*MseKernel)(MParams);
+
+template <int XT, int FMT, int B, int ROT>
+MseKernel pick_mse(bool sumsq) {
+    return sumsq ? k_block_mse<XT, FMT, B, ROT, true> : k_block_mse<XT, FMT, B, ROT, false>;
+}
+
+template <int XT, int FMT>
+MseKernel pick_mse_block(int block, int rotate, bool sumsq) {
+    if constexpr (FMT == kFmtMx) {
+        return rotate ? pick_mse<XT, FMT, 32, 32>(sumsq) : pick_mse<XT, FMT, 32, 0>(sumsq);
+    } else {
+        switch (block) {
+            case 8: return pick_mse<XT, FMT, 8, 0>(sumsq);
+            case 16: return rotate ? pick_mse<XT, FMT, 16, 16>(sumsq) : pick_mse<XT, FMT, 16, 0>(sumsq);
+            case 32: return rotate ? pick_mse<XT, FMT, 32, 32>(sumsq) : pick_mse<XT, FMT, 32, 0>(sumsq);
+            case 64: return pick_mse<XT, FMT, 64, 0>(sumsq);
+            case 128: return pick_mse<XT, FMT, 128, 0>(sumsq);
+            default: return pick_mse<XT, FMT, 256, 0>(sumsq);
+        }
+    }
+}
+
+}  // namespace
+
+int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
+    hipStream_t st = static_cast<hipStream_t>(j.stream);
+    uint8_t* ws = static_cast<uint8_t*>(j.ws);
+    const bool dynamic = (j.fmt != kFmtMx) && (j.gmode == 1);
+    if (j.n == 0) {
+        if (j.stats || dynamic) {
+            hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, st, j.stats, dynamic ? j.g : nullptr);
+            return report(hipGetLastError(), "empty-tensor kernel", msg, msg_len);
+        }
+        return 0;
+    }
+    const int64_t tiles = tiles_of(j.n);
+    const int G = grid_for(tiles);
+    QParams p{};
+    p.x = j.x;
+    p.n = j.n;
+    p.n_tiles = tiles;
+    p.n_blocks = j.n / j.block;
+    p.codes = j.codes;
+    p.scales = j.scales;
+    p.block_mse = j.block_mse;
+    p.mse_kind = j.mse_kind;
+    p.fmt = j.fmt;
+    p.gsrc = 0;
+    p.stats = j.stats;
+    if (ws) {
+        p.partials = reinterpret_cast<double*>(ws + kWsPartials);
+    }
+    if (j.fmt != kFmtMx) {
+        if (j.gmode == 2) {
+            p.gsrc = 1;
+            p.g_in = j.g;
+        } else if (j.gmode == 1) {
+            AParams a{j.x, j.n, tiles, reinterpret_cast<uint32_t*>(ws + kWsAmax)};
+            hipLaunchKernelGGL(pick_amax(j.xt, j.rotate), dim3(G), dim3(kThreads), 0, st, a);
+            int rc = report(hipGetLastError(), "amax kernel launch", msg, msg_len);
+            if (rc) return rc;
+            p.gsrc = 2;
+            p.amax_part = a.part;
+            p.n_amax = G;
+            p.g_out = j.g;
+        }
+    }
+    const bool err = (j.block_mse != nullptr) || (j.stats != nullptr);
+    const bool sumsq = (j.stats != nullptr) || (j.block_mse != nullptr && j.mse_kind == kMseRel);
+    QuantKernel k;
+    if (j.fmt == kFmtMx)
+        k = j.xt == 0 ? pick_quant_block<0, kFmtMx>(32, j.rotate, err, sumsq)
+                      : pick_quant_block<1, kFmtMx>(32, j.rotate, err, sumsq);
+    else
+        k = j.xt == 0 ? pick_quant_block<0, kFmtUe4m3>(j.block, j.rotate, err, sumsq)
+                      : pick_quant_block<1, kFmtUe4m3>(j.block, j.rotate, err, sumsq);
+    hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
+    int rc = report(hipGetLastError(), "quantize kernel launch", msg, msg_len);
+    if (rc || !j.stats) return rc;
+    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kThreads), 0, st, p.partials, G, j.stats,
+                       (long long)p.n_blocks);
+    return report(hipGetLastError(), "finalize kernel launch", msg, msg_len);
+}
+
+int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len) {
+    if (j.n == 0) return 0;
+    hipStream_t st = static_cast<hipStream_t>(j.stream);
+    const int64_t tiles = tiles_of(j.n);
+    DParams p{j.codes, j.scales, j.g, j.fmt, j.n, tiles, j.out};
+    DequantKernel k;
+    if (j.fmt == kFmtMx)
+        k = j.ot == 1 ? pick_dequant_block<kFmtMx, 1>(32, j.rotate)
+                      : pick_dequant_block<kFmtMx, 0>(32, j.rotate);
+    else
+        k = j.ot == 1 ? pick_dequant_block<kFmtUe4m3, 1>(j.block, j.rotate)
+                      : pick_dequant_block<kFmtUe4m3, 0>(j.block, j.rotate);
+    hipLaunchKernelGGL(k, dim3(grid_for(tiles)), dim3(kThreads), 0, st, p);
+    return report(hipGetLastError(), "dequantize kernel launch", msg, msg_len);
+}
+
+int launch_block_mse(const MseJob& j, char* msg, size_t msg_len) {
+    hipStream_t st = static_cast<hipStream_t>(j.stream);
+    if (j.n == 0) {
+        if (j.stats) {
+            hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, st, j.stats, nullptr);
+            return report(hipGetLastError(), "empty-tensor kernel", msg, msg_len);
+        }
+        return 0;
+    }
+    uint8_t* ws = static_cast<uint8_t*>(j.ws);
+    const int64_t tiles = tiles_of(j.n);
+    MParams p{};
+    p.x = j.x;
+    p.codes = j.codes;
+    p.scales = j.scales;
+    p.g = j.g;
+    p.fmt = j.fmt;
+    p.n = j.n;
+    p.n_tiles = tiles;
+    p.n_blocks = j.n / j.block;
+    p.block_mse = j.block_mse;
+    p.mse_kind = j.mse_kind;
+    p.stats = j.stats;
+    if (ws) {
+        p.partials = reinterpret_cast<double*>(ws + kWsPartials);
+    }
+    const bool sumsq = (j.stats != nullptr) || (j.mse_kind == kMseRel);
+    MseKernel k;
+    if (j.fmt == kFmtMx)
+        k = j.xt == 0 ? pick_mse_block<0, kFmtMx>(32, j.rotate, sumsq)
+                      : pick_mse_block<1, kFmtMx>(32, j.rotate, sumsq);
+    else
+        k = j.xt == 0 ? pick_mse_block<0, kFmtUe4m3>(j.block, j.rotate, sumsq)
+                      : pick_mse_block<1, kFmtUe4m3>(j.block, j.rotate, sumsq);
+    const int G = grid_for(tiles);
+    hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
+    int rc = report(hipGetLastError(), "block-mse kernel launch", msg, msg_len);
+    if (rc || !j.stats) return rc;
+    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kThreads), 0, st, p.partials, G, j.stats,
+                       (long long)p.n_blocks);
+    return report(hipGetLastError(), "finalize kernel launch", msg, msg_len);
+}
+
+int launch_rotate(const RotateJob& j, char* msg, size_t msg_len) {
+    if (j.n == 0) return 0;
+    hipStream_t st = static_cast<hipStream_t>(j.stream);
+    const int64_t tiles = tiles_of(j.n);
+    RParams p{j.x, j.n, tiles, j.out};
+    void (*k)(RParams);
+    if (j.xt == 0) k = j.rotate == 16 ? k_rotate<0, 16> : k_rotate<0, 32>;
+    else k = j.rotate == 16 ? k_rotate<1, 16> : k_rotate<1, 32>;
+    hipLaunchKernelGGL(k, dim3(grid_for(tiles)), dim3(kThreads), 0, st, p);
+    return report(hipGetLastError(), "rotate kernel launch", msg, msg_len);
+}
+
+}  // namespace fp4q

@@ -1,0 +1,81 @@
+// Internal interface between the C ABI layer (fp4q_abi.cpp) and the kernel
+// launchers (fp4q_kernels.hip).  Plain types only; arguments arrive here
+// already validated.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+// Workspace layout (bytes from the start of ws).  Every slot is written before
+// it is read within one call, so the workspace needs no initial contents.
+constexpr size_t kWsAmax = 256;             // uint32 per-workgroup |x| maxima
+constexpr int kMaxGroups = 4096;            // upper bound on any grid size
+constexpr size_t kWsPartials = kWsAmax + 4 * kMaxGroups;  // 5 x 8 bytes per group
+constexpr size_t kWsBytes = kWsPartials + 40 * kMaxGroups;
+
+struct QuantJob {
+    const void* x;
+    int xt;            // 0 bf16, 1 f32
+    int64_t n;         // rows * cols
+    int block;         // 8..256
+    int fmt;           // 0 MXFP4, 1 UE4M3, 2 UE5M3
+    int gmode;         // 0 none, 1 dynamic, 2 given
+    float* g;          // device: dynamic out / given in
+    int rotate;        // 0, 16, 32
+    uint8_t* codes;
+    uint8_t* scales;
+    float* block_mse;  // nullable
+    int mse_kind;      // 0 abs, 1 rel
+    void* stats;       // nullable, fp4q_stats layout
+    void* ws;
+    void* stream;
+};
+
+struct DequantJob {
+    const uint8_t* codes;
+    const uint8_t* scales;
+    int fmt;
+    int block;
+    const float* g;    // nullable (UE4M3)
+    int64_t n;
+    int rotate;
+    void* out;
+    int ot;            // 0 bf16, 1 f32
+    void* stream;
+};
+
+struct MseJob {
+    const void* x;
+    int xt;
+    const uint8_t* codes;
+    const uint8_t* scales;
+    int fmt;
+    int block;
+    const float* g;    // nullable (UE4M3)
+    int64_t n;
+    int rotate;
+    float* block_mse;
+    int mse_kind;
+    void* stats;
+    void* ws;
+    void* stream;
+};
+
+struct RotateJob {
+    const void* x;
+    int xt;
+    int64_t n;
+    int rotate;
+    float* out;
+    void* stream;
+};
+
+// Each returns 0 on success, else a HIP error code; `msg` gets a description.
+int launch_quantize(const QuantJob& j, char* msg, size_t msg_len);
+int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len);
+int launch_block_mse(const MseJob& j, char* msg, size_t msg_len);
+int launch_rotate(const RotateJob& j, char* msg, size_t msg_len);
+
+}  // namespace fp4q

@@ -1,0 +1,251 @@
+"""GPU parity: the library (through its C ABI) against the oracle, element by
+element, on seeded inputs at sizes the oracle finishes quickly: several tiles
+of 2048 elements, ragged tails, empty tensors, exhaustive bf16 patterns and
+adversarial values (ties, signed zeros, subnormals, zero-rounding, saturation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import microscaling_fp4_quantization_amd as fq
+from parity_util import assert_block_mse, assert_stats, compare_quant, to_oracle_input
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def seeded(shape, sigma, seed, dtype):
+    rng = np.random.default_rng(seed)
+    a = (rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma))
+    return torch.from_numpy(a).to(dtype).to(DEV)
+
+
+def adversarial_rows(cols: int, seed: int) -> np.ndarray:
+    """Rows of awkward values: zeros, -0, subnormals, exact E2M1 midpoints,
+    tiny blocks, huge values, many equal maxima."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    rows.append(np.zeros(cols, np.float32))
+    rows.append(np.full(cols, -0.0, np.float32))
+    rows.append((rng.integers(1, 128, cols) * 2.0 ** -133).astype(np.float32))  # bf16 subnormals
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 4.0], np.float32)
+    rows.append((rng.choice(mids, cols) * np.where(rng.random(cols) < .5, -1, 1)).astype(np.float32))
+    rows.append((rng.standard_normal(cols) * 1e-4).astype(np.float32))          # zero-rounding (UE4M3)
+    rows.append((rng.standard_normal(cols) * 3e4).astype(np.float32))           # large
+    r = np.full(cols, 0.125, np.float32)
+    r[1::3] = -0.125
+    rows.append(r)                                                                # tied maxima
+    return np.stack(rows)
+
+
+SHAPES = [(67, 768), (5, 256), (1, 256), (133, 512)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rotate", [0, 32])
+@pytest.mark.parametrize("kind", [fq.MSE_ABS, fq.MSE_REL])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_mxfp4_parity(dtype, rotate, kind, shape):
+    x = seeded(shape, 0.02, [101, *shape], dtype)
+    q = fq.mxfp4_quantize(x, rotate, mse_kind=kind)
+    ref = oracle.quantize(to_oracle_input(x), oracle.FMT_MXFP4, 32, rotate=rotate, mse_kind=kind)
+    compare_quant(q, ref, xin=to_oracle_input(x))
+
+
+UE_CASES = [(b, 0) for b in (8, 16, 32, 64, 128, 256)] + [(16, 16), (32, 32)]
+
+
+@pytest.mark.parametrize("block,rotate", UE_CASES)
+@pytest.mark.parametrize("gmode", [fq.G_NONE, fq.G_DYNAMIC, fq.G_GIVEN])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_ue4m3_parity(block, rotate, gmode, dtype):
+    shape = (67, 768)
+    x = seeded(shape, 0.005, [102, block, gmode], dtype)
+    g = None
+    gval = None
+    if gmode == fq.G_GIVEN:
+        gval = 0.0137
+        g = torch.tensor([gval], dtype=torch.float32, device=DEV)
+    q = fq.nvfp4_quantize(x, block, fq.FMT_UE4M3, gmode, g, rotate, mse_kind=fq.MSE_ABS)
+    ref = oracle.quantize(to_oracle_input(x), oracle.FMT_UE4M3, block, gmode, gval, rotate)
+    compare_quant(q, ref, xin=to_oracle_input(x))
+
+
+@pytest.mark.parametrize("block", [8, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("kind", [fq.MSE_ABS, fq.MSE_REL])
+def test_ue5m3_parity(block, kind):
+    x = seeded((37, 1024), 0.002, [103, block], torch.bfloat16)
+    q = fq.nvfp4_quantize(x, block, fq.FMT_UE5M3, fq.G_NONE, None, 0, mse_kind=kind)
+    ref = oracle.quantize(to_oracle_input(x), oracle.FMT_UE5M3, block, mse_kind=kind)
+    compare_quant(q, ref, xin=to_oracle_input(x))
+
+
+def all_bf16_blocks(order: str, limit: float = np.inf) -> torch.Tensor:
+    """Every finite bf16 value once (those of magnitude >= limit replaced by 0)."""
+    bits = np.arange(65536, dtype=np.uint32) << 16
+    v = bits.view(np.float32).copy()
+    v[~np.isfinite(v) | (np.abs(v) >= limit)] = 0.0
+    if order == "shuffled":
+        v = np.random.default_rng(104).permutation(v)
+    else:  # sorted by magnitude: neighbours share blocks, so blocks sit near their maximum
+        v = v[np.argsort(np.abs(v), kind="stable")]
+    return torch.from_numpy(v.reshape(-1, 512)).to(torch.bfloat16).to(DEV)
+
+
+@pytest.mark.parametrize("order", ["shuffled", "sorted"])
+@pytest.mark.parametrize("rotate", [0, 32])
+def test_mxfp4_all_bf16_patterns(order, rotate):
+    # with rotation, inputs must keep the binary32 butterfly finite (|x| < 2^100)
+    x = all_bf16_blocks(order, 2.0 ** 100 if rotate else np.inf)
+    q = fq.mxfp4_quantize(x, rotate)
+    ref = oracle.quantize(to_oracle_input(x), oracle.FMT_MXFP4, 32, rotate=rotate)
+    compare_quant(q, ref, xin=to_oracle_input(x))
+
+
+@pytest.mark.parametrize("order", ["shuffled", "sorted"])
+@pytest.mark.parametrize("gval", [1.0, 2.0 ** -12, 0.0137, 3.7e-5, 1e4, 1e-30])
+def test_ue4m3_all_bf16_patterns(order, gval):
+    x = all_bf16_blocks(order)
+    g = torch.tensor([gval], dtype=torch.float32, device=DEV)
+    q = fq.nvfp4_quantize(x, 16, fq.FMT_UE4M3, fq.G_GIVEN, g)
+    ref = oracle.quantize(to_oracle_input(x), oracle.FMT_UE4M3, 16, oracle.GMODE_GIVEN, gval)
+    compare_quant(q, ref, xin=to_oracle_input(x))
+
+
+@pytest.mark.parametrize("fmt,block,gmode", [(0, 32, 0), (1, 16, 1), (1, 8, 0), (2, 16, 0)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_adversarial_values(fmt, block, gmode, dtype):
+    a = adversarial_rows(512, 105)
+    x = torch.from_numpy(np.concatenate([a, a * 2.0 ** -20, a * 2.0 ** 20])).to(dtype).to(DEV)
+    if fmt == 0:
+        q = fq.mxfp4_quantize(x)
+    else:
+        q = fq.nvfp4_quantize(x, block, fmt, gmode)
+    ref = oracle.quantize(to_oracle_input(x), fmt, block, gmode)
+    compare_quant(q, ref, xin=to_oracle_input(x))
+
+
+def test_ue4m3_division_near_rounding_boundaries():
+    """Inputs x = t * d (t an E2M1 rounding boundary, d a block decode scale),
+    nudged by -3..3 binary32 ulps, across many scales: the quotient's rounding
+    decides the code, so this exercises the division exactly where it matters."""
+    rng = np.random.default_rng(106)
+    bounds = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    g = np.float32(0.0137)
+    rows = []
+    for _ in range(64):
+        shat = np.float32(oracle.ue4m3_value(int(rng.integers(1, 0x7F))))
+        d = np.float32(shat * g)
+        row = np.empty(16 * 32, np.float32)
+        for blk in range(32):
+            vals = (bounds[rng.integers(0, 7, 16)] * d).astype(np.float32)
+            vals = vals.view(np.int32) + rng.integers(-3, 4, 16).astype(np.int32)
+            vals = vals.view(np.float32)
+            vals[0] = np.float32(6.0) * d  # pin the block scale to shat
+            row[blk * 16:(blk + 1) * 16] = vals * np.where(rng.random(16) < .5, -1, 1)
+        rows.append(row)
+    x = torch.from_numpy(np.stack(rows)).to(DEV)
+    gt = torch.tensor([float(g)], dtype=torch.float32, device=DEV)
+    q = fq.nvfp4_quantize(x, 16, fq.FMT_UE4M3, fq.G_GIVEN, gt)
+    ref = oracle.quantize(to_oracle_input(x), oracle.FMT_UE4M3, 16, oracle.GMODE_GIVEN, float(g))
+    compare_quant(q, ref, xin=to_oracle_input(x))
+
+
+@pytest.mark.parametrize("fmt,block,rotate", [(0, 32, 0), (0, 32, 32), (1, 16, 0), (1, 16, 16),
+                                              (1, 8, 0), (1, 256, 0), (2, 64, 0)])
+@pytest.mark.parametrize("ot", [torch.float32, torch.bfloat16])
+def test_dequantize_parity(fmt, block, rotate, ot):
+    """Codes and scales written by the oracle, dequantized by both sides."""
+    x = seeded((67, 1024), 0.02, [107, fmt, block], torch.bfloat16)
+    gm = oracle.GMODE_DYNAMIC if fmt == 1 else oracle.GMODE_NONE
+    ref_q = oracle.quantize(to_oracle_input(x), fmt, block, gm, rotate=rotate)
+    codes = torch.from_numpy(ref_q["codes"]).to(DEV)
+    scales = torch.from_numpy(ref_q["scales"]).to(DEV)
+    g = torch.tensor([ref_q["g"]], dtype=torch.float32, device=DEV) if fmt == 1 else None
+    out = fq.fp4_dequantize(codes, scales, fmt, block, g, rotate, out_dtype=ot)
+    ref = oracle.dequantize(ref_q["codes"], ref_q["scales"], fmt, block, ref_q["g"], *x.shape,
+                            rotate=rotate)
+    if ot == torch.float32:
+        np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    else:
+        np.testing.assert_array_equal(out.cpu().view(torch.int16).numpy().view(np.uint16),
+                                      oracle.to_bf16_bits(ref))
+
+
+@pytest.mark.parametrize("fmt,block,rotate", [(0, 32, 0), (0, 32, 32), (1, 16, 0), (1, 16, 16),
+                                              (1, 128, 0), (2, 8, 0)])
+@pytest.mark.parametrize("kind", [fq.MSE_ABS, fq.MSE_REL])
+def test_block_mse_of_arbitrary_codes(fmt, block, rotate, kind):
+    """Stored codes that no quantizer produced (random bytes), with ties for the
+    block maximum: the max-element term must follow the lowest index."""
+    rng = np.random.default_rng([108, fmt, block, rotate, kind])
+    xa = (rng.standard_normal((41, 512)) * 0.02).astype(np.float32)
+    xa[3, :] = 0.015625
+    x = torch.from_numpy(xa).to(torch.bfloat16).to(DEV)
+    codes = torch.from_numpy(rng.integers(0, 256, (41, 256), dtype=np.uint8)).to(DEV)
+    lo, hi = (100, 130) if fmt == 0 else (0x30, 0x60)
+    scales = torch.from_numpy(rng.integers(lo, hi, (41, 512 // block), dtype=np.uint8)).to(DEV)
+    gval = 0.5
+    g = torch.tensor([gval], dtype=torch.float32, device=DEV)
+    bm, st = fq.fp4_block_mse(x, codes, scales, fmt, block, g if fmt == 1 else None, rotate,
+                              mse_kind=kind)
+    rbm, acc, cnt = oracle.block_mse(to_oracle_input(x), codes.cpu().numpy(), scales.cpu().numpy(),
+                                     fmt, block, gval if fmt == 1 else 1.0, rotate, kind)
+    assert_block_mse(bm.cpu().numpy(), rbm)
+    assert_stats(fq.stats_dict(st), acc, cnt)
+
+
+@pytest.mark.parametrize("fmt,block,rotate", [(0, 32, 0), (1, 16, 16), (0, 32, 32)])
+def test_block_mse_equals_fused(fmt, block, rotate):
+    x = seeded((67, 1024), 0.02, [109, fmt], torch.bfloat16)
+    if fmt == 0:
+        q = fq.mxfp4_quantize(x, rotate, mse_kind=fq.MSE_REL)
+    else:
+        q = fq.nvfp4_quantize(x, block, fmt, fq.G_DYNAMIC, None, rotate, mse_kind=fq.MSE_REL)
+    bm, st = fq.fp4_block_mse(x, q.codes, q.scales, fmt, block, q.g, rotate, mse_kind=fq.MSE_REL)
+    assert torch.equal(bm, q.block_mse)
+    assert fq.stats_dict(st) == fq.stats_dict(q.stats)
+
+
+@pytest.mark.parametrize("n", [16, 32])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_hadamard_parity(n, dtype):
+    x = seeded((67, 1024), 1.0, [110, n], dtype)
+    out = fq.hadamard_block_rotate(x, n)
+    ref = oracle.hadamard(to_oracle_input(x), n)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_empty_tensors():
+    for shape in [(0, 32), (3, 0), (0, 0)]:
+        x = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+        q = fq.mxfp4_quantize(x)
+        s = fq.stats_dict(q.stats)
+        assert s == {"sse_nonmax": 0.0, "sse_max": 0.0, "sse_zero": 0.0, "sum_x2": 0.0,
+                     "n_blocks": 0, "n_zero_blocks": 0}
+        g = torch.full((1,), 7.0, device=DEV)
+        q = fq.nvfp4_quantize(x, 16, fq.FMT_UE4M3, fq.G_DYNAMIC, g)
+        assert g.item() == 1.0
+
+
+def test_deterministic_repeat():
+    x = seeded((301, 3584), 0.02, 111, torch.bfloat16)
+    a = fq.nvfp4_quantize(x, 16)
+    b = fq.nvfp4_quantize(x, 16)
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+    assert torch.equal(a.block_mse, b.block_mse)
+    assert torch.equal(a.stats.view(torch.int64), b.stats.view(torch.int64))
+    c = fq.mxfp4_quantize(x)
+    d = fq.mxfp4_quantize(x)
+    assert torch.equal(c.stats.view(torch.int64), d.stats.view(torch.int64))
+
+
+def test_workspace_reuse_across_grid_sizes():
+    """Consecutive calls with different grid sizes share one workspace."""
+    for shape in [(4864, 896), (7, 256), (2000, 3584), (1, 32)]:
+        x = seeded(shape, 0.02, [112, *shape], torch.bfloat16)
+        q = fq.mxfp4_quantize(x)
+        ref = oracle.quantize(to_oracle_input(x), oracle.FMT_MXFP4, 32)
+        assert_stats(fq.stats_dict(q.stats), ref["terms"], ref["counts"])
