@@ -82,6 +82,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen7")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run one plain device copy of the first tensor (a kernel of "
+                         "known traffic, for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -150,6 +153,11 @@ def main():
     us_launch = k0.elapsed_time(k1) * 1e3 / (reps * len(xs))
     bytes_launch = xs[0].numel() * (2 + 0.5 + 1 / 16 + 4 / 16)
     achieved = bytes_launch / (us_launch * 1e-6) / 1e9
+
+    if args.calibration_copy:
+        dst = torch.empty_like(xs[0])
+        dst.copy_(xs[0])
+        torch.cuda.synchronize()
 
     line = {
         "metric": METRIC,
