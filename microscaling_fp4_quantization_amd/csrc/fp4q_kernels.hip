@@ -42,15 +42,24 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kLaneElems = 8;
 constexpr int kChunk = kWave * kLaneElems;  // 512 elements per wave per chunk
 constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
-constexpr int kUnroll = 4;                  // chunks per wave iteration
+#ifndef FP4Q_UNROLL
+#define FP4Q_UNROLL 4
+#endif
+#ifndef FP4Q_TILES_PER_WAVE
+#define FP4Q_TILES_PER_WAVE 4
+#endif
+constexpr int kUnroll = FP4Q_UNROLL;        // chunks per wave iteration
 constexpr int kTile = kChunk * kUnroll;     // elements per wave iteration
-constexpr int kGroupsPerCU = 8;
+// Grid sizing: enough workgroups that each wave streams about this many tiles.
+// Many short-lived waves keep more loads in flight than a few long loops.
+constexpr int kTilesPerWave = FP4Q_TILES_PER_WAVE;
 
 constexpr int kFmtMx = 0;
 constexpr int kFmtUe4m3 = 1;
@@ -140,20 +149,28 @@ struct Raw<1> {  // 8 fp32
     uint4 a, b;
 };
 
+// 16-byte streaming load: the input is read once, so it is marked
+// nontemporal and does not displace other cached data.
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Lanes past the end (base >= n) load the tensor's first 8 elements instead,
+// so every load is unconditional (no branch, so the compiler can wait for each
+// chunk separately).  Such lanes make up whole blocks of their own -- n is a
+// multiple of the block size -- and nothing computed from them is stored or
+// counted.
 template <int XT>
 __device__ __forceinline__ Raw<XT> load_chunk(const void* x, int64_t base, int64_t n) {
     Raw<XT> r;
+    const int64_t at = base < n ? base : 0;
     if constexpr (XT == 0) {
-        r.w = make_uint4(0, 0, 0, 0);
-        if (base < n) r.w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + base);
+        r.w = load16_stream(static_cast<const uint16_t*>(x) + at);
     } else {
-        r.a = make_uint4(0, 0, 0, 0);
-        r.b = r.a;
-        if (base < n) {
-            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + base);
-            r.a = p[0];
-            r.b = p[1];
-        }
+        const float* p = static_cast<const float*>(x) + at;
+        r.a = load16_stream(p);
+        r.b = load16_stream(p + 4);
     }
     return r;
 }
@@ -213,13 +230,21 @@ __device__ __forceinline__ void rotate8(float (&v)[8], int gl) {
 // normal value the binary32 significand is rounded to 3 bits in place (the
 // rounded bits then read directly as the byte, after removing the exponent
 // bias difference); below it the value is a multiple of the subnormal step.
-__device__ __forceinline__ uint32_t ue_encode(float s, int fmt) {
-    const bool e4 = (fmt == kFmtUe4m3);
+__device__ __forceinline__ uint32_t ue5m3_encode(float s) {
     const uint32_t b = __float_as_uint(s);
-    const uint32_t normal = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (e4 ? 960u : 896u);
-    const uint32_t sub = (uint32_t)__builtin_rintf(s * (e4 ? 0x1p9f : 0x1p17f));
-    const uint32_t byte = s < (e4 ? 0x1p-6f : 0x1p-14f) ? sub : normal;
-    return min(byte, e4 ? 0x7Eu : 0xF7u);
+    const uint32_t normal = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - 896u;
+    const uint32_t sub = (uint32_t)__builtin_rintf(s * 0x1p17f);
+    const uint32_t byte = s < 0x1p-14f ? sub : normal;
+    return min(byte, 0xF7u);
+}
+
+// UE4M3 uses the hardware OCP E4M3 conversion (round to nearest even, with
+// subnormals); it gives the NaN code 0x7F from 464 up instead of saturating,
+// so the byte is clamped to 0x7E (448).
+__device__ __forceinline__ uint32_t ue_encode(float s, int fmt) {
+    if (fmt == kFmtUe4m3)
+        return min((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s, 0.0f, 0, false) & 0xFFu, 0x7Eu);
+    return ue5m3_encode(s);
 }
 
 __device__ __forceinline__ float ue_decode(uint32_t byte, int fmt) {
@@ -239,14 +264,22 @@ __device__ __forceinline__ float div_rn(float x, float d, float r) {
 }
 
 // Per-workgroup table of decode scales: for every scale byte c, d_c =
-// RN32(s_hat_c * g) and r_c = RN32(1 / d_c) (0 when d_c = 0).
+// RN32(s_hat_c * g), r_c = RN32(1 / d_c) (0 when d_c = 0) and lim_c, the
+// largest block maximum for which the FMA-corrected quotients are exact:
+// 4096 d_c when d_c is in [2^-96, 2^100], infinity when d_c = 0 (the quotients
+// are then zeros of x's sign), and -1 (never) otherwise.  Only the saturating
+// top code can exceed 4096 d_c; every other code has m / d_c below 9.
 constexpr int kUeCodes = 256;  // covers UE4M3 (127 codes) and UE5M3 (248)
 
-__device__ __forceinline__ void build_scale_table(float2* tab, float g, int fmt) {
+__device__ __forceinline__ void build_scale_table(float4* tab, float g, int fmt) {
     const int n_codes = (fmt == kFmtUe4m3) ? 0x7F : 0xF8;
     for (int c = threadIdx.x; c < n_codes; c += kThreads) {
         const float d = ue_decode((uint32_t)c, fmt) * g;
-        tab[c] = make_float2(d, d > 0.0f ? 1.0f / d : 0.0f);
+        const float r = d > 0.0f ? 1.0f / d : 0.0f;
+        float lim = -1.0f;
+        if (d == 0.0f) lim = __builtin_inff();
+        else if (d >= 0x1p-96f && d <= 0x1p100f) lim = d * 4096.0f;
+        tab[c] = make_float4(d, r, lim, 0.0f);
     }
     __syncthreads();
 }
@@ -262,15 +295,18 @@ struct UeScale {
 // [2^-96, 2^100] and m / D <= 4096, which covers every unsaturated block),
 // else a plain division.
 __device__ __forceinline__ UeScale ue_scale(float m, float D, float rD, bool d_fast,
-                                            const float2* tab, int fmt) {
+                                            const float4* tab, int fmt) {
     UeScale st;
     float s = div_rn(m, D, rD);
-    if (!(d_fast && s <= 4096.0f)) s = m / D;
+    const bool slow = !(d_fast && s <= 4096.0f);
+    if (__builtin_amdgcn_ballot_w64(slow)) {  // wave-uniform: keeps the division off the fast path
+        if (slow) s = m / D;
+    }
     st.byte = ue_encode(s, fmt);
-    const float2 dr = tab[st.byte];
-    st.d = dr.x;
-    st.r = dr.y;
-    st.fast = (st.d == 0.0f) || (st.d >= 0x1p-96f && st.d <= 0x1p100f && m <= st.d * 4096.0f);
+    const float4 e = tab[st.byte];
+    st.d = e.x;
+    st.r = e.y;
+    st.fast = m <= e.z;
     return st;
 }
 
@@ -320,10 +356,10 @@ struct Acc {
     long long nzero = 0;
 };
 
-// Each workgroup writes its binary64 partial terms to partials[blockIdx.x]; a
-// separate one-workgroup kernel (k_finalize) sums them in index order.  The
-// kernel boundary is what makes the partials visible across XCDs, so no
-// device-scope fence (an L2 write-back per workgroup) is needed here.
+// Each workgroup writes its binary64 partial terms to slot blockIdx.x of the
+// partial arrays; a separate one-workgroup kernel (k_finalize) sums them in
+// index order.  The kernel boundary is what makes the partials visible across
+// XCDs, so no device-scope fence (an L2 write-back per workgroup) is needed.
 __device__ void write_partial(const Acc& a, double* partials) {
     __shared__ double s_acc[kWaves][4];
     __shared__ long long s_cnt[kWaves];
@@ -336,51 +372,61 @@ __device__ void write_partial(const Acc& a, double* partials) {
         s_cnt[wave] = tc;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        double* p = partials + 5 * (size_t)blockIdx.x;
-        for (int k = 0; k < 4; ++k) {
+    if (threadIdx.x < 5) {
+        const int k = threadIdx.x;
+        double* slot = partials + (size_t)k * kMaxGroups + blockIdx.x;
+        if (k < 4) {
             double s = 0.0;
             for (int w = 0; w < kWaves; ++w) s += s_acc[w][k];
-            p[k] = s;
+            *slot = s;
+        } else {
+            long long c = 0;
+            for (int w = 0; w < kWaves; ++w) c += s_cnt[w];
+            *reinterpret_cast<long long*>(slot) = c;
         }
-        long long c = 0;
-        for (int w = 0; w < kWaves; ++w) c += s_cnt[w];
-        reinterpret_cast<long long*>(p)[4] = c;
     }
 }
 
-// Fixed-order sum of G workgroup partials into the fp4q_stats struct
-// (one workgroup of kThreads threads).
+// Fixed-order sum of G workgroup partials into the fp4q_stats struct (one
+// workgroup): each thread sums a strided subset in index order, then a fixed
+// butterfly within each wave and the waves in order.
+// When sumsq_part is given (the amax pre-pass computed sum x^2), the sum x^2
+// term comes from it instead of the quantize partials.
 __global__ __launch_bounds__(kThreads) void k_finalize(const double* partials, int G, void* stats,
-                                                       long long n_blocks) {
-    __shared__ double s_red[kThreads];
-    __shared__ long long s_redc[kThreads];
-    double* out = static_cast<double*>(stats);
-    for (int k = 0; k < 5; ++k) {
-        double s = 0.0;
-        long long c = 0;
-        for (int i = threadIdx.x; i < G; i += kThreads) {
-            if (k < 4) s += partials[5 * (size_t)i + k];
-            else c += reinterpret_cast<const long long*>(partials + 5 * (size_t)i)[4];
+                                                       long long n_blocks,
+                                                       const double* sumsq_part) {
+    __shared__ double s_t[kWaves][4];
+    __shared__ long long s_c[kWaves];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    double t[4] = {0.0, 0.0, 0.0, 0.0};
+    long long c = 0;
+    const long long* cnt = reinterpret_cast<const long long*>(partials + 4 * (size_t)kMaxGroups);
+    for (int i = threadIdx.x; i < G; i += kThreads) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) t[k] += partials[(size_t)k * kMaxGroups + i];
+        t[3] += sumsq_part ? sumsq_part[i] : partials[(size_t)3 * kMaxGroups + i];
+        c += cnt[i];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = wave_sum(t[k]);
+    c = wave_sum_i64(c);
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s_t[wave][k] = t[k];
+        s_c[wave] = c;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double* out = static_cast<double*>(stats);
+        long long cz = 0;
+        for (int k = 0; k < 4; ++k) {
+            double s = 0.0;
+            for (int w = 0; w < kWaves; ++w) s += s_t[w][k];
+            out[k] = s;
         }
-        s_red[threadIdx.x] = s;
-        s_redc[threadIdx.x] = c;
-        __syncthreads();
-        for (int w = kThreads / 2; w > 0; w >>= 1) {
-            if (threadIdx.x < w) {
-                s_red[threadIdx.x] = s_red[threadIdx.x] + s_red[threadIdx.x + w];
-                s_redc[threadIdx.x] += s_redc[threadIdx.x + w];
-            }
-            __syncthreads();
-        }
-        if (threadIdx.x == 0) {
-            if (k < 4) out[k] = s_red[0];
-            else {
-                reinterpret_cast<long long*>(out)[4] = n_blocks;
-                reinterpret_cast<long long*>(out)[5] = s_redc[0];
-            }
-        }
-        __syncthreads();
+        for (int w = 0; w < kWaves; ++w) cz += s_c[w];
+        reinterpret_cast<long long*>(out)[4] = n_blocks;
+        reinterpret_cast<long long*>(out)[5] = cz;
     }
 }
 
@@ -392,39 +438,23 @@ struct QParams {
     uint8_t* scales;
     float* block_mse;
     int mse_kind;
-    int fmt;   // UE kernels: 1 UE4M3, 2 UE5M3
-    int gsrc;  // 0: g = 1, 1: g = *g_in, 2: g from the amax partials
-    const float* g_in;
-    float* g_out;
+    int fmt;            // UE kernels: 1 UE4M3, 2 UE5M3
+    const float* g_in;  // per-tensor scale (device), NULL for g = 1
+    // Dynamic mode: per-workgroup |x| maxima of the amax pass; every workgroup
+    // reduces them to g, and workgroup 0 also writes g to g_out.
     const uint32_t* amax_part;
     int n_amax;
+    float* g_out;
     double* partials;
     void* stats;
 };
-
-// Per-tensor scale from the amax pre-pass partials: g = RN32(amax / 2688),
-// 1 when that is not positive.
-__device__ float dynamic_g(const uint32_t* part, int n_part, float* g_out) {
-    __shared__ uint32_t s_m[kWaves];
-    uint32_t m = 0;
-    for (int i = threadIdx.x; i < n_part; i += kThreads) m = max(m, part[i]);
-    m = wave_max(m);
-    if (threadIdx.x % kWave == 0) s_m[threadIdx.x / kWave] = m;
-    __syncthreads();
-    uint32_t mm = s_m[0];
-    for (int w = 1; w < kWaves; ++w) mm = max(mm, s_m[w]);
-    float g = __uint_as_float(mm) / 2688.0f;
-    if (!(g > 0.0f)) g = 1.0f;
-    if (blockIdx.x == 0 && threadIdx.x == 0 && g_out) *g_out = g;
-    return g;
-}
 
 // Per-kernel UE scale context: g, D = RN32(6 g), rD = RN32(1 / D), whether the
 // corrected quotient m / D is usable, and the workgroup's decode-scale table.
 struct UeCtx {
     float g, D, rD;
     bool d_fast;
-    const float2* tab;
+    const float4* tab;
 };
 
 template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ>
@@ -534,17 +564,45 @@ __device__ __forceinline__ void load_tile(Raw<XT> (&raw)[kUnroll], const void* x
         raw[u] = load_chunk<XT>(x, t * kTile + u * kChunk + lane * kLaneElems, n);
 }
 
+// g = RN32(amax / 2688) (1 when that is not positive) from the amax pass's
+// per-workgroup maxima; every workgroup reduces the same values in the same
+// way, so all agree bit for bit.
+__device__ float dynamic_g(const uint32_t* part, int n_part) {
+    __shared__ uint32_t s_m[kWaves];
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < n_part; i += kThreads) m = max(m, part[i]);
+    m = wave_max(m);
+    if (threadIdx.x % kWave == 0) s_m[threadIdx.x / kWave] = m;
+    __syncthreads();
+    uint32_t mm = s_m[0];
+    for (int w = 1; w < kWaves; ++w) mm = max(mm, s_m[w]);
+    const float g = __uint_as_float(mm) / 2688.0f;
+    return g > 0.0f ? g : 1.0f;
+}
+
 template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ>
 __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
     constexpr int L = B / kLaneElems;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int gl = lane & (L - 1);
+    const int G = gridDim.x;
+    const int sl = xcd_slice(blockIdx.x, G);
+    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
+    // The first tile's loads go out before the per-workgroup set-up below, so
+    // that set-up overlaps their latency.
+    int64_t t = t0 + wave;
+    Raw<XT> cur[kUnroll];
+    if (t < t1) load_tile<XT>(cur, p.x, t, lane, p.n);
     UeCtx ue{1.0f, 6.0f, 0.0f, true, nullptr};
     if constexpr (FMT != kFmtMx) {
-        __shared__ float2 s_tab[kUeCodes];
+        __shared__ float4 s_tab[kUeCodes];
         float g = 1.0f;
-        if (p.gsrc == 1) g = *p.g_in;
-        else if (p.gsrc == 2) g = dynamic_g(p.amax_part, p.n_amax, p.g_out);
+        if (p.amax_part) {
+            g = dynamic_g(p.amax_part, p.n_amax);
+            if (blockIdx.x == 0 && threadIdx.x == 0) *p.g_out = g;
+        } else if (p.g_in) {
+            g = *p.g_in;
+        }
         build_scale_table(s_tab, g, p.fmt);
         ue.g = g;
         ue.D = 6.0f * g;
@@ -552,41 +610,31 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
         ue.d_fast = ue.D >= 0x1p-96f && ue.D <= 0x1p100f;
         ue.tab = s_tab;
     }
-    const int G = gridDim.x;
-    const int sl = xcd_slice(blockIdx.x, G);
-    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
     Acc acc;
-    // Software pipeline: the next tile's loads are in flight while this one is
-    // processed.  Loads never go past this wave's own range.
-    Raw<XT> cur[kUnroll];
-    int64_t t = t0 + wave;
-    if (t < t1) load_tile<XT>(cur, p.x, t, lane, p.n);
     for (; t < t1; t += kWaves) {
-        Raw<XT> nxt[kUnroll];
-        const bool more = t + kWaves < t1;
-        if (more) load_tile<XT>(nxt, p.x, t + kWaves, lane, p.n);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
             quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ>(
                 cur[u], t * kTile + u * kChunk + lane * kLaneElems, p, ue, gl, acc);
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
-        }
+        if (t + kWaves < t1) load_tile<XT>(cur, p.x, t + kWaves, lane, p.n);
     }
     if (p.stats) write_partial(acc, p.partials);
 }
+
 
 // ------------------------------------------------------------ amax pre-pass
 struct AParams {
     const void* x;
     int64_t n, n_tiles;
     uint32_t* part;
+    double* sumsq;  // per-workgroup sum x^2 (binary64), written when non-NULL
 };
 
-template <int XT, int ROT>
-__device__ __forceinline__ uint32_t chunk_absmax_bits(const Raw<XT>& raw, int gl) {
-    if constexpr (XT == 0 && ROT == 0) {
+// Max |x| bits of a lane's 8 values (rotated first when ROT != 0); with
+// SUMSQ also adds their squares into ss (binary64).
+template <int XT, int ROT, bool SUMSQ>
+__device__ __forceinline__ uint32_t chunk_absmax_bits(const Raw<XT>& raw, int gl, double& ss) {
+    if constexpr (XT == 0 && ROT == 0 && !SUMSQ) {
         const u16x2_t a0 = __builtin_bit_cast(u16x2_t, raw.w.x & 0x7FFF7FFFu);
         const u16x2_t a1 = __builtin_bit_cast(u16x2_t, raw.w.y & 0x7FFF7FFFu);
         const u16x2_t a2 = __builtin_bit_cast(u16x2_t, raw.w.z & 0x7FFF7FFFu);
@@ -598,15 +646,20 @@ __device__ __forceinline__ uint32_t chunk_absmax_bits(const Raw<XT>& raw, int gl
         float v[8];
         unpack<XT>(raw, v);
         if constexpr (ROT != 0) rotate8<ROT>(v, gl);
+        if constexpr (SUMSQ) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fma((double)v[i], (double)v[i], ss);
+        }
         float mf = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
                          fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
         return __float_as_uint(mf);
     }
 }
 
-template <int XT, int ROT>
+template <int XT, int ROT, bool SUMSQ>
 __global__ __launch_bounds__(kThreads) void k_amax(AParams p) {
     __shared__ uint32_t s_m[kWaves];
+    __shared__ double s_ss[kWaves];
     constexpr int L = ROT ? ROT / kLaneElems : 1;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int gl = lane & (L - 1);
@@ -614,27 +667,37 @@ __global__ __launch_bounds__(kThreads) void k_amax(AParams p) {
     const int sl = xcd_slice(blockIdx.x, G);
     const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
     uint32_t mx = 0;
-    Raw<XT> cur[kUnroll];
-    int64_t t = t0 + wave;
-    if (t < t1) load_tile<XT>(cur, p.x, t, lane, p.n);
-    for (; t < t1; t += kWaves) {
-        Raw<XT> nxt[kUnroll];
-        const bool more = t + kWaves < t1;
-        if (more) load_tile<XT>(nxt, p.x, t + kWaves, lane, p.n);
+    double ss = 0.0;
+    for (int64_t t = t0 + wave; t < t1; t += kWaves) {
+        Raw<XT> cur[kUnroll];
+        load_tile<XT>(cur, p.x, t, lane, p.n);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) mx = max(mx, chunk_absmax_bits<XT, ROT>(cur[u], gl));
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+        for (int u = 0; u < kUnroll; ++u) {
+            // lanes past the end loaded stand-in data: leave them out
+            double cs = 0.0;
+            const uint32_t c = chunk_absmax_bits<XT, ROT, SUMSQ>(cur[u], gl, cs);
+            if (t * kTile + u * kChunk + lane * kLaneElems < p.n) {
+                mx = max(mx, c);
+                if constexpr (SUMSQ) ss += cs;
+            }
         }
     }
     mx = wave_max(mx);
-    if (lane == 0) s_m[wave] = mx;
+    if constexpr (SUMSQ) ss = wave_sum(ss);
+    if (lane == 0) {
+        s_m[wave] = mx;
+        s_ss[wave] = ss;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t m = s_m[0];
         for (int w = 1; w < kWaves; ++w) m = max(m, s_m[w]);
         p.part[blockIdx.x] = m;
+        if constexpr (SUMSQ) {
+            double t = 0.0;
+            for (int w = 0; w < kWaves; ++w) t += s_ss[w];
+            p.sumsq[blockIdx.x] = t;
+        }
     }
 }
 
@@ -850,26 +913,12 @@ __global__ void k_empty(void* stats, float* g_out) {
 }
 
 // ------------------------------------------------------------ host side
-int num_cus() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    static int cache[64] = {0};
-    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
-    if (dev >= 0 && dev < 64) cache[dev] = cus;
-    return cus;
-}
-
 int64_t tiles_of(int64_t n) { return (n + kTile - 1) / kTile; }
 
 int grid_for(int64_t tiles) {
-    int64_t want = (tiles + kWaves - 1) / kWaves;
-    int64_t cap = (int64_t)num_cus() * kGroupsPerCU;
-    if (cap > kMaxGroups) cap = kMaxGroups;
-    if (want > cap) want = cap;
+    const int64_t per_group = (int64_t)kWaves * kTilesPerWave;
+    int64_t want = (tiles + per_group - 1) / per_group;
+    if (want > kMaxGroups) want = kMaxGroups;
     if (want < 1) want = 1;
     return (int)want;
 }
@@ -909,15 +958,20 @@ QuantKernel pick_quant_block(int block, int rotate, bool err, bool sumsq) {
 
 typedef void (*AmaxKernel)(AParams);
 
-AmaxKernel pick_amax(int xt, int rotate) {
+template <bool SUMSQ>
+AmaxKernel pick_amax_t(int xt, int rotate) {
     if (xt == 0) {
-        if (rotate == 16) return k_amax<0, 16>;
-        if (rotate == 32) return k_amax<0, 32>;
-        return k_amax<0, 0>;
+        if (rotate == 16) return k_amax<0, 16, SUMSQ>;
+        if (rotate == 32) return k_amax<0, 32, SUMSQ>;
+        return k_amax<0, 0, SUMSQ>;
     }
-    if (rotate == 16) return k_amax<1, 16>;
-    if (rotate == 32) return k_amax<1, 32>;
-    return k_amax<1, 0>;
+    if (rotate == 16) return k_amax<1, 16, SUMSQ>;
+    if (rotate == 32) return k_amax<1, 32, SUMSQ>;
+    return k_amax<1, 0, SUMSQ>;
+}
+
+AmaxKernel pick_amax(int xt, int rotate, bool sumsq) {
+    return sumsq ? pick_amax_t<true>(xt, rotate) : pick_amax_t<false>(xt, rotate);
 }
 
 typedef void (*DequantKernel)(DParams);
@@ -986,28 +1040,33 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     p.block_mse = j.block_mse;
     p.mse_kind = j.mse_kind;
     p.fmt = j.fmt;
-    p.gsrc = 0;
+    p.g_in = nullptr;
     p.stats = j.stats;
-    if (ws) {
-        p.partials = reinterpret_cast<double*>(ws + kWsPartials);
-    }
-    if (j.fmt != kFmtMx) {
-        if (j.gmode == 2) {
-            p.gsrc = 1;
-            p.g_in = j.g;
-        } else if (j.gmode == 1) {
-            AParams a{j.x, j.n, tiles, reinterpret_cast<uint32_t*>(ws + kWsAmax)};
-            hipLaunchKernelGGL(pick_amax(j.xt, j.rotate), dim3(G), dim3(kThreads), 0, st, a);
+    if (ws) p.partials = reinterpret_cast<double*>(ws + kWsPartials);
+    const bool err = (j.block_mse != nullptr) || (j.stats != nullptr);
+    const bool rel = (j.block_mse != nullptr && j.mse_kind == kMseRel);
+    // In the dynamic mode the amax pass reads every element anyway; when sum x^2
+    // is wanted only for the tensor stats it is accumulated there, and the
+    // quantize kernel skips it.
+    const bool sumsq_in_amax = dynamic && j.stats != nullptr && !rel;
+    const bool sumsq = (j.stats != nullptr || rel) && !sumsq_in_amax;
+    const double* amax_sumsq = nullptr;
+    if (j.fmt != kFmtMx && j.gmode != 0) {
+        if (dynamic) {
+            AParams a{j.x, j.n, tiles, reinterpret_cast<uint32_t*>(ws + kWsAmax),
+                      sumsq_in_amax ? reinterpret_cast<double*>(ws + kWsAmaxSumsq) : nullptr};
+            amax_sumsq = a.sumsq;
+            hipLaunchKernelGGL(pick_amax(j.xt, j.rotate, sumsq_in_amax), dim3(G), dim3(kThreads),
+                               0, st, a);
             int rc = report(hipGetLastError(), "amax kernel launch", msg, msg_len);
             if (rc) return rc;
-            p.gsrc = 2;
             p.amax_part = a.part;
             p.n_amax = G;
             p.g_out = j.g;
+        } else {
+            p.g_in = j.g;
         }
     }
-    const bool err = (j.block_mse != nullptr) || (j.stats != nullptr);
-    const bool sumsq = (j.stats != nullptr) || (j.block_mse != nullptr && j.mse_kind == kMseRel);
     QuantKernel k;
     if (j.fmt == kFmtMx)
         k = j.xt == 0 ? pick_quant_block<0, kFmtMx>(32, j.rotate, err, sumsq)
@@ -1019,7 +1078,7 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     int rc = report(hipGetLastError(), "quantize kernel launch", msg, msg_len);
     if (rc || !j.stats) return rc;
     hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kThreads), 0, st, p.partials, G, j.stats,
-                       (long long)p.n_blocks);
+                       (long long)p.n_blocks, amax_sumsq);
     return report(hipGetLastError(), "finalize kernel launch", msg, msg_len);
 }
 
@@ -1078,7 +1137,7 @@ int launch_block_mse(const MseJob& j, char* msg, size_t msg_len) {
     int rc = report(hipGetLastError(), "block-mse kernel launch", msg, msg_len);
     if (rc || !j.stats) return rc;
     hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kThreads), 0, st, p.partials, G, j.stats,
-                       (long long)p.n_blocks);
+                       (long long)p.n_blocks, (const double*)nullptr);
     return report(hipGetLastError(), "finalize kernel launch", msg, msg_len);
 }
 

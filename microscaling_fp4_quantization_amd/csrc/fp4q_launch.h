@@ -10,10 +10,14 @@ namespace fp4q {
 
 // Workspace layout (bytes from the start of ws).  Every slot is written before
 // it is read within one call, so the workspace needs no initial contents.
-constexpr size_t kWsAmax = 256;             // uint32 per-workgroup |x| maxima
-constexpr int kMaxGroups = 4096;            // upper bound on any grid size
-constexpr size_t kWsPartials = kWsAmax + 4 * kMaxGroups;  // 5 x 8 bytes per group
-constexpr size_t kWsBytes = kWsPartials + 40 * kMaxGroups;
+constexpr int kMaxGroups = 16384;           // upper bound on any grid size
+constexpr size_t kWsAmax = 0;               // uint32 per-workgroup |x| maxima
+// Per-workgroup error terms, one array per term (structure of arrays):
+// [non-max | max | zero-rounding | sum x^2] as double, then the zero-block count.
+constexpr size_t kWsPartials = kWsAmax + 4 * (size_t)kMaxGroups;
+// sum x^2 per workgroup of the amax pre-pass (dynamic mode), as double
+constexpr size_t kWsAmaxSumsq = kWsPartials + 5 * 8 * (size_t)kMaxGroups;
+constexpr size_t kWsBytes = kWsAmaxSumsq + 8 * (size_t)kMaxGroups;
 
 struct QuantJob {
     const void* x;
