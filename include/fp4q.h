@@ -168,10 +168,12 @@ fp4q_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales, int32_t 
                            int32_t ot, void* stream);
 
 /*
- * Error split of stored codes against x (rotated first when rotate != 0):
- * block MSE and tensor terms exactly as the fused quantize calls report them.
- * The max-element term uses the lowest index attaining the block maximum, so
- * codes need not come from this library.  ws is needed when stats != NULL.
+ * Error split of stored codes against x (rotated first when rotate != 0), by
+ * the same definitions as the fused quantize calls: for codes and scales they
+ * wrote, block_mse and the block counts are bit-identical to theirs and the
+ * tensor terms equal theirs up to the order of summation.  The max-element
+ * term uses the lowest index attaining the block maximum, so codes need not
+ * come from this library.  ws is needed when stats != NULL.
  */
 fp4q_status fp4_block_mse(const void* x, int32_t xt, const uint8_t* codes, const uint8_t* scales,
                           int32_t fmt, int32_t block, const float* g, int64_t rows, int64_t cols,

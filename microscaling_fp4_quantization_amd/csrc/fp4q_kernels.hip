@@ -6,10 +6,12 @@
 // spans L = b / 8 lanes of one wavefront and a 64-lane wave covers a 512-element
 // chunk with perfectly coalesced loads and 4-byte code stores.  Block maxima and
 // error sums are reduced across the L lanes with DPP quad permutes and row
-// mirrors; nothing goes through LDS on the hot path.  A wave takes kUnroll
-// chunks per iteration (all loads issued before any use); the 4 waves of a
-// workgroup walk adjacent tiles of one contiguous slice of the tensor, and the
-// slices are laid out so that each XCD streams one contiguous eighth.
+// mirrors; nothing goes through LDS on the hot path.  The grid is one round of
+// resident workgroups; each wave owns one contiguous run of chunks (all runs
+// within one chunk of the same length), takes kUnroll chunks per iteration
+// with every load issued before any use, and the runs are numbered so that
+// each XCD streams one contiguous eighth of the tensor.  Memory is reached
+// through range-checked buffer resources, so ragged ends need no branches.
 //
 // Arithmetic (the rules the pages leave open are stated in include/fp4q.h):
 //   MXFP4: the E8M0 byte is the block maximum's binary32 exponent field minus 2
@@ -20,19 +22,21 @@
 //   UE4M3/UE5M3: s = m / D and the reciprocal r = 1 / d are correctly rounded
 //   divisions once per block; the element quotient RN32(x / d) uses the
 //   FMA-corrected reciprocal product of Markstein (IBM J. Res. Dev. 34(1), 1990):
-//   q = x r, rem = fma(-q, d, x), y = fma(rem, r, q), which returns the
-//   correctly rounded quotient when r = RN(1/d) and no intermediate leaves the
-//   normal range; blocks whose d or x / d leave the safe range use a plain
-//   division.  y is then coded with the same cvt instruction at scale 1.
+//   q = x r, n = fma(q, d, -x), y = fma(-n, r, q), which returns the correctly
+//   rounded quotient when r = RN(1/d) and no intermediate leaves the normal
+//   range (the negated remainder keeps the sign of a zero quotient); blocks
+//   whose d or x / d leave the safe range use a plain division.  y is then coded with the same cvt instruction at scale 1.
 //   Errors: e = x - x_hat in binary32 (exact for MXFP4 and for unsaturated
 //   UE4M3 blocks), squared and summed in binary64.  The max-element term is
 //   computed from the block maximum m itself (every element attaining m has
 //   the same error), the non-max term as block SSE minus it.
-//   Tensor terms: per-workgroup binary64 partials, summed in a fixed order by
-//   the last workgroup to finish, so results are bit-reproducible.
+//   Tensor terms: per-workgroup binary64 partials, summed in a fixed order by a
+//   one-workgroup finalize kernel, so results are bit-reproducible.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
+
+#include <mutex>
 
 #include "fp4q_launch.h"
 
@@ -52,14 +56,17 @@ constexpr int kThreads = kWave * kWaves;
 #ifndef FP4Q_UNROLL
 #define FP4Q_UNROLL 4
 #endif
-#ifndef FP4Q_TILES_PER_WAVE
-#define FP4Q_TILES_PER_WAVE 4
-#endif
 constexpr int kUnroll = FP4Q_UNROLL;        // chunks per wave iteration
-constexpr int kTile = kChunk * kUnroll;     // elements per wave iteration
-// Grid sizing: enough workgroups that each wave streams about this many tiles.
-// Many short-lived waves keep more loads in flight than a few long loops.
-constexpr int kTilesPerWave = FP4Q_TILES_PER_WAVE;
+// Quantize and amax grids: at least this many chunks per wave, and at most
+// kGridRounds rounds of resident workgroups.
+#ifndef FP4Q_MIN_CHUNKS_PER_WAVE
+#define FP4Q_MIN_CHUNKS_PER_WAVE 8
+#endif
+#ifndef FP4Q_GRID_ROUNDS
+#define FP4Q_GRID_ROUNDS 1
+#endif
+constexpr int kMinChunksPerWave = FP4Q_MIN_CHUNKS_PER_WAVE;
+constexpr int kGridRounds = FP4Q_GRID_ROUNDS;
 
 constexpr int kFmtMx = 0;
 constexpr int kFmtUe4m3 = 1;
@@ -149,30 +156,61 @@ struct Raw<1> {  // 8 fp32
     uint4 a, b;
 };
 
-// 16-byte streaming load: the input is read once, so it is marked
-// nontemporal and does not displace other cached data.
-__device__ __forceinline__ uint4 load16_stream(const void* p) {
-    const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+// ------------------------------------------------------------ buffer resources
+// The hot kernels address memory through raw buffer resources (base, size in
+// bytes) built per chunk group in scalar registers.  The hardware range check
+// then does the bounds work: a load past the size returns zeros without
+// touching memory and a store past it is dropped, so the ragged end of a
+// tensor and the leader-only stores need no per-lane branches, and lane
+// addresses are 32-bit offsets from a wave-uniform base.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;       // raw (stride 0) buffer, 32-bit data format
+constexpr int kDropped = (int)0x80000000;    // an offset past every range: access dropped
+constexpr int kNt = 2;                       // cache policy: nontemporal (read-once data)
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 buf_load16(Rsrc r, int off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNt);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Lanes past the end (base >= n) load the tensor's first 8 elements instead,
-// so every load is unconditional (no branch, so the compiler can wait for each
-// chunk separately).  Such lanes make up whole blocks of their own -- n is a
-// multiple of the block size -- and nothing computed from them is stored or
-// counted.
+// Work split shared by the streaming kernels: the tensor is a run of 512-element
+// chunks, and wave `wid` of `W` owns chunks [wid * C / W, (wid + 1) * C / W), a
+// contiguous range within one chunk of every other wave's length.  Waves are
+// numbered so that each XCD owns one contiguous eighth of the tensor.
+struct WaveRange {
+    int64_t c0, c1;
+};
+
+__device__ __forceinline__ WaveRange wave_range(int64_t n_chunks) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t W = (int64_t)gridDim.x * kWaves;
+    const int64_t wid = (int64_t)xcd_slice(blockIdx.x, gridDim.x) * kWaves + wave;
+    return {wid * n_chunks / W, (wid + 1) * n_chunks / W};
+}
+
+// Loads the kUnroll chunks starting at chunk c; chunks at or past c1 (another
+// wave's) and elements past n read as zeros.
 template <int XT>
-__device__ __forceinline__ Raw<XT> load_chunk(const void* x, int64_t base, int64_t n) {
-    Raw<XT> r;
-    const int64_t at = base < n ? base : 0;
-    if constexpr (XT == 0) {
-        r.w = load16_stream(static_cast<const uint16_t*>(x) + at);
-    } else {
-        const float* p = static_cast<const float*>(x) + at;
-        r.a = load16_stream(p);
-        r.b = load16_stream(p + 4);
+__device__ __forceinline__ void load_group(Raw<XT> (&raw)[kUnroll], const void* x, int64_t n,
+                                           int64_t c, int64_t c1, int lane) {
+    constexpr int E = XT == 0 ? 2 : 4;
+    const int64_t first = c * kChunk;
+    int64_t avail = (c1 - c < kUnroll ? c1 - c : kUnroll) * kChunk;
+    if (avail > n - first) avail = n - first;
+    const Rsrc r = make_rsrc(static_cast<const char*>(x) + first * E, avail * E);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if constexpr (XT == 0) {
+            raw[u].w = buf_load16(r, u * kChunk * E + lane * 16);
+        } else {
+            raw[u].a = buf_load16(r, u * kChunk * E + lane * 32);
+            raw[u].b = buf_load16(r, u * kChunk * E + lane * 32 + 16);
+        }
     }
-    return r;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -300,7 +338,11 @@ __device__ __forceinline__ UeScale ue_scale(float m, float D, float rD, bool d_f
     float s = div_rn(m, D, rD);
     const bool slow = !(d_fast && s <= 4096.0f);
     if (__builtin_amdgcn_ballot_w64(slow)) {  // wave-uniform: keeps the division off the fast path
-        if (slow) s = m / D;
+        // The empty volatile asm pins the division inside the branch; without it
+        // the compiler evaluates the full IEEE division on every block and selects.
+        float mm = m;
+        asm volatile("" : "+v"(mm));
+        if (slow) s = mm / D;
     }
     st.byte = ue_encode(s, fmt);
     const float4 e = tab[st.byte];
@@ -387,26 +429,44 @@ __device__ void write_partial(const Acc& a, double* partials) {
     }
 }
 
+// Sum of entries [0, n) of a, in index order per thread (thread i takes i,
+// i + 256, ...); each batch of 8 entries is loaded before any is added, so the
+// loads overlap.
+template <typename T>
+__device__ __forceinline__ T strided_sum(const T* a, int n) {
+    constexpr int kBatch = 8;
+    T t = 0;
+    for (int b = threadIdx.x; b < n; b += kThreads * kBatch) {
+        T v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int i = b + q * kThreads;
+            v[q] = a[i < n ? i : 0];
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            if (b + q * kThreads < n) t += v[q];
+    }
+    return t;
+}
+
 // Fixed-order sum of G workgroup partials into the fp4q_stats struct (one
-// workgroup): each thread sums a strided subset in index order, then a fixed
-// butterfly within each wave and the waves in order.
-// When sumsq_part is given (the amax pre-pass computed sum x^2), the sum x^2
-// term comes from it instead of the quantize partials.
+// workgroup): per-thread strided sums, then a fixed butterfly within each wave
+// and the waves in order.  When sumsq_part is given (the amax pre-pass computed
+// sum x^2 in its G_sumsq workgroups), the sum x^2 term comes from it instead of
+// the quantize partials.
 __global__ __launch_bounds__(kThreads) void k_finalize(const double* partials, int G, void* stats,
                                                        long long n_blocks,
-                                                       const double* sumsq_part) {
+                                                       const double* sumsq_part, int G_sumsq) {
     __shared__ double s_t[kWaves][4];
     __shared__ long long s_c[kWaves];
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    double t[4] = {0.0, 0.0, 0.0, 0.0};
-    long long c = 0;
-    const long long* cnt = reinterpret_cast<const long long*>(partials + 4 * (size_t)kMaxGroups);
-    for (int i = threadIdx.x; i < G; i += kThreads) {
+    double t[4];
 #pragma unroll
-        for (int k = 0; k < 3; ++k) t[k] += partials[(size_t)k * kMaxGroups + i];
-        t[3] += sumsq_part ? sumsq_part[i] : partials[(size_t)3 * kMaxGroups + i];
-        c += cnt[i];
-    }
+    for (int k = 0; k < 3; ++k) t[k] = strided_sum(partials + (size_t)k * kMaxGroups, G);
+    t[3] = sumsq_part ? strided_sum(sumsq_part, G_sumsq)
+                      : strided_sum(partials + 3 * (size_t)kMaxGroups, G);
+    long long c = strided_sum(reinterpret_cast<const long long*>(partials + 4 * (size_t)kMaxGroups), G);
 #pragma unroll
     for (int k = 0; k < 4; ++k) t[k] = wave_sum(t[k]);
     c = wave_sum_i64(c);
@@ -433,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(const double* partials, i
 // ------------------------------------------------------------ quantize
 struct QParams {
     const void* x;
-    int64_t n, n_tiles, n_blocks;
+    int64_t n, n_chunks, n_blocks;
     uint8_t* codes;
     uint8_t* scales;
     float* block_mse;
@@ -457,12 +517,35 @@ struct UeCtx {
     const float4* tab;
 };
 
+// Output windows of one chunk group (wave-uniform): codes, scale bytes and
+// per-block MSE of the group's valid blocks.
+struct QOut {
+    Rsrc codes, scales, mse;
+};
+
+template <int B>
+__device__ __forceinline__ QOut group_outputs(const QParams& p, int64_t c, int64_t c1) {
+    const int64_t first = c * kChunk;
+    int64_t avail = (c1 - c < kUnroll ? c1 - c : kUnroll) * kChunk;
+    if (avail > p.n - first) avail = p.n - first;
+    QOut o;
+    o.codes = make_rsrc(p.codes + first / 2, avail / 2);
+    o.scales = make_rsrc(p.scales + first / B, avail / B);
+    o.mse = make_rsrc(p.block_mse + first / B, p.block_mse ? avail / B * 4 : 0);
+    return o;
+}
+
+// One 512-element chunk: lane `lane` holds elements 8 lane .. 8 lane + 7 of it
+// and block lane / L of it (gl = lane % L).  Every lane of a block ends with the
+// block's results; the block's first lane stores its scale and MSE, and every
+// lane adds the block's terms to acc (the caller keeps only the first lanes').
 template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ>
-__device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int64_t base, const QParams& p,
-                                               const UeCtx& ue, int gl, Acc& acc) {
+__device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const QOut& o,
+                                               const QParams& p, const UeCtx& ue, int lane,
+                                               int gl, Acc& acc) {
     constexpr int L = B / kLaneElems;
+    constexpr int kBlocks = kChunk / B;
     constexpr bool kPackedBf16 = (XT == 0) && (ROT == 0);
-    const bool valid = base < p.n;
     float v[8];
     uint32_t lane_max;
     if constexpr (kPackedBf16) {
@@ -517,10 +600,9 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int64_t base,
             xh_m = requant_ue(m, s);
         }
     }
-    if (valid) {
-        *reinterpret_cast<uint32_t*>(p.codes + base / 2) = cw;
-        if (gl == 0) p.scales[base / B] = (uint8_t)sbyte;
-    }
+    const int blk = u * kBlocks + lane / L;  // block index within the group
+    __builtin_amdgcn_raw_buffer_store_b32(cw, o.codes, (u * kChunk + lane * kLaneElems) / 2, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, o.scales, gl == 0 ? blk : kDropped, 0, 0);
     if constexpr (ERR) {
         double sse = 0.0, ss = 0.0;
 #pragma unroll
@@ -534,34 +616,24 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int64_t base,
         }
         sse = group_sum<L>(sse);
         if constexpr (SUMSQ) ss = group_sum<L>(ss);
-        if (valid && gl == 0) {
-            const double em = (double)(m - xh_m);
-            const double mterm = em * em;
-            const bool zero = (m > 0.0f) && (xh_m == 0.0f);
-            if (p.block_mse) {
-                float o;
-                if (p.mse_kind == kMseRel) o = ss > 0.0 ? (float)(sse / ss) : 0.0f;
-                else o = (float)(sse * (1.0 / B));
-                p.block_mse[base / B] = o;
-            }
-            if (zero) {
-                acc.zero += sse;
-                acc.nzero += 1;
-            } else {
-                acc.max += mterm;
-                acc.nonmax += sse - mterm;
-            }
-            acc.sumsq += ss;
+        if (p.block_mse) {
+            float mse;
+            if (p.mse_kind == kMseRel) mse = ss > 0.0 ? (float)(sse / ss) : 0.0f;
+            else mse = (float)(sse * (1.0 / B));
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mse), o.mse,
+                                                  gl == 0 ? blk * 4 : kDropped, 0, 0);
         }
+        // Zero-filled lanes past the end form all-zero blocks, which add 0 to
+        // every term and are not zero-rounded (m = 0).
+        const double em = (double)(m - xh_m);
+        const double mterm = em * em;
+        const bool zero = (m > 0.0f) && (xh_m == 0.0f);
+        acc.zero += zero ? sse : 0.0;
+        acc.nzero += zero ? 1 : 0;
+        acc.max += zero ? 0.0 : mterm;
+        acc.nonmax += zero ? 0.0 : sse - mterm;
+        acc.sumsq += ss;
     }
-}
-
-template <int XT>
-__device__ __forceinline__ void load_tile(Raw<XT> (&raw)[kUnroll], const void* x, int64_t t,
-                                          int lane, int64_t n) {
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-        raw[u] = load_chunk<XT>(x, t * kTile + u * kChunk + lane * kLaneElems, n);
 }
 
 // g = RN32(amax / 2688) (1 when that is not positive) from the amax pass's
@@ -583,16 +655,13 @@ __device__ float dynamic_g(const uint32_t* part, int n_part) {
 template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ>
 __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
     constexpr int L = B / kLaneElems;
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
-    const int G = gridDim.x;
-    const int sl = xcd_slice(blockIdx.x, G);
-    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
-    // The first tile's loads go out before the per-workgroup set-up below, so
+    const WaveRange wr = wave_range(p.n_chunks);
+    // The first group's loads go out before the per-workgroup set-up below, so
     // that set-up overlaps their latency.
-    int64_t t = t0 + wave;
     Raw<XT> cur[kUnroll];
-    if (t < t1) load_tile<XT>(cur, p.x, t, lane, p.n);
+    if (wr.c0 < wr.c1) load_group<XT>(cur, p.x, p.n, wr.c0, wr.c1, lane);
     UeCtx ue{1.0f, 6.0f, 0.0f, true, nullptr};
     if constexpr (FMT != kFmtMx) {
         __shared__ float4 s_tab[kUeCodes];
@@ -611,21 +680,26 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
         ue.tab = s_tab;
     }
     Acc acc;
-    for (; t < t1; t += kWaves) {
+    for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
+        const QOut o = group_outputs<B>(p, c, wr.c1);
+        const int64_t left = wr.c1 - c;  // wave-uniform
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ>(
-                cur[u], t * kTile + u * kChunk + lane * kLaneElems, p, ue, gl, acc);
-        if (t + kWaves < t1) load_tile<XT>(cur, p.x, t + kWaves, lane, p.n);
+            if (u < left)
+                quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ>(cur[u], u, o, p, ue, lane, gl, acc);
+        if (c + kUnroll < wr.c1) load_group<XT>(cur, p.x, p.n, c + kUnroll, wr.c1, lane);
     }
-    if (p.stats) write_partial(acc, p.partials);
+    if (p.stats) {
+        if (gl != 0) acc = Acc{};  // every lane of a block holds its terms: keep one copy
+        write_partial(acc, p.partials);
+    }
 }
 
 
 // ------------------------------------------------------------ amax pre-pass
 struct AParams {
     const void* x;
-    int64_t n, n_tiles;
+    int64_t n, n_chunks;
     uint32_t* part;
     double* sumsq;  // per-workgroup sum x^2 (binary64), written when non-NULL
 };
@@ -663,21 +737,20 @@ __global__ __launch_bounds__(kThreads) void k_amax(AParams p) {
     constexpr int L = ROT ? ROT / kLaneElems : 1;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int gl = lane & (L - 1);
-    const int G = gridDim.x;
-    const int sl = xcd_slice(blockIdx.x, G);
-    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
+    const WaveRange wr = wave_range(p.n_chunks);
     uint32_t mx = 0;
     double ss = 0.0;
-    for (int64_t t = t0 + wave; t < t1; t += kWaves) {
+    // Elements past the wave's range read as zeros, which leave both the
+    // maximum and the sum of squares unchanged.
+    for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
         Raw<XT> cur[kUnroll];
-        load_tile<XT>(cur, p.x, t, lane, p.n);
+        load_group<XT>(cur, p.x, p.n, c, wr.c1, lane);
+        const int64_t left = wr.c1 - c;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            // lanes past the end loaded stand-in data: leave them out
-            double cs = 0.0;
-            const uint32_t c = chunk_absmax_bits<XT, ROT, SUMSQ>(cur[u], gl, cs);
-            if (t * kTile + u * kChunk + lane * kLaneElems < p.n) {
-                mx = max(mx, c);
+            if (u < left) {
+                double cs = 0.0;
+                mx = max(mx, chunk_absmax_bits<XT, ROT, SUMSQ>(cur[u], gl, cs));
                 if constexpr (SUMSQ) ss += cs;
             }
         }
@@ -707,46 +780,72 @@ struct DParams {
     const uint8_t* scales;
     const float* g;
     int fmt;
-    int64_t n, n_tiles;
+    int64_t n, n_chunks;
     void* out;
 };
+
+// Stored codes and scales of one chunk group; bytes past the group's valid
+// blocks read as zeros (code +0, scale byte 0).
+template <int B>
+__device__ __forceinline__ void load_codes(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                                           int64_t c, int64_t c1, int lane,
+                                           uint32_t (&cw)[kUnroll], uint32_t (&sb)[kUnroll]) {
+    constexpr int L = B / kLaneElems;
+    const int64_t first = c * kChunk;
+    int64_t avail = (c1 - c < kUnroll ? c1 - c : kUnroll) * kChunk;
+    if (avail > n - first) avail = n - first;
+    const Rsrc rc = make_rsrc(codes + first / 2, avail / 2);
+    const Rsrc rs = make_rsrc(scales + first / B, avail / B);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        cw[u] = __builtin_amdgcn_raw_buffer_load_b32(rc, (u * kChunk + lane * kLaneElems) / 2, 0, kNt);
+        sb[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, u * (kChunk / B) + lane / L, 0, 0);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void dequant_word(uint32_t cw, uint32_t sbyte, int fmt, float g,
+                                             float (&xh)[8]) {
+    if constexpr (FMT == kFmtMx) {
+        decode_word(cw, __uint_as_float(sbyte << 23), xh);
+    } else {
+        const float d = ue_decode(sbyte, fmt) * g;
+        decode_word(cw, 1.0f, xh);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xh[i] = xh[i] * d;
+    }
+}
 
 template <int FMT, int B, int ROT, int OT>
 __global__ __launch_bounds__(kThreads) void k_dequant(DParams p) {
     constexpr int L = B / kLaneElems;
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    constexpr int E = OT == 1 ? 4 : 2;
+    const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
     const float g = (FMT != kFmtMx && p.g) ? *p.g : 1.0f;
-    const int G = gridDim.x;
-    const int sl = xcd_slice(blockIdx.x, G);
-    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
-    for (int64_t t = t0 + wave; t < t1; t += kWaves) {
+    const WaveRange wr = wave_range(p.n_chunks);
+    for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
+        uint32_t cw[kUnroll], sb[kUnroll];
+        load_codes<B>(p.codes, p.scales, p.n, c, wr.c1, lane, cw, sb);
+        const int64_t first = c * kChunk;
+        int64_t avail = (wr.c1 - c < kUnroll ? wr.c1 - c : kUnroll) * kChunk;
+        if (avail > p.n - first) avail = p.n - first;
+        const Rsrc ro = make_rsrc(static_cast<char*>(p.out) + first * E, avail * E);
+        const int64_t left = wr.c1 - c;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t base = (t * kUnroll + u) * kChunk + lane * kLaneElems;
-            const bool valid = base < p.n;
-            uint32_t cw = 0, sbyte = 0;
-            if (valid) {
-                cw = *reinterpret_cast<const uint32_t*>(p.codes + base / 2);
-                sbyte = p.scales[base / B];
-            }
+            if (u >= left) continue;
             float xh[8];
-            if constexpr (FMT == kFmtMx) {
-                decode_word(cw, __uint_as_float(sbyte << 23), xh);
-            } else {
-                const float d = ue_decode(sbyte, p.fmt) * g;
-                decode_word(cw, 1.0f, xh);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) xh[i] = xh[i] * d;
-            }
+            dequant_word<FMT>(cw[u], sb[u], p.fmt, g, xh);
             if constexpr (ROT != 0) rotate8<ROT>(xh, gl);
-            if (!valid) continue;
+            const int off = (u * kChunk + lane * kLaneElems) * E;
             if constexpr (OT == 1) {
-                uint4* o = reinterpret_cast<uint4*>(static_cast<float*>(p.out) + base);
-                o[0] = make_uint4(__float_as_uint(xh[0]), __float_as_uint(xh[1]),
-                                  __float_as_uint(xh[2]), __float_as_uint(xh[3]));
-                o[1] = make_uint4(__float_as_uint(xh[4]), __float_as_uint(xh[5]),
-                                  __float_as_uint(xh[6]), __float_as_uint(xh[7]));
+                const u32x4_t a = {__float_as_uint(xh[0]), __float_as_uint(xh[1]),
+                                   __float_as_uint(xh[2]), __float_as_uint(xh[3])};
+                const u32x4_t b = {__float_as_uint(xh[4]), __float_as_uint(xh[5]),
+                                   __float_as_uint(xh[6]), __float_as_uint(xh[7])};
+                __builtin_amdgcn_raw_buffer_store_b128(a, ro, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(b, ro, off + 16, 0, 0);
             } else {
                 uint32_t h[8];
 #pragma unroll
@@ -754,9 +853,9 @@ __global__ __launch_bounds__(kThreads) void k_dequant(DParams p) {
                     const uint32_t b = __float_as_uint(xh[i]);
                     h[i] = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;  // nearest, ties to even
                 }
-                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + base) =
-                    make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                               h[6] | (h[7] << 16));
+                const u32x4_t w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                   h[6] | (h[7] << 16)};
+                __builtin_amdgcn_raw_buffer_store_b128(w, ro, off, 0, 0);
             }
         }
     }
@@ -769,45 +868,42 @@ struct MParams {
     const uint8_t* scales;
     const float* g;
     int fmt;
-    int64_t n, n_tiles, n_blocks;
+    int64_t n, n_chunks, n_blocks;
     float* block_mse;
     int mse_kind;
     double* partials;
     void* stats;
 };
 
+// Same work split, per-element arithmetic and accumulation order as
+// k_quantize, so the per-block MSE of codes that k_quantize wrote is
+// bit-identical to the value it reported.
 template <int XT, int FMT, int B, int ROT, bool SUMSQ>
 __global__ __launch_bounds__(kThreads) void k_block_mse(MParams p) {
     constexpr int L = B / kLaneElems;
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    constexpr int kBlocks = kChunk / B;
+    const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
     const float g = (FMT != kFmtMx && p.g) ? *p.g : 1.0f;
-    const int G = gridDim.x;
-    const int sl = xcd_slice(blockIdx.x, G);
-    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
+    const WaveRange wr = wave_range(p.n_chunks);
     Acc acc;
-    for (int64_t t = t0 + wave; t < t1; t += kWaves) {
+    for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
+        Raw<XT> raw[kUnroll];
+        uint32_t cw[kUnroll], sb[kUnroll];
+        load_group<XT>(raw, p.x, p.n, c, wr.c1, lane);
+        load_codes<B>(p.codes, p.scales, p.n, c, wr.c1, lane, cw, sb);
+        const int64_t first = c * kChunk;
+        int64_t avail = (wr.c1 - c < kUnroll ? wr.c1 - c : kUnroll) * kChunk;
+        if (avail > p.n - first) avail = p.n - first;
+        const Rsrc rm = make_rsrc(p.block_mse + first / B, p.block_mse ? avail / B * 4 : 0);
+        const int64_t left = wr.c1 - c;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t base = (t * kUnroll + u) * kChunk + lane * kLaneElems;
-            const bool valid = base < p.n;
-            const Raw<XT> raw = load_chunk<XT>(p.x, base, p.n);
-            uint32_t cw = 0, sbyte = 0;
-            if (valid) {
-                cw = *reinterpret_cast<const uint32_t*>(p.codes + base / 2);
-                sbyte = p.scales[base / B];
-            }
+            if (u >= left) continue;
             float v[8], xh[8];
-            unpack<XT>(raw, v);
+            unpack<XT>(raw[u], v);
             if constexpr (ROT != 0) rotate8<ROT>(v, gl);
-            if constexpr (FMT == kFmtMx) {
-                decode_word(cw, __uint_as_float(sbyte << 23), xh);
-            } else {
-                const float d = ue_decode(sbyte, p.fmt) * g;
-                decode_word(cw, 1.0f, xh);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) xh[i] = xh[i] * d;
-            }
+            dequant_word<FMT>(cw[u], sb[u], p.fmt, g, xh);
             float mf = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) mf = fmaxf(mf, fabsf(v[i]));
@@ -829,7 +925,10 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MParams p) {
             for (int i = 0; i < 8; ++i) {
                 const double e = (double)(v[i] - xh[i]);
                 sse = fma(e, e, sse);
-                if constexpr (SUMSQ) ss = fma((double)v[i], (double)v[i], ss);
+                if constexpr (SUMSQ) {
+                    const double xv = (double)v[i];
+                    ss = fma(xv, xv, ss);
+                }
             }
             sse = group_sum<L>(sse);
             if constexpr (SUMSQ) ss = group_sum<L>(ss);
@@ -843,59 +942,63 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MParams p) {
                     e_key = oe;
                 }
             }
-            if (valid && gl == 0) {
-                const double mterm = (double)e_key * (double)e_key;
-                const bool zero = (m > 0.0f) && !any_nz;
-                if (p.block_mse) {
-                    float o;
-                    if (p.mse_kind == kMseRel) o = ss > 0.0 ? (float)(sse / ss) : 0.0f;
-                    else o = (float)(sse * (1.0 / B));
-                    p.block_mse[base / B] = o;
-                }
-                if (zero) {
-                    acc.zero += sse;
-                    acc.nzero += 1;
-                } else {
-                    acc.max += mterm;
-                    acc.nonmax += sse - mterm;
-                }
-                acc.sumsq += ss;
+            if (p.block_mse) {
+                float mse;
+                if (p.mse_kind == kMseRel) mse = ss > 0.0 ? (float)(sse / ss) : 0.0f;
+                else mse = (float)(sse * (1.0 / B));
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mse), rm,
+                                                      gl == 0 ? (u * kBlocks + lane / L) * 4 : kDropped,
+                                                      0, 0);
             }
+            const double mterm = (double)e_key * (double)e_key;
+            const bool zero = (m > 0.0f) && !any_nz;
+            acc.zero += zero ? sse : 0.0;
+            acc.nzero += zero ? 1 : 0;
+            acc.max += zero ? 0.0 : mterm;
+            acc.nonmax += zero ? 0.0 : sse - mterm;
+            acc.sumsq += ss;
         }
     }
-    if (p.stats) write_partial(acc, p.partials);
+    if (p.stats) {
+        if (gl != 0) acc = Acc{};
+        write_partial(acc, p.partials);
+    }
 }
 
 // ------------------------------------------------------------ rotation only
 struct RParams {
     const void* x;
-    int64_t n, n_tiles;
+    int64_t n, n_chunks;
     float* out;
 };
 
 template <int XT, int ROT>
 __global__ __launch_bounds__(kThreads) void k_rotate(RParams p) {
     constexpr int L = ROT / kLaneElems;
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
-    const int G = gridDim.x;
-    const int sl = xcd_slice(blockIdx.x, G);
-    const int64_t t0 = (int64_t)sl * p.n_tiles / G, t1 = (int64_t)(sl + 1) * p.n_tiles / G;
-    for (int64_t t = t0 + wave; t < t1; t += kWaves) {
+    const WaveRange wr = wave_range(p.n_chunks);
+    for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
+        Raw<XT> raw[kUnroll];
+        load_group<XT>(raw, p.x, p.n, c, wr.c1, lane);
+        const int64_t first = c * kChunk;
+        int64_t avail = (wr.c1 - c < kUnroll ? wr.c1 - c : kUnroll) * kChunk;
+        if (avail > p.n - first) avail = p.n - first;
+        const Rsrc ro = make_rsrc(p.out + first, avail * 4);
+        const int64_t left = wr.c1 - c;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t base = (t * kUnroll + u) * kChunk + lane * kLaneElems;
-            const Raw<XT> raw = load_chunk<XT>(p.x, base, p.n);
+            if (u >= left) continue;
             float v[8];
-            unpack<XT>(raw, v);
+            unpack<XT>(raw[u], v);
             rotate8<ROT>(v, gl);
-            if (base < p.n) {
-                uint4* o = reinterpret_cast<uint4*>(p.out + base);
-                o[0] = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
-                                  __float_as_uint(v[2]), __float_as_uint(v[3]));
-                o[1] = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]),
-                                  __float_as_uint(v[6]), __float_as_uint(v[7]));
-            }
+            const int off = (u * kChunk + lane * kLaneElems) * 4;
+            const u32x4_t a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                               __float_as_uint(v[3])};
+            const u32x4_t b = {__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                               __float_as_uint(v[7])};
+            __builtin_amdgcn_raw_buffer_store_b128(a, ro, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(b, ro, off + 16, 0, 0);
         }
     }
 }
@@ -913,11 +1016,46 @@ __global__ void k_empty(void* stats, float* g_out) {
 }
 
 // ------------------------------------------------------------ host side
-int64_t tiles_of(int64_t n) { return (n + kTile - 1) / kTile; }
+int64_t chunks_of(int64_t n) { return (n + kChunk - 1) / kChunk; }
 
-int grid_for(int64_t tiles) {
-    const int64_t per_group = (int64_t)kWaves * kTilesPerWave;
-    int64_t want = (tiles + per_group - 1) / per_group;
+// Workgroups of `kernel` that fit on the current device at once (compute units
+// times the occupancy its registers and LDS allow), cached per device and kernel.
+int resident_groups(const void* kernel) {
+    struct Entry {
+        int dev;
+        const void* kernel;
+        int groups;
+    };
+    static std::mutex mu;
+    static Entry cache[256];
+    static int n_cache = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < n_cache; ++i)
+            if (cache[i].dev == dev && cache[i].kernel == kernel) return cache[i].groups;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
+        per_cu <= 0)
+        per_cu = 1;
+    const int groups = cus * per_cu;
+    std::lock_guard<std::mutex> lock(mu);
+    if (n_cache < 256) cache[n_cache++] = {dev, kernel, groups};
+    return groups;
+}
+
+// Grid of a streaming kernel over `chunks` 512-element chunks: one round of
+// resident workgroups (so no workgroup waits for a second round), fewer when
+// the tensor gives each wave under kMinChunksPerWave chunks.
+int grid_for_chunks(int64_t chunks, const void* kernel) {
+    int64_t want = (chunks + (int64_t)kWaves * kMinChunksPerWave - 1) / ((int64_t)kWaves * kMinChunksPerWave);
+    const int64_t cap = (int64_t)resident_groups(kernel) * kGridRounds;
+    if (want > cap) want = cap;
     if (want > kMaxGroups) want = kMaxGroups;
     if (want < 1) want = 1;
     return (int)want;
@@ -1028,12 +1166,11 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
         }
         return 0;
     }
-    const int64_t tiles = tiles_of(j.n);
-    const int G = grid_for(tiles);
+    const int64_t chunks = chunks_of(j.n);
     QParams p{};
     p.x = j.x;
     p.n = j.n;
-    p.n_tiles = tiles;
+    p.n_chunks = chunks;
     p.n_blocks = j.n / j.block;
     p.codes = j.codes;
     p.scales = j.scales;
@@ -1050,23 +1187,6 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     // quantize kernel skips it.
     const bool sumsq_in_amax = dynamic && j.stats != nullptr && !rel;
     const bool sumsq = (j.stats != nullptr || rel) && !sumsq_in_amax;
-    const double* amax_sumsq = nullptr;
-    if (j.fmt != kFmtMx && j.gmode != 0) {
-        if (dynamic) {
-            AParams a{j.x, j.n, tiles, reinterpret_cast<uint32_t*>(ws + kWsAmax),
-                      sumsq_in_amax ? reinterpret_cast<double*>(ws + kWsAmaxSumsq) : nullptr};
-            amax_sumsq = a.sumsq;
-            hipLaunchKernelGGL(pick_amax(j.xt, j.rotate, sumsq_in_amax), dim3(G), dim3(kThreads),
-                               0, st, a);
-            int rc = report(hipGetLastError(), "amax kernel launch", msg, msg_len);
-            if (rc) return rc;
-            p.amax_part = a.part;
-            p.n_amax = G;
-            p.g_out = j.g;
-        } else {
-            p.g_in = j.g;
-        }
-    }
     QuantKernel k;
     if (j.fmt == kFmtMx)
         k = j.xt == 0 ? pick_quant_block<0, kFmtMx>(32, j.rotate, err, sumsq)
@@ -1074,19 +1194,39 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     else
         k = j.xt == 0 ? pick_quant_block<0, kFmtUe4m3>(j.block, j.rotate, err, sumsq)
                       : pick_quant_block<1, kFmtUe4m3>(j.block, j.rotate, err, sumsq);
+    const int G = grid_for_chunks(chunks, reinterpret_cast<const void*>(k));
+    const double* amax_sumsq = nullptr;
+    int G_amax = 0;
+    if (j.fmt != kFmtMx && j.gmode != 0) {
+        if (dynamic) {
+            AParams a{j.x, j.n, chunks, reinterpret_cast<uint32_t*>(ws + kWsAmax),
+                      sumsq_in_amax ? reinterpret_cast<double*>(ws + kWsAmaxSumsq) : nullptr};
+            amax_sumsq = a.sumsq;
+            const AmaxKernel ka = pick_amax(j.xt, j.rotate, sumsq_in_amax);
+            G_amax = grid_for_chunks(chunks, reinterpret_cast<const void*>(ka));
+            hipLaunchKernelGGL(ka, dim3(G_amax), dim3(kThreads), 0, st, a);
+            int rc = report(hipGetLastError(), "amax kernel launch", msg, msg_len);
+            if (rc) return rc;
+            p.amax_part = a.part;
+            p.n_amax = G_amax;
+            p.g_out = j.g;
+        } else {
+            p.g_in = j.g;
+        }
+    }
     hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
     int rc = report(hipGetLastError(), "quantize kernel launch", msg, msg_len);
     if (rc || !j.stats) return rc;
     hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kThreads), 0, st, p.partials, G, j.stats,
-                       (long long)p.n_blocks, amax_sumsq);
+                       (long long)p.n_blocks, amax_sumsq, G_amax);
     return report(hipGetLastError(), "finalize kernel launch", msg, msg_len);
 }
 
 int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len) {
     if (j.n == 0) return 0;
     hipStream_t st = static_cast<hipStream_t>(j.stream);
-    const int64_t tiles = tiles_of(j.n);
-    DParams p{j.codes, j.scales, j.g, j.fmt, j.n, tiles, j.out};
+    const int64_t chunks = chunks_of(j.n);
+    DParams p{j.codes, j.scales, j.g, j.fmt, j.n, chunks, j.out};
     DequantKernel k;
     if (j.fmt == kFmtMx)
         k = j.ot == 1 ? pick_dequant_block<kFmtMx, 1>(32, j.rotate)
@@ -1094,7 +1234,8 @@ int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len) {
     else
         k = j.ot == 1 ? pick_dequant_block<kFmtUe4m3, 1>(j.block, j.rotate)
                       : pick_dequant_block<kFmtUe4m3, 0>(j.block, j.rotate);
-    hipLaunchKernelGGL(k, dim3(grid_for(tiles)), dim3(kThreads), 0, st, p);
+    const int G = grid_for_chunks(chunks, reinterpret_cast<const void*>(k));
+    hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
     return report(hipGetLastError(), "dequantize kernel launch", msg, msg_len);
 }
 
@@ -1108,7 +1249,7 @@ int launch_block_mse(const MseJob& j, char* msg, size_t msg_len) {
         return 0;
     }
     uint8_t* ws = static_cast<uint8_t*>(j.ws);
-    const int64_t tiles = tiles_of(j.n);
+    const int64_t chunks = chunks_of(j.n);
     MParams p{};
     p.x = j.x;
     p.codes = j.codes;
@@ -1116,7 +1257,7 @@ int launch_block_mse(const MseJob& j, char* msg, size_t msg_len) {
     p.g = j.g;
     p.fmt = j.fmt;
     p.n = j.n;
-    p.n_tiles = tiles;
+    p.n_chunks = chunks;
     p.n_blocks = j.n / j.block;
     p.block_mse = j.block_mse;
     p.mse_kind = j.mse_kind;
@@ -1132,24 +1273,25 @@ int launch_block_mse(const MseJob& j, char* msg, size_t msg_len) {
     else
         k = j.xt == 0 ? pick_mse_block<0, kFmtUe4m3>(j.block, j.rotate, sumsq)
                       : pick_mse_block<1, kFmtUe4m3>(j.block, j.rotate, sumsq);
-    const int G = grid_for(tiles);
+    const int G = grid_for_chunks(chunks, reinterpret_cast<const void*>(k));
     hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
     int rc = report(hipGetLastError(), "block-mse kernel launch", msg, msg_len);
     if (rc || !j.stats) return rc;
     hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kThreads), 0, st, p.partials, G, j.stats,
-                       (long long)p.n_blocks, (const double*)nullptr);
+                       (long long)p.n_blocks, (const double*)nullptr, 0);
     return report(hipGetLastError(), "finalize kernel launch", msg, msg_len);
 }
 
 int launch_rotate(const RotateJob& j, char* msg, size_t msg_len) {
     if (j.n == 0) return 0;
     hipStream_t st = static_cast<hipStream_t>(j.stream);
-    const int64_t tiles = tiles_of(j.n);
-    RParams p{j.x, j.n, tiles, j.out};
+    const int64_t chunks = chunks_of(j.n);
+    RParams p{j.x, j.n, chunks, j.out};
     void (*k)(RParams);
     if (j.xt == 0) k = j.rotate == 16 ? k_rotate<0, 16> : k_rotate<0, 32>;
     else k = j.rotate == 16 ? k_rotate<1, 16> : k_rotate<1, 32>;
-    hipLaunchKernelGGL(k, dim3(grid_for(tiles)), dim3(kThreads), 0, st, p);
+    const int G = grid_for_chunks(chunks, reinterpret_cast<const void*>(k));
+    hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
     return report(hipGetLastError(), "rotate kernel launch", msg, msg_len);
 }
 

@@ -206,7 +206,13 @@ def test_block_mse_equals_fused(fmt, block, rotate):
         q = fq.nvfp4_quantize(x, block, fmt, fq.G_DYNAMIC, None, rotate, mse_kind=fq.MSE_REL)
     bm, st = fq.fp4_block_mse(x, q.codes, q.scales, fmt, block, q.g, rotate, mse_kind=fq.MSE_REL)
     assert torch.equal(bm, q.block_mse)
-    assert fq.stats_dict(st) == fq.stats_dict(q.stats)
+    # Both calls sum the same block terms in fixed but possibly different
+    # orders (their grids follow each kernel's occupancy).
+    a, b = fq.stats_dict(st), fq.stats_dict(q.stats)
+    for key in ("n_blocks", "n_zero_blocks"):
+        assert a[key] == b[key], key
+    for key in ("sse_nonmax", "sse_max", "sse_zero", "sum_x2"):
+        assert a[key] == pytest.approx(b[key], rel=1e-12, abs=1e-300), key
 
 
 @pytest.mark.parametrize("n", [16, 32])
