@@ -51,8 +51,17 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kLaneElems = 8;
 constexpr int kChunk = kWave * kLaneElems;  // 512 elements per wave per chunk
-constexpr int kWaves = 4;
+#ifndef FP4Q_WAVES
+#define FP4Q_WAVES 4
+#endif
+constexpr int kWaves = FP4Q_WAVES;
 constexpr int kThreads = kWave * kWaves;
+#ifndef FP4Q_PREFETCH
+#define FP4Q_PREFETCH 1
+#endif
+#ifndef FP4Q_LOAD_NT
+#define FP4Q_LOAD_NT 1
+#endif
 #ifndef FP4Q_UNROLL
 #define FP4Q_UNROLL 4
 #endif
@@ -66,10 +75,23 @@ constexpr int kUnroll = FP4Q_UNROLL;        // chunks per wave iteration
 #define FP4Q_GRID_ROUNDS 1
 #endif
 constexpr int kMinChunksPerWave = FP4Q_MIN_CHUNKS_PER_WAVE;
+// Chunks per wave of the fixed split (0 = balanced one-round split) for the
+// quantize, amax and other streaming kernels.
+#ifndef FP4Q_QCPW
+#define FP4Q_QCPW 0
+#endif
+#ifndef FP4Q_ACPW
+#define FP4Q_ACPW 0
+#endif
+#ifndef FP4Q_SCPW
+#define FP4Q_SCPW 0
+#endif
+constexpr int kQuantCpw = FP4Q_QCPW, kAmaxCpw = FP4Q_ACPW, kStreamCpw = FP4Q_SCPW;
 constexpr int kGridRounds = FP4Q_GRID_ROUNDS;
 
 constexpr int kFmtMx = 0;
 constexpr int kFmtUe4m3 = 1;
+constexpr int kFmtUe5m3 = 2;
 constexpr int kMseRel = 1;
 
 // DPP controls (GFX9 encoding).
@@ -166,7 +188,7 @@ struct Raw<1> {  // 8 fp32
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;       // raw (stride 0) buffer, 32-bit data format
 constexpr int kDropped = (int)0x80000000;    // an offset past every range: access dropped
-constexpr int kNt = 2;                       // cache policy: nontemporal (read-once data)
+constexpr int kNt = FP4Q_LOAD_NT ? 2 : 0;    // cache policy: nontemporal (read-once data)
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
@@ -177,18 +199,25 @@ __device__ __forceinline__ uint4 buf_load16(Rsrc r, int off) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Work split shared by the streaming kernels: the tensor is a run of 512-element
-// chunks, and wave `wid` of `W` owns chunks [wid * C / W, (wid + 1) * C / W), a
-// contiguous range within one chunk of every other wave's length.  Waves are
-// numbered so that each XCD owns one contiguous eighth of the tensor.
+// Work split shared by the streaming kernels.  The tensor is a run of C
+// 512-element chunks and each wave owns one contiguous range of them, either
+//   cpw > 0: chunks [wid * cpw, (wid + 1) * cpw) (clipped to C), on a grid of
+//            ceil(C / (4 cpw)) workgroups that may take several rounds, or
+//   cpw = 0: wave wid of W owns [wid * C / W, (wid + 1) * C / W), ranges within
+//            one chunk of each other's length, for a one-round grid.
+// Waves are numbered so that each XCD owns one contiguous eighth of the tensor.
 struct WaveRange {
     int64_t c0, c1;
 };
 
-__device__ __forceinline__ WaveRange wave_range(int64_t n_chunks) {
+__device__ __forceinline__ WaveRange wave_range(int64_t n_chunks, int64_t cpw) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t W = (int64_t)gridDim.x * kWaves;
     const int64_t wid = (int64_t)xcd_slice(blockIdx.x, gridDim.x) * kWaves + wave;
+    if (cpw > 0) {
+        const int64_t c0 = wid * cpw < n_chunks ? wid * cpw : n_chunks;
+        return {c0, c0 + cpw < n_chunks ? c0 + cpw : n_chunks};
+    }
     return {wid * n_chunks / W, (wid + 1) * n_chunks / W};
 }
 
@@ -307,9 +336,14 @@ __device__ __forceinline__ float div_rn(float x, float d, float r) {
 // 4096 d_c when d_c is in [2^-96, 2^100], infinity when d_c = 0 (the quotients
 // are then zeros of x's sign), and -1 (never) otherwise.  Only the saturating
 // top code can exceed 4096 d_c; every other code has m / d_c below 9.
+// The fourth entry is 1 when the block maximum is known to code to 6: c is a
+// normal scale code and D = RN32(6 g) and d_c are normal binary32 numbers.
+// Then s_hat_c is s rounded to 4 significant bits (relative error below 1/17,
+// or s_hat_c < s when saturating) and D, d_c carry relative errors of at most
+// 2^-24, so RN32(m / d_c) is about 6 s / s_hat_c > 5.6 and rounds to 6.
 constexpr int kUeCodes = 256;  // covers UE4M3 (127 codes) and UE5M3 (248)
 
-__device__ __forceinline__ void build_scale_table(float4* tab, float g, int fmt) {
+__device__ __forceinline__ void build_scale_table(float4* tab, float g, float D, int fmt) {
     const int n_codes = (fmt == kFmtUe4m3) ? 0x7F : 0xF8;
     for (int c = threadIdx.x; c < n_codes; c += kThreads) {
         const float d = ue_decode((uint32_t)c, fmt) * g;
@@ -317,7 +351,8 @@ __device__ __forceinline__ void build_scale_table(float4* tab, float g, int fmt)
         float lim = -1.0f;
         if (d == 0.0f) lim = __builtin_inff();
         else if (d >= 0x1p-96f && d <= 0x1p100f) lim = d * 4096.0f;
-        tab[c] = make_float4(d, r, lim, 0.0f);
+        const bool six = c >= 8 && d >= 0x1p-126f && D >= 0x1p-126f;
+        tab[c] = make_float4(d, r, lim, six ? 1.0f : 0.0f);
     }
     __syncthreads();
 }
@@ -327,16 +362,18 @@ struct UeScale {
     uint32_t byte;
     float d, r;
     bool fast;  // the FMA-corrected quotient is exact for every element
+    bool six;   // the block maximum codes to 6
 };
 
 // s = RN32(m / D): the corrected quotient when it is in its exact range (D in
 // [2^-96, 2^100] and m / D <= 4096, which covers every unsaturated block),
-// else a plain division.
-__device__ __forceinline__ UeScale ue_scale(float m, float D, float rD, bool d_fast,
-                                            const float4* tab, int fmt) {
+// else a plain division.  s_fast_max is 4096 when D is in that range, else -1.
+template <int FMT>
+__device__ __forceinline__ UeScale ue_scale(float m, float D, float rD, float s_fast_max,
+                                            const float4* tab) {
     UeScale st;
     float s = div_rn(m, D, rD);
-    const bool slow = !(d_fast && s <= 4096.0f);
+    const bool slow = !(s <= s_fast_max);
     if (__builtin_amdgcn_ballot_w64(slow)) {  // wave-uniform: keeps the division off the fast path
         // The empty volatile asm pins the division inside the branch; without it
         // the compiler evaluates the full IEEE division on every block and selects.
@@ -344,11 +381,12 @@ __device__ __forceinline__ UeScale ue_scale(float m, float D, float rD, bool d_f
         asm volatile("" : "+v"(mm));
         if (slow) s = mm / D;
     }
-    st.byte = ue_encode(s, fmt);
+    st.byte = ue_encode(s, FMT);
     const float4 e = tab[st.byte];
     st.d = e.x;
     st.r = e.y;
     st.fast = m <= e.z;
+    st.six = e.w != 0.0f;
     return st;
 }
 
@@ -395,8 +433,27 @@ __device__ __forceinline__ float requant_ue(float m, const UeScale& s) {
 // ------------------------------------------------------------ tensor terms
 struct Acc {
     double nonmax = 0.0, max = 0.0, zero = 0.0, sumsq = 0.0;
-    long long nzero = 0;
+    uint32_t nzero = 0;  // per lane: at most one per chunk the wave processes
 };
+
+// Adds one block's terms.  A zero-rounded block (m > 0, every x_hat = 0)
+// contributes its SSE to the zero-rounding term; any other block splits its
+// SSE into the max-element term and the rest.  Zero-rounded blocks are rare, so
+// the selects run only in waves that hold one; the plain adds give the same
+// sums for every other block.
+__device__ __forceinline__ void add_block(Acc& acc, bool zero, double sse, double mterm,
+                                          double ss) {
+    if (__builtin_amdgcn_ballot_w64(zero)) {
+        acc.zero += zero ? sse : 0.0;
+        acc.nzero += zero ? 1u : 0u;
+        acc.max += zero ? 0.0 : mterm;
+        acc.nonmax += zero ? 0.0 : sse - mterm;
+    } else {
+        acc.max += mterm;
+        acc.nonmax += sse - mterm;
+    }
+    acc.sumsq += ss;
+}
 
 // Each workgroup writes its binary64 partial terms to slot blockIdx.x of the
 // partial arrays; a separate one-workgroup kernel (k_finalize) sums them in
@@ -408,7 +465,7 @@ __device__ void write_partial(const Acc& a, double* partials) {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const double t0 = wave_sum(a.nonmax), t1 = wave_sum(a.max), t2 = wave_sum(a.zero),
                  t3 = wave_sum(a.sumsq);
-    const long long tc = wave_sum_i64(a.nzero);
+    const long long tc = wave_sum_i64((long long)a.nzero);
     if (lane == 0) {
         s_acc[wave][0] = t0; s_acc[wave][1] = t1; s_acc[wave][2] = t2; s_acc[wave][3] = t3;
         s_cnt[wave] = tc;
@@ -429,44 +486,49 @@ __device__ void write_partial(const Acc& a, double* partials) {
     }
 }
 
-// Sum of entries [0, n) of a, in index order per thread (thread i takes i,
-// i + 256, ...); each batch of 8 entries is loaded before any is added, so the
-// loads overlap.
-template <typename T>
-__device__ __forceinline__ T strided_sum(const T* a, int n) {
-    constexpr int kBatch = 8;
-    T t = 0;
-    for (int b = threadIdx.x; b < n; b += kThreads * kBatch) {
-        T v[kBatch];
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            const int i = b + q * kThreads;
-            v[q] = a[i < n ? i : 0];
-        }
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q)
-            if (b + q * kThreads < n) t += v[q];
-    }
-    return t;
-}
-
 // Fixed-order sum of G workgroup partials into the fp4q_stats struct (one
-// workgroup): per-thread strided sums, then a fixed butterfly within each wave
-// and the waves in order.  When sumsq_part is given (the amax pre-pass computed
-// sum x^2 in its G_sumsq workgroups), the sum x^2 term comes from it instead of
-// the quantize partials.
+// workgroup): thread i sums entries i, i + 256, ... of each term in index
+// order, then a fixed butterfly within each wave and the waves in order.
+// Each batch loads 8 entries of every term before adding any, so a whole batch
+// costs one memory round trip.  When sumsq_part is given (the amax pre-pass
+// computed sum x^2 in its G_sumsq workgroups), the sum x^2 term comes from it
+// instead of the quantize partials.
 __global__ __launch_bounds__(kThreads) void k_finalize(const double* partials, int G, void* stats,
                                                        long long n_blocks,
                                                        const double* sumsq_part, int G_sumsq) {
     __shared__ double s_t[kWaves][4];
     __shared__ long long s_c[kWaves];
+    constexpr int kBatch = 8;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    double t[4];
+    const double* ssq = sumsq_part ? sumsq_part : partials + 3 * (size_t)kMaxGroups;
+    const int Gs = sumsq_part ? G_sumsq : G;
+    const long long* cnt = reinterpret_cast<const long long*>(partials + 4 * (size_t)kMaxGroups);
+    const int n_max = G > Gs ? G : Gs;
+    double t[4] = {0.0, 0.0, 0.0, 0.0};
+    long long c = 0;
+    for (int b = threadIdx.x; b < n_max; b += kThreads * kBatch) {
+        double v[4][kBatch];
+        long long vc[kBatch];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) t[k] = strided_sum(partials + (size_t)k * kMaxGroups, G);
-    t[3] = sumsq_part ? strided_sum(sumsq_part, G_sumsq)
-                      : strided_sum(partials + 3 * (size_t)kMaxGroups, G);
-    long long c = strided_sum(reinterpret_cast<const long long*>(partials + 4 * (size_t)kMaxGroups), G);
+        for (int q = 0; q < kBatch; ++q) {
+            const int i = b + q * kThreads;
+            const int ig = i < G ? i : 0, is = i < Gs ? i : 0;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) v[k][q] = partials[(size_t)k * kMaxGroups + ig];
+            v[3][q] = ssq[is];
+            vc[q] = cnt[ig];
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int i = b + q * kThreads;
+            if (i < G) {
+#pragma unroll
+                for (int k = 0; k < 3; ++k) t[k] += v[k][q];
+                c += vc[q];
+            }
+            if (i < Gs) t[3] += v[3][q];
+        }
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) t[k] = wave_sum(t[k]);
     c = wave_sum_i64(c);
@@ -494,6 +556,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(const double* partials, i
 struct QParams {
     const void* x;
     int64_t n, n_chunks, n_blocks;
+    int64_t cpw;  // chunks per wave, 0 = balanced one-round split
     uint8_t* codes;
     uint8_t* scales;
     float* block_mse;
@@ -513,7 +576,7 @@ struct QParams {
 // corrected quotient m / D is usable, and the workgroup's decode-scale table.
 struct UeCtx {
     float g, D, rD;
-    bool d_fast;
+    float s_fast_max;  // 4096 when D is in [2^-96, 2^100], else -1
     const float4* tab;
 };
 
@@ -582,7 +645,7 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
             xh_m = requant_mx(m, sc);
         }
     } else {
-        const UeScale s = ue_scale(m, ue.D, ue.rD, ue.d_fast, ue.tab, p.fmt);
+        const UeScale s = ue_scale<FMT>(m, ue.D, ue.rD, ue.s_fast_max, ue.tab);
         sbyte = s.byte;
         float y[8];
         if (s.fast) {
@@ -597,7 +660,10 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
             decode_word(cw, 1.0f, xh);
 #pragma unroll
             for (int i = 0; i < 8; ++i) xh[i] = xh[i] * s.d;
-            xh_m = requant_ue(m, s);
+            xh_m = 6.0f * s.d;  // the decoded code 6, as for the elements
+            if (__builtin_amdgcn_ballot_w64(!s.six)) {
+                if (!s.six) xh_m = requant_ue(m, s);
+            }
         }
     }
     const int blk = u * kBlocks + lane / L;  // block index within the group
@@ -618,7 +684,8 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
         if constexpr (SUMSQ) ss = group_sum<L>(ss);
         if (p.block_mse) {
             float mse;
-            if (p.mse_kind == kMseRel) mse = ss > 0.0 ? (float)(sse / ss) : 0.0f;
+            // Relative MSE always comes with the sum of squares (SUMSQ).
+            if (SUMSQ && p.mse_kind == kMseRel) mse = ss > 0.0 ? (float)(sse / ss) : 0.0f;
             else mse = (float)(sse * (1.0 / B));
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mse), o.mse,
                                                   gl == 0 ? blk * 4 : kDropped, 0, 0);
@@ -626,13 +693,7 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
         // Zero-filled lanes past the end form all-zero blocks, which add 0 to
         // every term and are not zero-rounded (m = 0).
         const double em = (double)(m - xh_m);
-        const double mterm = em * em;
-        const bool zero = (m > 0.0f) && (xh_m == 0.0f);
-        acc.zero += zero ? sse : 0.0;
-        acc.nzero += zero ? 1 : 0;
-        acc.max += zero ? 0.0 : mterm;
-        acc.nonmax += zero ? 0.0 : sse - mterm;
-        acc.sumsq += ss;
+        add_block(acc, (m > 0.0f) && (xh_m == 0.0f), sse, em * em, ss);
     }
 }
 
@@ -657,12 +718,12 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
     constexpr int L = B / kLaneElems;
     const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
-    const WaveRange wr = wave_range(p.n_chunks);
+    const WaveRange wr = wave_range(p.n_chunks, p.cpw);
     // The first group's loads go out before the per-workgroup set-up below, so
     // that set-up overlaps their latency.
     Raw<XT> cur[kUnroll];
     if (wr.c0 < wr.c1) load_group<XT>(cur, p.x, p.n, wr.c0, wr.c1, lane);
-    UeCtx ue{1.0f, 6.0f, 0.0f, true, nullptr};
+    UeCtx ue{1.0f, 6.0f, 0.0f, 4096.0f, nullptr};
     if constexpr (FMT != kFmtMx) {
         __shared__ float4 s_tab[kUeCodes];
         float g = 1.0f;
@@ -672,22 +733,31 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
         } else if (p.g_in) {
             g = *p.g_in;
         }
-        build_scale_table(s_tab, g, p.fmt);
         ue.g = g;
         ue.D = 6.0f * g;
         ue.rD = 1.0f / ue.D;
-        ue.d_fast = ue.D >= 0x1p-96f && ue.D <= 0x1p100f;
+        ue.s_fast_max = (ue.D >= 0x1p-96f && ue.D <= 0x1p100f) ? 4096.0f : -1.0f;
+        build_scale_table(s_tab, g, ue.D, FMT);
         ue.tab = s_tab;
     }
     Acc acc;
     for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
         const QOut o = group_outputs<B>(p, c, wr.c1);
         const int64_t left = wr.c1 - c;  // wave-uniform
+#if FP4Q_PREFETCH
+        Raw<XT> nxt[kUnroll];
+        if (c + kUnroll < wr.c1) load_group<XT>(nxt, p.x, p.n, c + kUnroll, wr.c1, lane);
+#endif
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
             if (u < left)
                 quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ>(cur[u], u, o, p, ue, lane, gl, acc);
+#if FP4Q_PREFETCH
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+#else
         if (c + kUnroll < wr.c1) load_group<XT>(cur, p.x, p.n, c + kUnroll, wr.c1, lane);
+#endif
     }
     if (p.stats) {
         if (gl != 0) acc = Acc{};  // every lane of a block holds its terms: keep one copy
@@ -699,7 +769,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
 // ------------------------------------------------------------ amax pre-pass
 struct AParams {
     const void* x;
-    int64_t n, n_chunks;
+    int64_t n, n_chunks, cpw;
     uint32_t* part;
     double* sumsq;  // per-workgroup sum x^2 (binary64), written when non-NULL
 };
@@ -737,14 +807,23 @@ __global__ __launch_bounds__(kThreads) void k_amax(AParams p) {
     constexpr int L = ROT ? ROT / kLaneElems : 1;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int gl = lane & (L - 1);
-    const WaveRange wr = wave_range(p.n_chunks);
+    const WaveRange wr = wave_range(p.n_chunks, p.cpw);
     uint32_t mx = 0;
     double ss = 0.0;
     // Elements past the wave's range read as zeros, which leave both the
     // maximum and the sum of squares unchanged.
+#if FP4Q_PREFETCH
+    Raw<XT> cur[kUnroll];
+    if (wr.c0 < wr.c1) load_group<XT>(cur, p.x, p.n, wr.c0, wr.c1, lane);
+#endif
     for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
+#if FP4Q_PREFETCH
+        Raw<XT> nxt[kUnroll];
+        if (c + kUnroll < wr.c1) load_group<XT>(nxt, p.x, p.n, c + kUnroll, wr.c1, lane);
+#else
         Raw<XT> cur[kUnroll];
         load_group<XT>(cur, p.x, p.n, c, wr.c1, lane);
+#endif
         const int64_t left = wr.c1 - c;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -754,6 +833,10 @@ __global__ __launch_bounds__(kThreads) void k_amax(AParams p) {
                 if constexpr (SUMSQ) ss += cs;
             }
         }
+#if FP4Q_PREFETCH
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+#endif
     }
     mx = wave_max(mx);
     if constexpr (SUMSQ) ss = wave_sum(ss);
@@ -780,7 +863,7 @@ struct DParams {
     const uint8_t* scales;
     const float* g;
     int fmt;
-    int64_t n, n_chunks;
+    int64_t n, n_chunks, cpw;
     void* out;
 };
 
@@ -823,7 +906,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant(DParams p) {
     const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
     const float g = (FMT != kFmtMx && p.g) ? *p.g : 1.0f;
-    const WaveRange wr = wave_range(p.n_chunks);
+    const WaveRange wr = wave_range(p.n_chunks, p.cpw);
     for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
         uint32_t cw[kUnroll], sb[kUnroll];
         load_codes<B>(p.codes, p.scales, p.n, c, wr.c1, lane, cw, sb);
@@ -868,7 +951,7 @@ struct MParams {
     const uint8_t* scales;
     const float* g;
     int fmt;
-    int64_t n, n_chunks, n_blocks;
+    int64_t n, n_chunks, n_blocks, cpw;
     float* block_mse;
     int mse_kind;
     double* partials;
@@ -885,7 +968,7 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MParams p) {
     const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
     const float g = (FMT != kFmtMx && p.g) ? *p.g : 1.0f;
-    const WaveRange wr = wave_range(p.n_chunks);
+    const WaveRange wr = wave_range(p.n_chunks, p.cpw);
     Acc acc;
     for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
         Raw<XT> raw[kUnroll];
@@ -950,13 +1033,7 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MParams p) {
                                                       gl == 0 ? (u * kBlocks + lane / L) * 4 : kDropped,
                                                       0, 0);
             }
-            const double mterm = (double)e_key * (double)e_key;
-            const bool zero = (m > 0.0f) && !any_nz;
-            acc.zero += zero ? sse : 0.0;
-            acc.nzero += zero ? 1 : 0;
-            acc.max += zero ? 0.0 : mterm;
-            acc.nonmax += zero ? 0.0 : sse - mterm;
-            acc.sumsq += ss;
+            add_block(acc, (m > 0.0f) && !any_nz, sse, (double)e_key * (double)e_key, ss);
         }
     }
     if (p.stats) {
@@ -968,7 +1045,7 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MParams p) {
 // ------------------------------------------------------------ rotation only
 struct RParams {
     const void* x;
-    int64_t n, n_chunks;
+    int64_t n, n_chunks, cpw;
     float* out;
 };
 
@@ -977,7 +1054,7 @@ __global__ __launch_bounds__(kThreads) void k_rotate(RParams p) {
     constexpr int L = ROT / kLaneElems;
     const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
-    const WaveRange wr = wave_range(p.n_chunks);
+    const WaveRange wr = wave_range(p.n_chunks, p.cpw);
     for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
         Raw<XT> raw[kUnroll];
         load_group<XT>(raw, p.x, p.n, c, wr.c1, lane);
@@ -1059,6 +1136,21 @@ int grid_for_chunks(int64_t chunks, const void* kernel) {
     if (want > kMaxGroups) want = kMaxGroups;
     if (want < 1) want = 1;
     return (int)want;
+}
+
+struct Split {
+    int G;
+    int64_t cpw;
+};
+
+// Fixed ranges of `cpw` chunks per wave when that grid fits the workspace's
+// partial slots, else the balanced one-round split.
+Split split_for(int64_t chunks, const void* kernel, int cpw) {
+    if (cpw > 0) {
+        const int64_t G = (chunks + (int64_t)kWaves * cpw - 1) / ((int64_t)kWaves * cpw);
+        if (G <= kMaxGroups) return {(int)G, cpw};
+    }
+    return {grid_for_chunks(chunks, kernel), 0};
 }
 
 int report(hipError_t e, const char* what, char* msg, size_t len) {
@@ -1192,18 +1284,24 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
         k = j.xt == 0 ? pick_quant_block<0, kFmtMx>(32, j.rotate, err, sumsq)
                       : pick_quant_block<1, kFmtMx>(32, j.rotate, err, sumsq);
     else
-        k = j.xt == 0 ? pick_quant_block<0, kFmtUe4m3>(j.block, j.rotate, err, sumsq)
-                      : pick_quant_block<1, kFmtUe4m3>(j.block, j.rotate, err, sumsq);
-    const int G = grid_for_chunks(chunks, reinterpret_cast<const void*>(k));
+        k = j.fmt == kFmtUe4m3
+                ? (j.xt == 0 ? pick_quant_block<0, kFmtUe4m3>(j.block, j.rotate, err, sumsq)
+                             : pick_quant_block<1, kFmtUe4m3>(j.block, j.rotate, err, sumsq))
+                : (j.xt == 0 ? pick_quant_block<0, kFmtUe5m3>(j.block, j.rotate, err, sumsq)
+                             : pick_quant_block<1, kFmtUe5m3>(j.block, j.rotate, err, sumsq));
+    const Split sq = split_for(chunks, reinterpret_cast<const void*>(k), kQuantCpw);
+    const int G = sq.G;
+    p.cpw = sq.cpw;
     const double* amax_sumsq = nullptr;
     int G_amax = 0;
     if (j.fmt != kFmtMx && j.gmode != 0) {
         if (dynamic) {
-            AParams a{j.x, j.n, chunks, reinterpret_cast<uint32_t*>(ws + kWsAmax),
+            const AmaxKernel ka = pick_amax(j.xt, j.rotate, sumsq_in_amax);
+            const Split sa = split_for(chunks, reinterpret_cast<const void*>(ka), kAmaxCpw);
+            AParams a{j.x, j.n, chunks, sa.cpw, reinterpret_cast<uint32_t*>(ws + kWsAmax),
                       sumsq_in_amax ? reinterpret_cast<double*>(ws + kWsAmaxSumsq) : nullptr};
             amax_sumsq = a.sumsq;
-            const AmaxKernel ka = pick_amax(j.xt, j.rotate, sumsq_in_amax);
-            G_amax = grid_for_chunks(chunks, reinterpret_cast<const void*>(ka));
+            G_amax = sa.G;
             hipLaunchKernelGGL(ka, dim3(G_amax), dim3(kThreads), 0, st, a);
             int rc = report(hipGetLastError(), "amax kernel launch", msg, msg_len);
             if (rc) return rc;
@@ -1226,7 +1324,7 @@ int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len) {
     if (j.n == 0) return 0;
     hipStream_t st = static_cast<hipStream_t>(j.stream);
     const int64_t chunks = chunks_of(j.n);
-    DParams p{j.codes, j.scales, j.g, j.fmt, j.n, chunks, j.out};
+    DParams p{j.codes, j.scales, j.g, j.fmt, j.n, chunks, 0, j.out};
     DequantKernel k;
     if (j.fmt == kFmtMx)
         k = j.ot == 1 ? pick_dequant_block<kFmtMx, 1>(32, j.rotate)
@@ -1234,8 +1332,9 @@ int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len) {
     else
         k = j.ot == 1 ? pick_dequant_block<kFmtUe4m3, 1>(j.block, j.rotate)
                       : pick_dequant_block<kFmtUe4m3, 0>(j.block, j.rotate);
-    const int G = grid_for_chunks(chunks, reinterpret_cast<const void*>(k));
-    hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
+    const Split sp = split_for(chunks, reinterpret_cast<const void*>(k), kStreamCpw);
+    p.cpw = sp.cpw;
+    hipLaunchKernelGGL(k, dim3(sp.G), dim3(kThreads), 0, st, p);
     return report(hipGetLastError(), "dequantize kernel launch", msg, msg_len);
 }
 
@@ -1273,7 +1372,9 @@ int launch_block_mse(const MseJob& j, char* msg, size_t msg_len) {
     else
         k = j.xt == 0 ? pick_mse_block<0, kFmtUe4m3>(j.block, j.rotate, sumsq)
                       : pick_mse_block<1, kFmtUe4m3>(j.block, j.rotate, sumsq);
-    const int G = grid_for_chunks(chunks, reinterpret_cast<const void*>(k));
+    const Split sp = split_for(chunks, reinterpret_cast<const void*>(k), kStreamCpw);
+    const int G = sp.G;
+    p.cpw = sp.cpw;
     hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
     int rc = report(hipGetLastError(), "block-mse kernel launch", msg, msg_len);
     if (rc || !j.stats) return rc;
@@ -1286,12 +1387,13 @@ int launch_rotate(const RotateJob& j, char* msg, size_t msg_len) {
     if (j.n == 0) return 0;
     hipStream_t st = static_cast<hipStream_t>(j.stream);
     const int64_t chunks = chunks_of(j.n);
-    RParams p{j.x, j.n, chunks, j.out};
+    RParams p{j.x, j.n, chunks, 0, j.out};
     void (*k)(RParams);
     if (j.xt == 0) k = j.rotate == 16 ? k_rotate<0, 16> : k_rotate<0, 32>;
     else k = j.rotate == 16 ? k_rotate<1, 16> : k_rotate<1, 32>;
-    const int G = grid_for_chunks(chunks, reinterpret_cast<const void*>(k));
-    hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
+    const Split sp = split_for(chunks, reinterpret_cast<const void*>(k), kStreamCpw);
+    p.cpw = sp.cpw;
+    hipLaunchKernelGGL(k, dim3(sp.G), dim3(kThreads), 0, st, p);
     return report(hipGetLastError(), "rotate kernel launch", msg, msg_len);
 }
 
