@@ -7,15 +7,28 @@ Default workload (one step = the whole path over one batch):
   per-tensor scale, E2M1 codes packed two per byte, dequantization, per-block
   MSE and the three-term error split.  Inputs are resident in HBM before timing.
 
-Prints one JSON line.  `value` is GB/s of bf16 input quantized+packed+MSE'd
-over the whole step (all kernels of all six tensors).  `roofline` is the
-quantize kernel alone (the step's own k_quantize instantiation, launched once
-per tensor with the step's per-tensor scale given), timed with HIP events on
-the stream it runs on; algorithmic bytes per element = 2 (read) + 0.5 (codes)
-+ 1/16 (scales) + 4/16 (per-block MSE).  `cpu_baseline` times the oracle
-(single thread) on two of the six tensors.
+Prints one JSON line.  `value` is GB/s of input quantized+packed+MSE'd over
+the whole step (all kernels of all tensors).  For the default workload
+`roofline` is the quantize kernel alone (the step's own k_quantize
+instantiation, launched once per tensor with the step's per-tensor scale
+given), timed with HIP events on the stream it runs on; algorithmic bytes per
+element = 2 (read) + 0.5 (codes) + 1/16 (scales) + 4/16 (per-block MSE).  For
+the other workloads it is the whole step's algorithmic bytes (every kernel,
+the amax pre-pass read included) over the step time.  `cpu_baseline` times the
+oracle (single thread) on a bounded sample of the same workload.
 
-Other workloads for reference numbers: --workload qwen05 | llama8 | qwen14rot | qwen14model.
+Workloads (--workload):
+  qwen7        the default above
+  qwen05       fp32 4864 x 896 (Qwen2.5-0.5B up-projection), MXFP4 with per-block
+               MSE: launch-bound, reported in GB/s only
+  llama8       four bf16 14336 x 4096 tensors (Llama-3.1-8B MLP), narrow Normal
+               sigma in {0.002, 0.005, 0.01, 0.05}, UE4M3 without a per-tensor
+               scale at block sizes 256, 128, 64, 32, 16 and 8, MSE and split
+  qwen14rot    bf16 13824 x 5120 Student-t(4) with 1 % outlier columns x20:
+               MXFP4 and dynamic NVFP4, each without and with block rotation
+  qwen14model  a random-init Qwen2.5-14B-shaped stack (48 layers x 7 projections,
+               13.2e9 bf16 parameters, 26.4 GB) quantized whole to MXFP4 and to
+               dynamic NVFP4, relative per-block MSE and per-tensor split
 """
 import argparse
 import hashlib
@@ -23,8 +36,7 @@ import json
 import os
 import sys
 import time
-
-import numpy as np
+from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -51,38 +63,204 @@ def read_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def gen_qwen7():
+# ------------------------------------------------------------------ workloads
+class Spec:
+    """One quantization call applied to every tensor of a workload."""
+
+    def __init__(self, tag, fmt, block, scale_fmt=1, gmode=0, rotate=0, mse_kind=0,
+                 block_mse=True, stats=True):
+        self.tag, self.fmt, self.block, self.scale_fmt = tag, fmt, block, scale_fmt
+        self.gmode, self.rotate, self.mse_kind = gmode, rotate, mse_kind
+        self.block_mse, self.stats = block_mse, stats
+
+    def algorithmic_bytes(self, n, in_bytes):
+        """Bytes every kernel of the call must move: the amax pre-pass read (dynamic
+        NVFP4), the quantize read, codes, scale bytes and per-block MSE."""
+        b = n * (in_bytes + 0.5 + 1.0 / self.block + (4.0 / self.block if self.block_mse else 0))
+        if self.fmt == "nv" and self.gmode == 1:
+            b += n * in_bytes
+        return b
+
+    def describe(self):
+        if self.fmt == "mx":
+            s = "MXFP4 b32"
+        else:
+            s = f"{'UE4M3' if self.scale_fmt == 1 else 'UE5M3'} b{self.block}"
+            s += {0: "", 1: " dynamic g", 2: " given g"}[self.gmode]
+        if self.rotate:
+            s += f" rot{self.rotate}"
+        return s
+
+
+class Workload:
+    """`sample` = (description, tensors, repeats, spec index) of the oracle's
+    bounded CPU sample."""
+
+    def __init__(self, name, config, make_tensors, specs, steps, warmup, sample):
+        self.name, self.config, self.make_tensors = name, config, make_tensors
+        self.specs, self.steps, self.warmup, self.sample = specs, steps, warmup, sample
+
+
+def _qwen7_tensors():
     import fp4_workloads as wl
-    xs = []
-    for si in range(2):
-        for gi in range(3):
-            xs.append(wl.qwen7_mlp(si, gi))
-    return xs
+    return [wl.qwen7_mlp(si, gi) for si in range(2) for gi in range(3)]
 
 
-def cpu_baseline(xs_host):
-    """The oracle as it stands (one thread) on two whole tensors of the workload."""
+def _qwen05_tensors():
+    import torch
+    import fp4_workloads as wl
+    return [torch.from_numpy(wl.qwen05_up())]
+
+
+def _llama8_tensors():
+    import fp4_workloads as wl
+    return [wl.llama8_sweep(i) for i in range(len(wl.LLAMA8_SIGMAS))]
+
+
+def _qwen14rot_tensors():
+    import fp4_workloads as wl
+    return [wl.qwen14_outliers()]
+
+
+def _qwen14model_tensors():
+    """Generated on host threads (one PCG64 stream per tensor, as the recipe says)
+    and moved to the device one by one; yields host tensors lazily."""
+    import fp4_workloads as wl
+    keys = [(layer, p) for layer in range(wl.QWEN14_LAYERS) for p in range(len(wl.QWEN14_PROJ))]
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(workers) as ex:
+        for t in ex.map(lambda k: wl.qwen14_layer_tensor(*k), keys):
+            yield t
+
+
+WORKLOADS = {
+    "qwen7": Workload(
+        "qwen2.5-7b-mlp-nvfp4",
+        {"tensors": "6 bf16: 18944x3584 and 3584x18944, sigma 0.01/0.02/0.04",
+         "format": "NVFP4: block 16, UE4M3 scales, dynamic FP32 per-tensor scale",
+         "outputs": "codes + scales + per-block MSE + three-term error split"},
+        _qwen7_tensors, [Spec("nv16_dyn", "nv", 16, 1, 1)], 50, 5,
+        ("2 of the 6 tensors (18944x3584, sigma 0.01 and 0.02), whole", 2, 1, 0)),
+    "qwen05": Workload(
+        "qwen2.5-0.5b-up-mxfp4-fp32",
+        {"tensors": "1 fp32 4864x896, N(0, 0.02), seed 0",
+         "format": "MXFP4: block 32, E8M0 scales", "outputs": "codes + scales + per-block MSE"},
+        _qwen05_tensors, [Spec("mx32", "mx", 32, stats=False)], 400, 20,
+        ("the tensor, whole, 40 times", 1, 40, 0)),
+    "llama8": Workload(
+        "llama3.1-8b-mlp-ue4m3-block-sweep",
+        {"tensors": "4 bf16 14336x4096, sigma 0.002/0.005/0.01/0.05",
+         "format": "UE4M3 scales, no per-tensor scale, blocks 256/128/64/32/16/8",
+         "outputs": "codes + scales + per-block MSE + three-term error split"},
+        _llama8_tensors, [Spec(f"ue4m3_b{b}", "nv", b, 1, 0) for b in (256, 128, 64, 32, 16, 8)],
+        20, 2, ("2 of the 4 tensors (sigma 0.002 and 0.005), whole", 2, 1, 4)),
+    "qwen14rot": Workload(
+        "qwen2.5-14b-mlp-outliers-rotation",
+        {"tensors": "1 bf16 13824x5120, Student-t(4) sd 0.02, 51 outlier columns x20",
+         "format": "MXFP4 b32 and NVFP4 b16 dynamic g, each without and with block Hadamard",
+         "outputs": "codes + scales + per-block MSE + three-term error split"},
+        _qwen14rot_tensors,
+        [Spec("mx32", "mx", 32), Spec("mx32_rot", "mx", 32, rotate=32),
+         Spec("nv16_dyn", "nv", 16, 1, 1), Spec("nv16_dyn_rot", "nv", 16, 1, 1, rotate=16)],
+        50, 5, ("the tensor, whole, 3 times", 1, 3, 2)),
+    "qwen14model": Workload(
+        "qwen2.5-14b-shaped-model-sweep",
+        {"tensors": "336 bf16 (48 layers x q,k,v,o,gate,up,down), N(0, 0.02), 13.2e9 params",
+         "format": "MXFP4 b32 and NVFP4 b16 dynamic g",
+         "outputs": "codes + scales + relative per-block MSE + per-tensor split"},
+        _qwen14model_tensors,
+        [Spec("mx32", "mx", 32, mse_kind=1), Spec("nv16_dyn", "nv", 16, 1, 1, mse_kind=1)],
+        5, 1, ("layer 0's q, k, v, o, gate and up projections, whole", 6, 1, 1)),
+}
+
+
+# ------------------------------------------------------------------ running
+class Runner:
+    """Device buffers and calls for every (tensor, spec) pair of a workload."""
+
+    def __init__(self, fq, torch, dev, xs, specs):
+        self.fq, self.torch, self.dev, self.xs, self.specs = fq, torch, dev, xs, specs
+        self.ws = fq.workspace(dev)
+        self.out = {}
+        # Outputs are shared by tensors of one shape (each call overwrites them);
+        # g and stats are per call so the given-g replay can reuse the step's g.
+        shared = {}
+        for ti, x in enumerate(xs):
+            r, c = x.shape
+            for si, s in enumerate(specs):
+                key = (r, c, s.block)
+                if key not in shared:
+                    shared[key] = dict(
+                        codes=torch.empty((r, c // 2), dtype=torch.uint8, device=dev),
+                        scales=torch.empty((r, c // s.block), dtype=torch.uint8, device=dev),
+                        block_mse=torch.empty((r, c // s.block), dtype=torch.float32, device=dev))
+                o = dict(shared[key])
+                o["stats"] = fq.new_stats(dev)
+                o["g"] = torch.ones(1, dtype=torch.float32, device=dev)
+                self.out[(ti, si)] = o
+
+    def call(self, ti, si, given=False):
+        fq, x, s, o = self.fq, self.xs[ti], self.specs[si], self.out[(ti, si)]
+        bm = o["block_mse"] if s.block_mse else False
+        if s.fmt == "mx":
+            st = o["stats"] if (s.stats and not given) else False
+            fq.mxfp4_quantize(x, s.rotate, codes=o["codes"], scales=o["scales"], block_mse=bm,
+                              mse_kind=s.mse_kind, stats=st, ws=self.ws)
+        else:
+            gmode = fq.G_GIVEN if (given and s.gmode == 1) else s.gmode
+            st = o["stats"] if (s.stats and not given) else False
+            fq.nvfp4_quantize(x, s.block, s.scale_fmt, gmode, o["g"], s.rotate, codes=o["codes"],
+                              scales=o["scales"], block_mse=bm, mse_kind=s.mse_kind, stats=st,
+                              ws=self.ws)
+
+    def step(self, given=False):
+        for ti in range(len(self.xs)):
+            for si in range(len(self.specs)):
+                self.call(ti, si, given)
+
+
+def time_region(torch, stream, fn, reps):
+    """ms per rep of fn, bracketed by HIP events on `stream`."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline(w, xs_host_sample):
+    """The oracle as it stands (one thread) on a bounded sample of the workload."""
+    import numpy as np
     import oracle
-    n, el = 0, 0.0
-    for x in xs_host[:2]:
-        xf = x.float().numpy()
-        t = time.perf_counter()
-        oracle.quantize(xf, oracle.FMT_UE4M3, 16, oracle.GMODE_DYNAMIC)
-        el += time.perf_counter() - t
-        n += xf.size
-    return {"value": round(n * 2 / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "2 of the 6 tensors (18944x3584, sigma 0.01 and 0.02), whole, NVFP4 with "
-                      "dynamic per-tensor scale, single-threaded C oracle",
+    desc, n_tensors, repeat, spec_idx = w.sample
+    s = w.specs[spec_idx]
+    fmt = oracle.FMT_MXFP4 if s.fmt == "mx" else s.scale_fmt
+    gmode = {0: oracle.GMODE_NONE, 1: oracle.GMODE_DYNAMIC, 2: oracle.GMODE_GIVEN}[s.gmode]
+    n, el, in_bytes = 0, 0.0, 2
+    for x in xs_host_sample[:n_tensors]:
+        xf = x.float().numpy() if hasattr(x, "float") else np.asarray(x, np.float32)
+        in_bytes = 4 if (hasattr(x, "dtype") and str(x.dtype) == "torch.float32") else 2
+        for _ in range(repeat):
+            t = time.perf_counter()
+            oracle.quantize(xf, fmt, s.block, gmode, None, s.rotate, s.mse_kind)
+            el += time.perf_counter() - t
+            n += xf.size
+    return {"value": round(n * in_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{desc}, {s.describe()}, single-threaded C oracle",
             "seconds": round(el, 2)}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="qwen7")
+    ap.add_argument("--workload", default="qwen7", choices=sorted(WORKLOADS))
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain device copy of the first tensor (a kernel of "
                          "known traffic, for scaling rocprofv3 byte counters)")
@@ -92,107 +270,98 @@ def main():
               "(the path shards by rows with one max- and one sum-all-reduce; see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
-    if args.workload != "qwen7":
-        import bench_workloads
-        bench_workloads.run(args)
-        return
+    w = WORKLOADS[args.workload]
+    steps = args.steps if args.steps is not None else w.steps
+    warmup = args.warmup if args.warmup is not None else w.warmup
 
     import torch
     import microscaling_fp4_quantization_amd as fq
 
     dev = torch.device("cuda:0")
-    xs_host = gen_qwen7()
-    xs = [x.to(dev) for x in xs_host]
-    outs = []
-    for x in xs:
-        r, c = x.shape
-        outs.append(dict(codes=torch.empty((r, c // 2), dtype=torch.uint8, device=dev),
-                         scales=torch.empty((r, c // 16), dtype=torch.uint8, device=dev),
-                         block_mse=torch.empty((r, c // 16), dtype=torch.float32, device=dev),
-                         stats=fq.new_stats(dev),
-                         g=torch.empty(1, dtype=torch.float32, device=dev)))
-    ws = fq.workspace(dev)
-    n_elem = sum(x.numel() for x in xs)
+    xs, sample_host = [], []
+    n_sample = w.sample[1]
+    for x in w.make_tensors():
+        if len(sample_host) < n_sample:
+            sample_host.append(x)
+        xs.append(x.to(dev))
+        del x
+    in_bytes = xs[0].element_size()
+    run = Runner(fq, torch, dev, xs, w.specs)
+    n_elem_calls = sum(x.numel() for x in xs) * len(w.specs)
+    alg_bytes = sum(s.algorithmic_bytes(x.numel(), in_bytes) for x in xs for s in w.specs)
 
-    def step():
-        for x, o in zip(xs, outs):
-            fq.nvfp4_quantize(x, 16, fq.FMT_UE4M3, fq.G_DYNAMIC, o["g"], 0, codes=o["codes"],
-                              scales=o["scales"], block_mse=o["block_mse"], stats=o["stats"],
-                              ws=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    for _ in range(warmup):
+        run.step()
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    ms_step = time_region(torch, stream, run.step, steps)
     t_wall = time.perf_counter() - t_wall
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
-    value = n_elem * 2 / (ms_step * 1e-3) / 1e9
+    value = n_elem_calls * in_bytes / (ms_step * 1e-3) / 1e9
 
-    # Dominant kernel alone.  With the per-tensor scale given (the g each step
-    # computed), per-block MSE and no stats, a call launches exactly one kernel:
-    # the same k_quantize instantiation the step runs (in the dynamic mode the
-    # amax pass supplies sum x^2, so the step's quantize kernel omits it too).
-    reps = max(10, args.steps)
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.workload == "qwen7":
+        # Dominant kernel alone.  With the per-tensor scale given (the g each step
+        # computed), per-block MSE and no stats, a call launches exactly one
+        # kernel: the same k_quantize instantiation the step runs (in the dynamic
+        # mode the amax pass supplies sum x^2, so the step's quantize kernel omits
+        # it too).
+        reps = max(10, steps)
+        run.step(given=True)
+        us_launch = time_region(torch, stream, lambda: run.step(given=True), reps) * 1e3 / len(xs)
+        bytes_launch = xs[0].numel() * (2 + 0.5 + 1 / 16 + 4 / 16)
+        achieved = bytes_launch / (us_launch * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": read_traffic(),
+                    "kernel": "k_quantize<bf16, UE, 16, no rotation, err, no sumsq>",
+                    "us_per_launch": round(us_launch, 3),
+                    "algorithmic_bytes_per_launch": int(bytes_launch)}
+    else:
+        achieved = alg_bytes / (ms_step * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "whole step (every kernel of every call)",
+                    "algorithmic_bytes_per_step": int(alg_bytes)}
 
-    def quantize_only():
-        for x, o in zip(xs, outs):
-            fq.nvfp4_quantize(x, 16, fq.FMT_UE4M3, fq.G_GIVEN, o["g"], 0, codes=o["codes"],
-                              scales=o["scales"], block_mse=o["block_mse"], stats=False)
-
-    quantize_only()
-    torch.cuda.synchronize()
-    k0.record(stream)
-    for _ in range(reps):
-        quantize_only()
-    k1.record(stream)
-    torch.cuda.synchronize()
-    us_launch = k0.elapsed_time(k1) * 1e3 / (reps * len(xs))
-    bytes_launch = xs[0].numel() * (2 + 0.5 + 1 / 16 + 4 / 16)
-    achieved = bytes_launch / (us_launch * 1e-6) / 1e9
+    # Per-spec breakdown: one timed pass of each call type over all tensors.
+    breakdown = {}
+    if len(w.specs) > 1:
+        for si, s in enumerate(w.specs):
+            fn = lambda si=si: [run.call(ti, si) for ti in range(len(xs))]
+            ms = time_region(torch, stream, fn, max(1, min(steps, 10)))
+            nb = sum(s.algorithmic_bytes(x.numel(), in_bytes) for x in xs)
+            breakdown[s.tag] = {"us_per_call": round(ms * 1e3 / len(xs), 2),
+                                "input_GBps": round(sum(x.numel() for x in xs) * in_bytes
+                                                    / (ms * 1e-3) / 1e9, 1),
+                                "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
 
     if args.calibration_copy:
         dst = torch.empty_like(xs[0])
         dst.copy_(xs[0])
         torch.cuda.synchronize()
 
+    config = {"workload": w.name, **w.config, "elements_per_step": n_elem_calls}
     line = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded numpy PCG64 normal, rounded to bf16)",
-        "config": {"workload": "qwen2.5-7b-mlp-nvfp4",
-                   "tensors": "6 bf16: 18944x3584 and 3584x18944, sigma 0.01/0.02/0.04",
-                   "format": "NVFP4: block 16, UE4M3 scales, dynamic FP32 per-tensor scale",
-                   "outputs": "codes + scales + per-block MSE + three-term error split",
-                   "elements_per_step": n_elem},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": read_traffic(),
-                     "kernel": "k_quantize<bf16, UE, 16, no rotation, err, no sumsq>",
-                     "us_per_launch": round(us_launch, 3),
-                     "algorithmic_bytes_per_launch": int(bytes_launch)},
-        "step_breakdown": {"algorithmic_GBps_both_passes":
-                           round(n_elem * (2 + 2.8125) / (ms_step * 1e-3) / 1e9, 1)},
+        "data": "synthetic (seeded numpy PCG64, " +
+                ("fp32" if in_bytes == 4 else "rounded to bf16") + ")",
+        "config": config,
+        "roofline": roofline,
+        "step_breakdown": {"algorithmic_GBps_all_kernels":
+                           round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
+                           "wall_s_timed_region": round(t_wall, 3), **breakdown},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(xs_host)
+        line["cpu_baseline"] = cpu_baseline(w, sample_host)
     print(json.dumps(line), flush=True)
 
 
