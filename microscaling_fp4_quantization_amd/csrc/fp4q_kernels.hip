@@ -56,6 +56,9 @@ constexpr int kChunk = kWave * kLaneElems;  // 512 elements per wave per chunk
 #endif
 constexpr int kWaves = FP4Q_WAVES;
 constexpr int kThreads = kWave * kWaves;
+#ifndef FP4Q_STORE_NT
+#define FP4Q_STORE_NT 0
+#endif
 #ifndef FP4Q_PREFETCH
 #define FP4Q_PREFETCH 1
 #endif
@@ -66,6 +69,14 @@ constexpr int kThreads = kWave * kWaves;
 #define FP4Q_UNROLL 4
 #endif
 constexpr int kUnroll = FP4Q_UNROLL;        // chunks per wave iteration
+#ifndef FP4Q_QUNROLL
+#define FP4Q_QUNROLL 2
+#endif
+#ifndef FP4Q_AUNROLL
+#define FP4Q_AUNROLL 4
+#endif
+constexpr int kQuantUnroll = FP4Q_QUNROLL;  // ... of the quantize kernel
+constexpr int kAmaxUnroll = FP4Q_AUNROLL;   // ... of the amax pre-pass
 // Quantize and amax grids: at least this many chunks per wave, and at most
 // kGridRounds rounds of resident workgroups.
 #ifndef FP4Q_MIN_CHUNKS_PER_WAVE
@@ -78,15 +89,24 @@ constexpr int kMinChunksPerWave = FP4Q_MIN_CHUNKS_PER_WAVE;
 // Chunks per wave of the fixed split (0 = balanced one-round split) for the
 // quantize, amax and other streaming kernels.
 #ifndef FP4Q_QCPW
-#define FP4Q_QCPW 0
+#define FP4Q_QCPW -1
 #endif
 #ifndef FP4Q_ACPW
-#define FP4Q_ACPW 0
+#define FP4Q_ACPW 8
 #endif
 #ifndef FP4Q_SCPW
 #define FP4Q_SCPW 0
 #endif
 constexpr int kQuantCpw = FP4Q_QCPW, kAmaxCpw = FP4Q_ACPW, kStreamCpw = FP4Q_SCPW;
+// The amax pre-pass has no per-workgroup set-up, so it runs larger workgroups
+// of short-lived waves: fewer per-workgroup maxima for the quantize kernel to
+// reduce at the same wave count.
+#ifndef FP4Q_AMAX_WAVES
+#define FP4Q_AMAX_WAVES 16
+#endif
+constexpr int kAmaxWaves = FP4Q_AMAX_WAVES;
+
+constexpr int kAmaxThreads = kWave * kAmaxWaves;
 constexpr int kGridRounds = FP4Q_GRID_ROUNDS;
 
 constexpr int kFmtMx = 0;
@@ -189,6 +209,7 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;       // raw (stride 0) buffer, 32-bit data format
 constexpr int kDropped = (int)0x80000000;    // an offset past every range: access dropped
 constexpr int kNt = FP4Q_LOAD_NT ? 2 : 0;    // cache policy: nontemporal (read-once data)
+constexpr int kStNt = FP4Q_STORE_NT ? 2 : 0;
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
@@ -200,39 +221,56 @@ __device__ __forceinline__ uint4 buf_load16(Rsrc r, int off) {
 }
 
 // Work split shared by the streaming kernels.  The tensor is a run of C
-// 512-element chunks and each wave owns one contiguous range of them, either
-//   cpw > 0: chunks [wid * cpw, (wid + 1) * cpw) (clipped to C), on a grid of
-//            ceil(C / (4 cpw)) workgroups that may take several rounds, or
+// 512-element chunks; a wave takes n groups of up to kUnroll chunks, starting
+// at chunks c0, c0 + step, ... (step may be negative), each clipped at c1:
+//   cpw > 0: its own range [wid * cpw, (wid + 1) * cpw) (clipped to C), on a
+//            grid of ceil(C / (4 cpw)) workgroups that may take several rounds;
 //   cpw = 0: wave wid of W owns [wid * C / W, (wid + 1) * C / W), ranges within
-//            one chunk of each other's length, for a one-round grid.
-// Waves are numbered so that each XCD owns one contiguous eighth of the tensor.
+//            one chunk of each other's length, for a one-round grid;
+//   cpw < 0: groups wid, wid + W, wid + 2W, ... of the whole tensor on a
+//            one-round grid, so that all waves sweep the tensor together and
+//            the accesses in flight stay within a compact region; cpw = -2
+//            sweeps from the end of the tensor to its start.
+// Waves are numbered so that each XCD owns one contiguous eighth of the
+// tensor (cpw >= 0) or of every sweep (cpw < 0).
 struct WaveRange {
-    int64_t c0, c1;
+    int64_t c0, step, n, c1;
 };
 
+template <int WAVES = kWaves, int U = kUnroll>
 __device__ __forceinline__ WaveRange wave_range(int64_t n_chunks, int64_t cpw) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t W = (int64_t)gridDim.x * kWaves;
-    const int64_t wid = (int64_t)xcd_slice(blockIdx.x, gridDim.x) * kWaves + wave;
-    if (cpw > 0) {
-        const int64_t c0 = wid * cpw < n_chunks ? wid * cpw : n_chunks;
-        return {c0, c0 + cpw < n_chunks ? c0 + cpw : n_chunks};
+    const int64_t W = (int64_t)gridDim.x * WAVES;
+    const int64_t wid = (int64_t)xcd_slice(blockIdx.x, gridDim.x) * WAVES + wave;
+    if (cpw < 0) {
+        const int64_t groups = (n_chunks + U - 1) / U;
+        const int64_t n = wid < groups ? (groups - wid + W - 1) / W : 0;
+        if (cpw == -2) return {(groups - 1 - wid) * U, -W * U, n, n_chunks};
+        return {wid * U, W * U, n, n_chunks};
     }
-    return {wid * n_chunks / W, (wid + 1) * n_chunks / W};
+    int64_t c0, c1;
+    if (cpw > 0) {
+        c0 = wid * cpw < n_chunks ? wid * cpw : n_chunks;
+        c1 = c0 + cpw < n_chunks ? c0 + cpw : n_chunks;
+    } else {
+        c0 = wid * n_chunks / W;
+        c1 = (wid + 1) * n_chunks / W;
+    }
+    return {c0, U, (c1 - c0 + U - 1) / U, c1};
 }
 
 // Loads the kUnroll chunks starting at chunk c; chunks at or past c1 (another
 // wave's) and elements past n read as zeros.
-template <int XT>
-__device__ __forceinline__ void load_group(Raw<XT> (&raw)[kUnroll], const void* x, int64_t n,
+template <int XT, int U = kUnroll>
+__device__ __forceinline__ void load_group(Raw<XT> (&raw)[U], const void* x, int64_t n,
                                            int64_t c, int64_t c1, int lane) {
     constexpr int E = XT == 0 ? 2 : 4;
     const int64_t first = c * kChunk;
-    int64_t avail = (c1 - c < kUnroll ? c1 - c : kUnroll) * kChunk;
+    int64_t avail = (c1 - c < U ? c1 - c : U) * kChunk;
     if (avail > n - first) avail = n - first;
     const Rsrc r = make_rsrc(static_cast<const char*>(x) + first * E, avail * E);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
         if constexpr (XT == 0) {
             raw[u].w = buf_load16(r, u * kChunk * E + lane * 16);
         } else {
@@ -455,53 +493,34 @@ __device__ __forceinline__ void add_block(Acc& acc, bool zero, double sse, doubl
     acc.sumsq += ss;
 }
 
-// Each workgroup writes its binary64 partial terms to slot blockIdx.x of the
-// partial arrays; a separate one-workgroup kernel (k_finalize) sums them in
-// index order.  The kernel boundary is what makes the partials visible across
-// XCDs, so no device-scope fence (an L2 write-back per workgroup) is needed.
-__device__ void write_partial(const Acc& a, double* partials) {
-    __shared__ double s_acc[kWaves][4];
-    __shared__ long long s_cnt[kWaves];
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const double t0 = wave_sum(a.nonmax), t1 = wave_sum(a.max), t2 = wave_sum(a.zero),
-                 t3 = wave_sum(a.sumsq);
-    const long long tc = wave_sum_i64((long long)a.nzero);
-    if (lane == 0) {
-        s_acc[wave][0] = t0; s_acc[wave][1] = t1; s_acc[wave][2] = t2; s_acc[wave][3] = t3;
-        s_cnt[wave] = tc;
-    }
-    __syncthreads();
-    if (threadIdx.x < 5) {
-        const int k = threadIdx.x;
-        double* slot = partials + (size_t)k * kMaxGroups + blockIdx.x;
-        if (k < 4) {
-            double s = 0.0;
-            for (int w = 0; w < kWaves; ++w) s += s_acc[w][k];
-            *slot = s;
-        } else {
-            long long c = 0;
-            for (int w = 0; w < kWaves; ++w) c += s_cnt[w];
-            *reinterpret_cast<long long*>(slot) = c;
-        }
-    }
-}
+// Where the tensor terms go: per-workgroup binary64 partials (structure of
+// arrays, slot blockIdx.x of each term), summed in index order by k_finalize
+// after the producing kernel.  (Summing them in the producing kernel's last
+// workgroup needs a device-scope release per workgroup, which on this chip
+// writes back every dirty L2 line of the XCD; with the output streams in
+// flight that cost more than the separate kernel.)
+struct StatsOut {
+    double* partials;
+    void* stats;               // fp4q_stats
+    long long n_blocks;
+    const double* sumsq_part;  // sum x^2 of the amax pre-pass, or NULL
+    int G_sumsq;
+};
 
-// Fixed-order sum of G workgroup partials into the fp4q_stats struct (one
-// workgroup): thread i sums entries i, i + 256, ... of each term in index
-// order, then a fixed butterfly within each wave and the waves in order.
-// Each batch loads 8 entries of every term before adding any, so a whole batch
-// costs one memory round trip.  When sumsq_part is given (the amax pre-pass
-// computed sum x^2 in its G_sumsq workgroups), the sum x^2 term comes from it
-// instead of the quantize partials.
-__global__ __launch_bounds__(kThreads) void k_finalize(const double* partials, int G, void* stats,
-                                                       long long n_blocks,
-                                                       const double* sumsq_part, int G_sumsq) {
+// Fixed-order sum of G partials into the fp4q_stats struct, by one workgroup:
+// thread i sums entries i, i + 256, ... of each term in index order, then a
+// fixed butterfly within each wave and the waves in order.  Each batch loads 8
+// entries of every term before adding any, so a batch costs one memory round
+// trip.  When sumsq_part is given (the amax pre-pass computed sum x^2 in its
+// G_sumsq workgroups), the sum x^2 term comes from it.
+__device__ void sum_partials(const StatsOut& so, int G) {
     __shared__ double s_t[kWaves][4];
     __shared__ long long s_c[kWaves];
     constexpr int kBatch = 8;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const double* ssq = sumsq_part ? sumsq_part : partials + 3 * (size_t)kMaxGroups;
-    const int Gs = sumsq_part ? G_sumsq : G;
+    const double* partials = so.partials;
+    const double* ssq = so.sumsq_part ? so.sumsq_part : partials + 3 * (size_t)kMaxGroups;
+    const int Gs = so.sumsq_part ? so.G_sumsq : G;
     const long long* cnt = reinterpret_cast<const long long*>(partials + 4 * (size_t)kMaxGroups);
     const int n_max = G > Gs ? G : Gs;
     double t[4] = {0.0, 0.0, 0.0, 0.0};
@@ -539,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(const double* partials, i
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        double* out = static_cast<double*>(stats);
+        double* out = static_cast<double*>(so.stats);
         long long cz = 0;
         for (int k = 0; k < 4; ++k) {
             double s = 0.0;
@@ -547,10 +566,38 @@ __global__ __launch_bounds__(kThreads) void k_finalize(const double* partials, i
             out[k] = s;
         }
         for (int w = 0; w < kWaves; ++w) cz += s_c[w];
-        reinterpret_cast<long long*>(out)[4] = n_blocks;
+        reinterpret_cast<long long*>(out)[4] = so.n_blocks;
         reinterpret_cast<long long*>(out)[5] = cz;
     }
 }
+
+// Each workgroup writes its partial terms to slot blockIdx.x; the kernel
+// boundary makes them visible to k_finalize on every XCD.
+__device__ void write_partial(const Acc& a, const StatsOut& so) {
+    __shared__ double s_acc[kWaves][4];
+    __shared__ long long s_cnt[kWaves];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const double t0 = wave_sum(a.nonmax), t1 = wave_sum(a.max), t2 = wave_sum(a.zero),
+                 t3 = wave_sum(a.sumsq);
+    const long long tc = wave_sum_i64((long long)a.nzero);
+    if (lane == 0) {
+        s_acc[wave][0] = t0; s_acc[wave][1] = t1; s_acc[wave][2] = t2; s_acc[wave][3] = t3;
+        s_cnt[wave] = tc;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 0; k < 4; ++k) {
+            double s = 0.0;
+            for (int w = 0; w < kWaves; ++w) s += s_acc[w][k];
+            so.partials[(size_t)k * kMaxGroups + blockIdx.x] = s;
+        }
+        long long c = 0;
+        for (int w = 0; w < kWaves; ++w) c += s_cnt[w];
+        reinterpret_cast<long long*>(so.partials + 4 * (size_t)kMaxGroups)[blockIdx.x] = c;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_finalize(StatsOut so, int G) { sum_partials(so, G); }
 
 // ------------------------------------------------------------ quantize
 struct QParams {
@@ -568,8 +615,7 @@ struct QParams {
     const uint32_t* amax_part;
     int n_amax;
     float* g_out;
-    double* partials;
-    void* stats;
+    StatsOut so;
 };
 
 // Per-kernel UE scale context: g, D = RN32(6 g), rD = RN32(1 / D), whether the
@@ -586,10 +632,10 @@ struct QOut {
     Rsrc codes, scales, mse;
 };
 
-template <int B>
+template <int B, int U>
 __device__ __forceinline__ QOut group_outputs(const QParams& p, int64_t c, int64_t c1) {
     const int64_t first = c * kChunk;
-    int64_t avail = (c1 - c < kUnroll ? c1 - c : kUnroll) * kChunk;
+    int64_t avail = (c1 - c < U ? c1 - c : U) * kChunk;
     if (avail > p.n - first) avail = p.n - first;
     QOut o;
     o.codes = make_rsrc(p.codes + first / 2, avail / 2);
@@ -667,8 +713,8 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
         }
     }
     const int blk = u * kBlocks + lane / L;  // block index within the group
-    __builtin_amdgcn_raw_buffer_store_b32(cw, o.codes, (u * kChunk + lane * kLaneElems) / 2, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, o.scales, gl == 0 ? blk : kDropped, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(cw, o.codes, (u * kChunk + lane * kLaneElems) / 2, 0, kStNt);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, o.scales, gl == 0 ? blk : kDropped, 0, kStNt);
     if constexpr (ERR) {
         double sse = 0.0, ss = 0.0;
 #pragma unroll
@@ -688,7 +734,7 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
             if (SUMSQ && p.mse_kind == kMseRel) mse = ss > 0.0 ? (float)(sse / ss) : 0.0f;
             else mse = (float)(sse * (1.0 / B));
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mse), o.mse,
-                                                  gl == 0 ? blk * 4 : kDropped, 0, 0);
+                                                  gl == 0 ? blk * 4 : kDropped, 0, kStNt);
         }
         // Zero-filled lanes past the end form all-zero blocks, which add 0 to
         // every term and are not zero-rounded (m = 0).
@@ -713,16 +759,23 @@ __device__ float dynamic_g(const uint32_t* part, int n_part) {
     return g > 0.0f ? g : 1.0f;
 }
 
+#ifndef FP4Q_QUANT_WPE
+#define FP4Q_QUANT_WPE 0
+#endif
 template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ>
-__global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
+__global__ __launch_bounds__(kThreads)
+#if FP4Q_QUANT_WPE
+__attribute__((amdgpu_waves_per_eu(FP4Q_QUANT_WPE)))
+#endif
+void k_quantize(QParams p) {
     constexpr int L = B / kLaneElems;
     const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
-    const WaveRange wr = wave_range(p.n_chunks, p.cpw);
+    const WaveRange wr = wave_range<kWaves, kQuantUnroll>(p.n_chunks, p.cpw);
     // The first group's loads go out before the per-workgroup set-up below, so
     // that set-up overlaps their latency.
-    Raw<XT> cur[kUnroll];
-    if (wr.c0 < wr.c1) load_group<XT>(cur, p.x, p.n, wr.c0, wr.c1, lane);
+    Raw<XT> cur[kQuantUnroll];
+    if (wr.n > 0) load_group<XT, kQuantUnroll>(cur, p.x, p.n, wr.c0, wr.c1, lane);
     UeCtx ue{1.0f, 6.0f, 0.0f, 4096.0f, nullptr};
     if constexpr (FMT != kFmtMx) {
         __shared__ float4 s_tab[kUeCodes];
@@ -741,27 +794,27 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
         ue.tab = s_tab;
     }
     Acc acc;
-    for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
-        const QOut o = group_outputs<B>(p, c, wr.c1);
+    for (int64_t i = 0, c = wr.c0; i < wr.n; ++i, c += wr.step) {
+        const QOut o = group_outputs<B, kQuantUnroll>(p, c, wr.c1);
         const int64_t left = wr.c1 - c;  // wave-uniform
 #if FP4Q_PREFETCH
-        Raw<XT> nxt[kUnroll];
-        if (c + kUnroll < wr.c1) load_group<XT>(nxt, p.x, p.n, c + kUnroll, wr.c1, lane);
+        Raw<XT> nxt[kQuantUnroll];
+        if (i + 1 < wr.n) load_group<XT, kQuantUnroll>(nxt, p.x, p.n, c + wr.step, wr.c1, lane);
 #endif
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < kQuantUnroll; ++u)
             if (u < left)
                 quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ>(cur[u], u, o, p, ue, lane, gl, acc);
 #if FP4Q_PREFETCH
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+        for (int u = 0; u < kQuantUnroll; ++u) cur[u] = nxt[u];
 #else
-        if (c + kUnroll < wr.c1) load_group<XT>(cur, p.x, p.n, c + kUnroll, wr.c1, lane);
+        if (i + 1 < wr.n) load_group<XT, kQuantUnroll>(cur, p.x, p.n, c + wr.step, wr.c1, lane);
 #endif
     }
-    if (p.stats) {
+    if (p.so.stats) {
         if (gl != 0) acc = Acc{};  // every lane of a block holds its terms: keep one copy
-        write_partial(acc, p.partials);
+        write_partial(acc, p.so);
     }
 }
 
@@ -801,32 +854,32 @@ __device__ __forceinline__ uint32_t chunk_absmax_bits(const Raw<XT>& raw, int gl
 }
 
 template <int XT, int ROT, bool SUMSQ>
-__global__ __launch_bounds__(kThreads) void k_amax(AParams p) {
-    __shared__ uint32_t s_m[kWaves];
-    __shared__ double s_ss[kWaves];
+__global__ __launch_bounds__(kAmaxThreads) void k_amax(AParams p) {
+    __shared__ uint32_t s_m[kAmaxWaves];
+    __shared__ double s_ss[kAmaxWaves];
     constexpr int L = ROT ? ROT / kLaneElems : 1;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int gl = lane & (L - 1);
-    const WaveRange wr = wave_range(p.n_chunks, p.cpw);
+    const WaveRange wr = wave_range<kAmaxWaves, kAmaxUnroll>(p.n_chunks, p.cpw);
     uint32_t mx = 0;
     double ss = 0.0;
     // Elements past the wave's range read as zeros, which leave both the
     // maximum and the sum of squares unchanged.
 #if FP4Q_PREFETCH
-    Raw<XT> cur[kUnroll];
-    if (wr.c0 < wr.c1) load_group<XT>(cur, p.x, p.n, wr.c0, wr.c1, lane);
+    Raw<XT> cur[kAmaxUnroll];
+    if (wr.n > 0) load_group<XT, kAmaxUnroll>(cur, p.x, p.n, wr.c0, wr.c1, lane);
 #endif
-    for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
+    for (int64_t i = 0, c = wr.c0; i < wr.n; ++i, c += wr.step) {
 #if FP4Q_PREFETCH
-        Raw<XT> nxt[kUnroll];
-        if (c + kUnroll < wr.c1) load_group<XT>(nxt, p.x, p.n, c + kUnroll, wr.c1, lane);
+        Raw<XT> nxt[kAmaxUnroll];
+        if (i + 1 < wr.n) load_group<XT, kAmaxUnroll>(nxt, p.x, p.n, c + wr.step, wr.c1, lane);
 #else
-        Raw<XT> cur[kUnroll];
-        load_group<XT>(cur, p.x, p.n, c, wr.c1, lane);
+        Raw<XT> cur[kAmaxUnroll];
+        load_group<XT, kAmaxUnroll>(cur, p.x, p.n, c, wr.c1, lane);
 #endif
         const int64_t left = wr.c1 - c;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kAmaxUnroll; ++u) {
             if (u < left) {
                 double cs = 0.0;
                 mx = max(mx, chunk_absmax_bits<XT, ROT, SUMSQ>(cur[u], gl, cs));
@@ -835,7 +888,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(AParams p) {
         }
 #if FP4Q_PREFETCH
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+        for (int u = 0; u < kAmaxUnroll; ++u) cur[u] = nxt[u];
 #endif
     }
     mx = wave_max(mx);
@@ -847,11 +900,11 @@ __global__ __launch_bounds__(kThreads) void k_amax(AParams p) {
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t m = s_m[0];
-        for (int w = 1; w < kWaves; ++w) m = max(m, s_m[w]);
+        for (int w = 1; w < kAmaxWaves; ++w) m = max(m, s_m[w]);
         p.part[blockIdx.x] = m;
         if constexpr (SUMSQ) {
             double t = 0.0;
-            for (int w = 0; w < kWaves; ++w) t += s_ss[w];
+            for (int w = 0; w < kAmaxWaves; ++w) t += s_ss[w];
             p.sumsq[blockIdx.x] = t;
         }
     }
@@ -907,7 +960,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant(DParams p) {
     const int gl = lane & (L - 1);
     const float g = (FMT != kFmtMx && p.g) ? *p.g : 1.0f;
     const WaveRange wr = wave_range(p.n_chunks, p.cpw);
-    for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
+    for (int64_t i = 0, c = wr.c0; i < wr.n; ++i, c += wr.step) {
         uint32_t cw[kUnroll], sb[kUnroll];
         load_codes<B>(p.codes, p.scales, p.n, c, wr.c1, lane, cw, sb);
         const int64_t first = c * kChunk;
@@ -954,8 +1007,7 @@ struct MParams {
     int64_t n, n_chunks, n_blocks, cpw;
     float* block_mse;
     int mse_kind;
-    double* partials;
-    void* stats;
+    StatsOut so;
 };
 
 // Same work split, per-element arithmetic and accumulation order as
@@ -970,7 +1022,7 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MParams p) {
     const float g = (FMT != kFmtMx && p.g) ? *p.g : 1.0f;
     const WaveRange wr = wave_range(p.n_chunks, p.cpw);
     Acc acc;
-    for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
+    for (int64_t i = 0, c = wr.c0; i < wr.n; ++i, c += wr.step) {
         Raw<XT> raw[kUnroll];
         uint32_t cw[kUnroll], sb[kUnroll];
         load_group<XT>(raw, p.x, p.n, c, wr.c1, lane);
@@ -1036,9 +1088,9 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MParams p) {
             add_block(acc, (m > 0.0f) && !any_nz, sse, (double)e_key * (double)e_key, ss);
         }
     }
-    if (p.stats) {
+    if (p.so.stats) {
         if (gl != 0) acc = Acc{};
-        write_partial(acc, p.partials);
+        write_partial(acc, p.so);
     }
 }
 
@@ -1055,7 +1107,7 @@ __global__ __launch_bounds__(kThreads) void k_rotate(RParams p) {
     const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
     const WaveRange wr = wave_range(p.n_chunks, p.cpw);
-    for (int64_t c = wr.c0; c < wr.c1; c += kUnroll) {
+    for (int64_t i = 0, c = wr.c0; i < wr.n; ++i, c += wr.step) {
         Raw<XT> raw[kUnroll];
         load_group<XT>(raw, p.x, p.n, c, wr.c1, lane);
         const int64_t first = c * kChunk;
@@ -1097,7 +1149,7 @@ int64_t chunks_of(int64_t n) { return (n + kChunk - 1) / kChunk; }
 
 // Workgroups of `kernel` that fit on the current device at once (compute units
 // times the occupancy its registers and LDS allow), cached per device and kernel.
-int resident_groups(const void* kernel) {
+int resident_groups(const void* kernel, int threads) {
     struct Entry {
         int dev;
         const void* kernel;
@@ -1117,7 +1169,7 @@ int resident_groups(const void* kernel) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
         per_cu <= 0)
         per_cu = 1;
     const int groups = cus * per_cu;
@@ -1129,9 +1181,9 @@ int resident_groups(const void* kernel) {
 // Grid of a streaming kernel over `chunks` 512-element chunks: one round of
 // resident workgroups (so no workgroup waits for a second round), fewer when
 // the tensor gives each wave under kMinChunksPerWave chunks.
-int grid_for_chunks(int64_t chunks, const void* kernel) {
-    int64_t want = (chunks + (int64_t)kWaves * kMinChunksPerWave - 1) / ((int64_t)kWaves * kMinChunksPerWave);
-    const int64_t cap = (int64_t)resident_groups(kernel) * kGridRounds;
+int grid_for_chunks(int64_t chunks, const void* kernel, int waves = kWaves) {
+    int64_t want = (chunks + (int64_t)waves * kMinChunksPerWave - 1) / ((int64_t)waves * kMinChunksPerWave);
+    const int64_t cap = (int64_t)resident_groups(kernel, waves * kWave) * kGridRounds;
     if (want > cap) want = cap;
     if (want > kMaxGroups) want = kMaxGroups;
     if (want < 1) want = 1;
@@ -1145,18 +1197,25 @@ struct Split {
 
 // Fixed ranges of `cpw` chunks per wave when that grid fits the workspace's
 // partial slots, else the balanced one-round split.
-Split split_for(int64_t chunks, const void* kernel, int cpw) {
+Split split_for(int64_t chunks, const void* kernel, int cpw, int waves = kWaves) {
+    if (cpw < 0) return {grid_for_chunks(chunks, kernel, waves), cpw};
     if (cpw > 0) {
-        const int64_t G = (chunks + (int64_t)kWaves * cpw - 1) / ((int64_t)kWaves * cpw);
+        const int64_t G = (chunks + (int64_t)waves * cpw - 1) / ((int64_t)waves * cpw);
         if (G <= kMaxGroups) return {(int)G, cpw};
     }
-    return {grid_for_chunks(chunks, kernel), 0};
+    return {grid_for_chunks(chunks, kernel, waves), 0};
 }
 
 int report(hipError_t e, const char* what, char* msg, size_t len) {
     if (e == hipSuccess) return 0;
     snprintf(msg, len, "%s: %s", what, hipGetErrorString(e));
     return (int)e;
+}
+
+// Sums the partials of a G-workgroup stats kernel.
+int launch_finalize(const StatsOut& so, int G, hipStream_t st, char* msg, size_t len) {
+    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kThreads), 0, st, so, G);
+    return report(hipGetLastError(), "finalize kernel launch", msg, len);
 }
 
 typedef void (*QuantKernel)(QParams);
@@ -1270,8 +1329,11 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     p.mse_kind = j.mse_kind;
     p.fmt = j.fmt;
     p.g_in = nullptr;
-    p.stats = j.stats;
-    if (ws) p.partials = reinterpret_cast<double*>(ws + kWsPartials);
+    p.so.stats = j.stats;
+    p.so.n_blocks = j.n / j.block;
+    if (ws) {
+        p.so.partials = reinterpret_cast<double*>(ws + kWsPartials);
+    }
     const bool err = (j.block_mse != nullptr) || (j.stats != nullptr);
     const bool rel = (j.block_mse != nullptr && j.mse_kind == kMseRel);
     // In the dynamic mode the amax pass reads every element anyway; when sum x^2
@@ -1292,17 +1354,17 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     const Split sq = split_for(chunks, reinterpret_cast<const void*>(k), kQuantCpw);
     const int G = sq.G;
     p.cpw = sq.cpw;
-    const double* amax_sumsq = nullptr;
     int G_amax = 0;
     if (j.fmt != kFmtMx && j.gmode != 0) {
         if (dynamic) {
             const AmaxKernel ka = pick_amax(j.xt, j.rotate, sumsq_in_amax);
-            const Split sa = split_for(chunks, reinterpret_cast<const void*>(ka), kAmaxCpw);
+            const Split sa = split_for(chunks, reinterpret_cast<const void*>(ka), kAmaxCpw, kAmaxWaves);
             AParams a{j.x, j.n, chunks, sa.cpw, reinterpret_cast<uint32_t*>(ws + kWsAmax),
                       sumsq_in_amax ? reinterpret_cast<double*>(ws + kWsAmaxSumsq) : nullptr};
-            amax_sumsq = a.sumsq;
+            p.so.sumsq_part = a.sumsq;
+            p.so.G_sumsq = sa.G;
             G_amax = sa.G;
-            hipLaunchKernelGGL(ka, dim3(G_amax), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL(ka, dim3(G_amax), dim3(kAmaxThreads), 0, st, a);
             int rc = report(hipGetLastError(), "amax kernel launch", msg, msg_len);
             if (rc) return rc;
             p.amax_part = a.part;
@@ -1315,9 +1377,7 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
     int rc = report(hipGetLastError(), "quantize kernel launch", msg, msg_len);
     if (rc || !j.stats) return rc;
-    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kThreads), 0, st, p.partials, G, j.stats,
-                       (long long)p.n_blocks, amax_sumsq, G_amax);
-    return report(hipGetLastError(), "finalize kernel launch", msg, msg_len);
+    return launch_finalize(p.so, G, st, msg, msg_len);
 }
 
 int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len) {
@@ -1360,9 +1420,10 @@ int launch_block_mse(const MseJob& j, char* msg, size_t msg_len) {
     p.n_blocks = j.n / j.block;
     p.block_mse = j.block_mse;
     p.mse_kind = j.mse_kind;
-    p.stats = j.stats;
+    p.so.stats = j.stats;
+    p.so.n_blocks = j.n / j.block;
     if (ws) {
-        p.partials = reinterpret_cast<double*>(ws + kWsPartials);
+        p.so.partials = reinterpret_cast<double*>(ws + kWsPartials);
     }
     const bool sumsq = (j.stats != nullptr) || (j.mse_kind == kMseRel);
     MseKernel k;
@@ -1378,9 +1439,7 @@ int launch_block_mse(const MseJob& j, char* msg, size_t msg_len) {
     hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
     int rc = report(hipGetLastError(), "block-mse kernel launch", msg, msg_len);
     if (rc || !j.stats) return rc;
-    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kThreads), 0, st, p.partials, G, j.stats,
-                       (long long)p.n_blocks, (const double*)nullptr, 0);
-    return report(hipGetLastError(), "finalize kernel launch", msg, msg_len);
+    return launch_finalize(p.so, G, st, msg, msg_len);
 }
 
 int launch_rotate(const RotateJob& j, char* msg, size_t msg_len) {
