@@ -6,6 +6,8 @@ Default workload (one step = the whole path over one batch):
   the per-tensor amax pass, then block-16 UE4M3 scales under the dynamic FP32
   per-tensor scale, E2M1 codes packed two per byte, dequantization, per-block
   MSE and the three-term error split.  Inputs are resident in HBM before timing.
+  The step spreads its independent per-tensor calls over two HIP streams (one
+  workspace each; --streams 1 runs them back to back on one stream).
 
 Prints one JSON line.  `value` is GB/s of input quantized+packed+MSE'd over
 the whole step (all kernels of all tensors).  For the default workload
@@ -176,19 +178,32 @@ WORKLOADS = {
 
 # ------------------------------------------------------------------ running
 class Runner:
-    """Device buffers and calls for every (tensor, spec) pair of a workload."""
+    """Device buffers and calls for every (tensor, spec) pair of a workload.
 
-    def __init__(self, fq, torch, dev, xs, specs):
+    The step issues its calls round-robin over `n_streams` HIP streams (default
+    priority, one workspace each), so that independent calls overlap: one
+    tensor's memory-bound amax pass runs beside another's quantize pass.  The
+    streams join the caller's stream at the start and end of every step."""
+
+    def __init__(self, fq, torch, dev, xs, specs, n_streams=1):
         self.fq, self.torch, self.dev, self.xs, self.specs = fq, torch, dev, xs, specs
-        self.ws = fq.workspace(dev)
+        self.streams = [torch.cuda.current_stream(dev)] + [torch.cuda.Stream(dev)
+                                                           for _ in range(n_streams - 1)]
+        ws_bytes = fq.workspace_bytes()
+        self.wss = [fq.workspace(dev)] + [torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+                                          for _ in range(n_streams - 1)]
+        self.ws = self.wss[0]
         self.out = {}
-        # Outputs are shared by tensors of one shape (each call overwrites them);
-        # g and stats are per call so the given-g replay can reuse the step's g.
+        # Outputs are shared by the calls of one stream on tensors of one shape
+        # (each call overwrites them); g and stats are per call so the given-g
+        # replay can reuse the step's g.
         shared = {}
+        k = 0
         for ti, x in enumerate(xs):
             r, c = x.shape
             for si, s in enumerate(specs):
-                key = (r, c, s.block)
+                key = (r, c, s.block, k % n_streams)
+                k += 1
                 if key not in shared:
                     shared[key] = dict(
                         codes=torch.empty((r, c // 2), dtype=torch.uint8, device=dev),
@@ -197,26 +212,42 @@ class Runner:
                 o = dict(shared[key])
                 o["stats"] = fq.new_stats(dev)
                 o["g"] = torch.ones(1, dtype=torch.float32, device=dev)
+                o["stream"] = key[3]
                 self.out[(ti, si)] = o
 
-    def call(self, ti, si, given=False):
+    def call(self, ti, si, given=False, ws=None):
         fq, x, s, o = self.fq, self.xs[ti], self.specs[si], self.out[(ti, si)]
+        ws = self.ws if ws is None else ws
         bm = o["block_mse"] if s.block_mse else False
         if s.fmt == "mx":
             st = o["stats"] if (s.stats and not given) else False
             fq.mxfp4_quantize(x, s.rotate, codes=o["codes"], scales=o["scales"], block_mse=bm,
-                              mse_kind=s.mse_kind, stats=st, ws=self.ws)
+                              mse_kind=s.mse_kind, stats=st, ws=ws)
         else:
             gmode = fq.G_GIVEN if (given and s.gmode == 1) else s.gmode
             st = o["stats"] if (s.stats and not given) else False
             fq.nvfp4_quantize(x, s.block, s.scale_fmt, gmode, o["g"], s.rotate, codes=o["codes"],
                               scales=o["scales"], block_mse=bm, mse_kind=s.mse_kind, stats=st,
-                              ws=self.ws)
+                              ws=ws)
 
     def step(self, given=False):
+        """All calls of one step; with given=True each runs alone on the caller's
+        stream (the roofline leg)."""
+        if given or len(self.streams) == 1:
+            for ti in range(len(self.xs)):
+                for si in range(len(self.specs)):
+                    self.call(ti, si, given)
+            return
+        main = self.streams[0]
+        for st in self.streams[1:]:
+            st.wait_stream(main)
         for ti in range(len(self.xs)):
             for si in range(len(self.specs)):
-                self.call(ti, si, given)
+                k = self.out[(ti, si)]["stream"]
+                with self.torch.cuda.stream(self.streams[k]):
+                    self.call(ti, si, False, self.wss[k])
+        for st in self.streams[1:]:
+            main.wait_stream(st)
 
 
 def time_region(torch, stream, fn, reps):
@@ -261,6 +292,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen7", choices=sorted(WORKLOADS))
+    ap.add_argument("--streams", type=int, default=2,
+                    help="HIP streams the step's independent calls are spread over")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain device copy of the first tensor (a kernel of "
                          "known traffic, for scaling rocprofv3 byte counters)")
@@ -286,7 +319,7 @@ def main():
         xs.append(x.to(dev))
         del x
     in_bytes = xs[0].element_size()
-    run = Runner(fq, torch, dev, xs, w.specs)
+    run = Runner(fq, torch, dev, xs, w.specs, max(1, args.streams))
     n_elem_calls = sum(x.numel() for x in xs) * len(w.specs)
     alg_bytes = sum(s.algorithmic_bytes(x.numel(), in_bytes) for x in xs for s in w.specs)
 
@@ -339,7 +372,8 @@ def main():
         dst.copy_(xs[0])
         torch.cuda.synchronize()
 
-    config = {"workload": w.name, **w.config, "elements_per_step": n_elem_calls}
+    config = {"workload": w.name, **w.config, "elements_per_step": n_elem_calls,
+              "streams": max(1, args.streams)}
     line = {
         "metric": METRIC,
         "value": round(value, 2),
