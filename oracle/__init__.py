@@ -88,6 +88,9 @@ def _bind(lib):
     lib.oracle_quantize.argtypes = [P, i64, i64, c.c_int, c.c_int, c.c_int, P, c.c_int,
                                     P, P, P, c.c_int, P, P]
     lib.oracle_quantize.restype = c.c_int
+    lib.oracle_quantize_search.argtypes = [P, i64, i64, c.c_int, c.c_int, c.c_int, P, c.c_int,
+                                           c.c_int, P, P, P, c.c_int, P, P]
+    lib.oracle_quantize_search.restype = c.c_int
     lib.oracle_dequantize.argtypes = [P, P, c.c_int, c.c_int, c.c_float, i64, i64, c.c_int, P]
     lib.oracle_dequantize.restype = c.c_int
     lib.oracle_block_mse.argtypes = [P, P, P, c.c_int, c.c_int, c.c_float, i64, i64, c.c_int,
@@ -189,6 +192,30 @@ def quantize(x, fmt: int, block: int, gmode: int = GMODE_NONE, g: float | None =
                                 _ptr(cnt))
     if rc:
         raise OracleError("quantize: bad arguments")
+    return {"codes": codes, "scales": scales, "block_mse": mse, "terms": acc, "counts": cnt,
+            "g": float(gbuf[0])}
+
+
+def quantize_search(x, fmt: int, block: int, gmode: int = GMODE_NONE, g: float | None = None,
+                    rotate: int = 0, radius: int = 1, mse_kind: int = MSE_ABS) -> dict:
+    """Quantize with the per-block scale search of reading R8 (the max-based scale
+    code and its neighbours within ``radius``, lowest block SSE).  Returns the
+    same dict as :func:`quantize`."""
+    a = _f32_2d(x)
+    rows, cols = a.shape
+    if cols % block:
+        raise OracleError("cols must be a multiple of the block size")
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // block), np.uint8)
+    mse = np.zeros((rows, cols // block), np.float32)
+    acc = np.zeros(4, np.float64)
+    cnt = np.zeros(2, np.int64)
+    gbuf = np.array([1.0 if g is None else g], np.float32)
+    rc = load().oracle_quantize_search(_ptr(a), rows, cols, fmt, block, gmode, _ptr(gbuf), rotate,
+                                       radius, _ptr(codes), _ptr(scales), _ptr(mse), mse_kind,
+                                       _ptr(acc), _ptr(cnt))
+    if rc:
+        raise OracleError("quantize_search: bad arguments")
     return {"codes": codes, "scales": scales, "block_mse": mse, "terms": acc, "counts": cnt,
             "g": float(gbuf[0])}
 

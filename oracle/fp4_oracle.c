@@ -49,6 +49,9 @@
  *   R7  UE5M3 (unsigned, 5 exponent bits, 3 mantissa bits, bias 15): values
  *       j*2^-17 (e = 0) and (1 + j/8)*2^(e-15) (e = 1..30); exponent 31 is
  *       reserved; largest value 1.875 * 2^15 = 61440.
+ *   R8  Scale search: the max-based code and its neighbours within a radius,
+ *       scored by block SSE, visited nearest first, replaced only when better
+ *       by more than a relative 2^-40 (see oracle_quantize_search).
  */
 #include <math.h>
 #include <stddef.h>
@@ -436,6 +439,94 @@ int oracle_quantize(const float* x, int64_t rows, int64_t cols, int fmt, int blo
                 codes[byte_idx] = (uint8_t)(cd[i] | (cd[i + 1] << 4));
             }
             float mse = block_error(v, xh, block, mse_kind, acc, cnt);
+            if (block_mse) block_mse[r * nblk_row + k] = mse;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Scale search ([MRGPTQ] Sommario tecnico section 3 item 2: scales chosen to
+ * minimise the reconstruction MSE instead of the max-based scale; the page
+ * gives no search procedure).  Reading R8:
+ *   - Candidates are the max-based scale code c0 (the one oracle_quantize
+ *     picks) and its neighbours c0 + j, 0 < |j| <= radius, that lie in the
+ *     format's code range: MXFP4 bytes 0..254, UE4M3 0..0x7E, UE5M3 0..0xF7.
+ *     Consecutive bytes are consecutive scale values in all three formats.
+ *   - Each candidate is scored by its block SSE in binary64, with the
+ *     elements coded and dequantized exactly as oracle_quantize does under
+ *     that scale code.
+ *   - Candidates are visited in the order j = 0, -1, +1, -2, +2, ...; one
+ *     replaces the best so far only when its SSE is below
+ *     best - best * 2^-40.  Near-ties therefore keep the code closest to c0
+ *     (the smaller code first), and the choice does not hinge on the last
+ *     bits of a sum.
+ *   - The chosen code's codes, dequantized values and error split are the
+ *     outputs, as in oracle_quantize.  The per-tensor scale g is found as
+ *     there; no search over g.
+ */
+static double block_sse_under(int fmt, const float* v, int b, block_scale s, int* cd, float* xh)
+{
+    double sse = 0.0;
+    for (int i = 0; i < b; ++i) {
+        cd[i] = element_code(fmt, v[i], s);
+        xh[i] = element_value(fmt, cd[i], s);
+        double e = (double)v[i] - (double)xh[i];
+        sse += e * e;
+    }
+    return sse;
+}
+
+int oracle_quantize_search(const float* x, int64_t rows, int64_t cols, int fmt, int block,
+                           int gmode, float* g, int rotate, int radius, uint8_t* codes,
+                           uint8_t* scales, float* block_mse, int mse_kind, double* acc,
+                           int64_t* cnt)
+{
+    if (!valid_shape(fmt, block, rows, cols, rotate)) return ORACLE_BAD_ARG;
+    if (fmt != FMT_UE4M3 && gmode != GMODE_NONE) return ORACLE_BAD_ARG;
+    if (radius < 0 || radius > 8) return ORACLE_BAD_ARG;
+    float gv = 1.0f;
+    if (fmt == FMT_UE4M3) {
+        if (gmode == GMODE_DYNAMIC) {
+            gv = oracle_dynamic_g(oracle_tensor_amax(x, rows, cols, rotate));
+            if (g) *g = gv;
+        } else if (gmode == GMODE_GIVEN) {
+            if (!g) return ORACLE_BAD_ARG;
+            gv = *g;
+        }
+    }
+    const int max_byte = fmt == FMT_MXFP4 ? 254 : (fmt == FMT_UE4M3 ? 0x7E : 0xF7);
+    if (acc) memset(acc, 0, 4 * sizeof(double));
+    if (cnt) memset(cnt, 0, 2 * sizeof(int64_t));
+    int64_t nblk_row = cols / block;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t k = 0; k < nblk_row; ++k) {
+            const float* src = x + r * cols + k * block;
+            float v[256], xh[256], best_xh[256];
+            int cd[256], best_cd[256];
+            for (int i = 0; i < block; ++i) v[i] = src[i];
+            if (rotate) oracle_hadamard_block(v, rotate);
+            int c0 = scale_for_block(fmt, block_absmax(v, block), gv).byte;
+            int best_byte = c0;
+            double best_sse = 0.0;
+            for (int t = 0; t <= 2 * radius; ++t) {
+                int j = t == 0 ? 0 : ((t & 1) ? -(t + 1) / 2 : t / 2);
+                int byte = c0 + j;
+                if (byte < 0 || byte > max_byte) continue;
+                double sse = block_sse_under(fmt, v, block, scale_from_byte(fmt, byte, gv), cd, xh);
+                if (t == 0 || sse < best_sse - best_sse * 0x1p-40) {
+                    best_sse = sse;
+                    best_byte = byte;
+                    memcpy(best_cd, cd, sizeof(int) * (size_t)block);
+                    memcpy(best_xh, xh, sizeof(float) * (size_t)block);
+                }
+            }
+            scales[r * nblk_row + k] = (uint8_t)best_byte;
+            for (int i = 0; i < block; i += 2) {
+                int64_t byte_idx = (r * cols + k * block + i) / 2;
+                codes[byte_idx] = (uint8_t)(best_cd[i] | (best_cd[i + 1] << 4));
+            }
+            float mse = block_error(v, best_xh, block, mse_kind, acc, cnt);
             if (block_mse) block_mse[r * nblk_row + k] = mse;
         }
     }
