@@ -28,6 +28,8 @@ Workloads (--workload):
                scale at block sizes 256, 128, 64, 32, 16 and 8, MSE and split
   qwen14rot    bf16 13824 x 5120 Student-t(4) with 1 % outlier columns x20:
                MXFP4 and dynamic NVFP4, each without and with block rotation
+  qwen7search  the six default tensors, MXFP4 and dynamic NVFP4 with the per-block
+               scale search (radius 1)
   qwen14model  a random-init Qwen2.5-14B-shaped stack (48 layers x 7 projections,
                13.2e9 bf16 parameters, 26.4 GB) quantized whole to MXFP4 and to
                dynamic NVFP4, relative per-block MSE and per-tensor split
@@ -70,10 +72,11 @@ class Spec:
     """One quantization call applied to every tensor of a workload."""
 
     def __init__(self, tag, fmt, block, scale_fmt=1, gmode=0, rotate=0, mse_kind=0,
-                 block_mse=True, stats=True):
+                 block_mse=True, stats=True, radius=None):
         self.tag, self.fmt, self.block, self.scale_fmt = tag, fmt, block, scale_fmt
         self.gmode, self.rotate, self.mse_kind = gmode, rotate, mse_kind
         self.block_mse, self.stats = block_mse, stats
+        self.radius = radius  # per-block scale search radius, None for the plain call
 
     def algorithmic_bytes(self, n, in_bytes):
         """Bytes every kernel of the call must move: the amax pre-pass read (dynamic
@@ -91,6 +94,8 @@ class Spec:
             s += {0: "", 1: " dynamic g", 2: " given g"}[self.gmode]
         if self.rotate:
             s += f" rot{self.rotate}"
+        if self.radius is not None:
+            s += f" scale search radius {self.radius}"
         return s
 
 
@@ -165,6 +170,15 @@ WORKLOADS = {
         [Spec("mx32", "mx", 32), Spec("mx32_rot", "mx", 32, rotate=32),
          Spec("nv16_dyn", "nv", 16, 1, 1), Spec("nv16_dyn_rot", "nv", 16, 1, 1, rotate=16)],
         50, 5, ("the tensor, whole, 3 times", 1, 3, 2)),
+    "qwen7search": Workload(
+        "qwen2.5-7b-mlp-scale-search",
+        {"tensors": "6 bf16: 18944x3584 and 3584x18944, sigma 0.01/0.02/0.04",
+         "format": "MXFP4 b32 and NVFP4 b16 dynamic g, per-block scale search over the "
+                   "max-based code and its neighbours (radius 1)",
+         "outputs": "codes + scales + per-block MSE + three-term error split"},
+        _qwen7_tensors,
+        [Spec("mx32_search1", "mx", 32, radius=1), Spec("nv16_dyn_search1", "nv", 16, 1, 1, radius=1)],
+        20, 2, ("1 of the 6 tensors (18944x3584, sigma 0.01), whole", 1, 1, 1)),
     "qwen14model": Workload(
         "qwen2.5-14b-shaped-model-sweep",
         {"tensors": "336 bf16 (48 layers x q,k,v,o,gate,up,down), N(0, 0.02), 13.2e9 params",
@@ -219,7 +233,14 @@ class Runner:
         fq, x, s, o = self.fq, self.xs[ti], self.specs[si], self.out[(ti, si)]
         ws = self.ws if ws is None else ws
         bm = o["block_mse"] if s.block_mse else False
-        if s.fmt == "mx":
+        if s.radius is not None:
+            fmt = fq.FMT_MXFP4 if s.fmt == "mx" else s.scale_fmt
+            gmode = fq.G_GIVEN if (given and s.gmode == 1) else s.gmode
+            st = o["stats"] if (s.stats and not given) else False
+            fq.fp4_quantize_search(x, fmt, s.block, gmode, o["g"] if s.fmt == "nv" else None,
+                                   s.rotate, s.radius, codes=o["codes"], scales=o["scales"],
+                                   block_mse=bm, mse_kind=s.mse_kind, stats=st, ws=ws)
+        elif s.fmt == "mx":
             st = o["stats"] if (s.stats and not given) else False
             fq.mxfp4_quantize(x, s.rotate, codes=o["codes"], scales=o["scales"], block_mse=bm,
                               mse_kind=s.mse_kind, stats=st, ws=ws)
@@ -250,6 +271,29 @@ class Runner:
             main.wait_stream(st)
 
 
+def search_gain(fq, torch, run, si):
+    """For a scale-search spec: total SSE over the workload with the search and
+    with the max-based scales (radius 0), and their ratio."""
+    s = run.specs[si]
+    if s.radius is None or not s.stats:
+        return {}
+    tot = {}
+    for radius in (s.radius, 0):
+        acc = 0.0
+        for ti, x in enumerate(run.xs):
+            o = run.out[(ti, si)]
+            fmt = fq.FMT_MXFP4 if s.fmt == "mx" else s.scale_fmt
+            st = fq.new_stats(x.device)
+            fq.fp4_quantize_search(x, fmt, s.block, s.gmode, o["g"] if s.fmt == "nv" else None,
+                                   s.rotate, radius, codes=o["codes"], scales=o["scales"],
+                                   block_mse=False, stats=st, ws=run.ws)
+            d = fq.stats_dict(st)
+            acc += d["sse_nonmax"] + d["sse_max"] + d["sse_zero"]
+        tot[radius] = acc
+    return {"sse_with_search": tot[s.radius], "sse_max_based": tot[0],
+            "sse_ratio": round(tot[s.radius] / tot[0], 6)}
+
+
 def time_region(torch, stream, fn, reps):
     """ms per rep of fn, bracketed by HIP events on `stream`."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -276,7 +320,11 @@ def cpu_baseline(w, xs_host_sample):
         in_bytes = 4 if (hasattr(x, "dtype") and str(x.dtype) == "torch.float32") else 2
         for _ in range(repeat):
             t = time.perf_counter()
-            oracle.quantize(xf, fmt, s.block, gmode, None, s.rotate, s.mse_kind)
+            if s.radius is not None:
+                oracle.quantize_search(xf, fmt, s.block, gmode, None, s.rotate, s.radius,
+                                       s.mse_kind)
+            else:
+                oracle.quantize(xf, fmt, s.block, gmode, None, s.rotate, s.mse_kind)
             el += time.perf_counter() - t
             n += xf.size
     return {"value": round(n * in_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
@@ -363,6 +411,7 @@ def main():
             ms = time_region(torch, stream, fn, max(1, min(steps, 10)))
             nb = sum(s.algorithmic_bytes(x.numel(), in_bytes) for x in xs)
             breakdown[s.tag] = {"us_per_call": round(ms * 1e3 / len(xs), 2),
+                                **search_gain(fq, torch, run, si),
                                 "input_GBps": round(sum(x.numel() for x in xs) * in_bytes
                                                     / (ms * 1e-3) / 1e9, 1),
                                 "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}

@@ -153,6 +153,36 @@ fp4q_status nvfp4_quantize(const void* x, int32_t xt, int64_t rows, int64_t cols
                            fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Quantization with a per-block scale search ("Bridging the Gap...", Sommario
+ * tecnico section 3 item 2: scales chosen to minimise the reconstruction MSE
+ * rather than taken from the block maximum).  The page gives no procedure; this
+ * library's reading:
+ *   - candidates are the max-based scale code c0 (the code mxfp4_quantize /
+ *     nvfp4_quantize would write) and c0 + j for 0 < |j| <= radius, within the
+ *     format's codes (MXFP4 0..254, UE4M3 0..0x7E, UE5M3 0..0xF7);
+ *   - each is scored by the block's sum of squared errors in binary64, with
+ *     codes and dequantized values formed exactly as the plain calls do under
+ *     that code;
+ *   - candidates are visited as j = 0, -1, +1, -2, +2, ...; one replaces the
+ *     best so far only when its SSE is below best - best * 2^-40, so near-ties
+ *     keep the code closest to c0;
+ *   - codes, scales, block_mse and stats are those of the chosen code.
+ * The per-tensor scale g (UE4M3) is found as in nvfp4_quantize; it is not
+ * searched.  radius 0 gives exactly the plain calls' results.
+ *   fmt, block  FP4Q_FMT_MXFP4 (block 32, gmode NONE), UE4M3 or UE5M3 (block
+ *               8..256; UE5M3 with gmode NONE)
+ *   radius      0..FP4Q_SEARCH_MAX_RADIUS
+ * Other arguments and the workspace rule as for nvfp4_quantize.  The search
+ * costs about 2 * radius + 1 times the arithmetic of a plain call.
+ */
+#define FP4Q_SEARCH_MAX_RADIUS 8
+fp4q_status fp4_quantize_search(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t fmt,
+                                int32_t block, int32_t gmode, float* g, int32_t rotate,
+                                int32_t radius, uint8_t* codes, uint8_t* scales, float* block_mse,
+                                int32_t mse_kind, fp4q_stats* stats, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
  * Dequantization of stored codes and scales ("Diagnosing FP4 inference",
  * section 2: weights are dequantized for the compute).  x_hat = v * 2^E (MXFP4,
  * exact) or RN32(v * d) with d = RN32(s_hat * g); with rotate the block

@@ -33,8 +33,8 @@ G_NONE, G_DYNAMIC, G_GIVEN = 0, 1, 2
 MSE_ABS, MSE_REL = 0, 1
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
 
-EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "fp4_dequantize", "fp4_block_mse",
-           "hadamard_block_rotate", "fp4q_workspace_bytes", "fp4q_last_error",
+EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "fp4_quantize_search", "fp4_dequantize",
+           "fp4_block_mse", "hadamard_block_rotate", "fp4q_workspace_bytes", "fp4q_last_error",
            "fp4q_abi_version")
 
 
@@ -64,6 +64,8 @@ def _bind(l):
     l.mxfp4_quantize.argtypes = [P, i32, i64, i64, i32, P, P, P, i32, P, P, sz, P]
     l.nvfp4_quantize.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, P, P, P, i32, P, P, sz, P]
     l.fp4_dequantize.argtypes = [P, P, i32, i32, P, i64, i64, i32, P, i32, P]
+    l.fp4_quantize_search.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, i32, P, P, P, i32,
+                                      P, P, sz, P]
     l.fp4_block_mse.argtypes = [P, i32, P, P, i32, i32, P, i64, i64, i32, P, i32, P, P, sz, P]
     l.hadamard_block_rotate.argtypes = [P, i32, i64, i64, i32, P, P]
     for name in ("mxfp4_quantize", "nvfp4_quantize", "fp4_dequantize", "fp4_block_mse",
@@ -202,6 +204,27 @@ def nvfp4_quantize(x: torch.Tensor, block: int = 16, scale_fmt: int = FMT_UE4M3,
                                 scale_fmt, gmode, _ptr(g), rotate, _ptr(codes), _ptr(scales),
                                 _ptr(block_mse), mse_kind, _ptr(stats), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(x.device)))
+    return Quantized(codes, scales, block_mse, stats, g)
+
+
+def fp4_quantize_search(x: torch.Tensor, fmt: int = FMT_UE4M3, block: int = 16,
+                        gmode: int = G_DYNAMIC, g: Optional[torch.Tensor] = None, rotate: int = 0,
+                        radius: int = 1, *, codes=None, scales=None, block_mse=True,
+                        mse_kind: int = MSE_ABS, stats=True,
+                        ws: Optional[torch.Tensor] = None) -> Quantized:
+    """Block quantize with the per-block scale search (the max-based scale code and
+    its neighbours within ``radius``, lowest block SSE) + pack + error split.
+    ``fmt`` is FMT_MXFP4 (block 32, gmode G_NONE), FMT_UE4M3 or FMT_UE5M3."""
+    x = _matrix(x)
+    codes, scales, block_mse, stats = _outputs(x, block, codes, scales, block_mse, stats)
+    if gmode != G_NONE and g is None:
+        g = torch.empty(1, dtype=torch.float32, device=x.device)
+    need_ws = stats is not None or gmode == G_DYNAMIC
+    ws = ws if ws is not None else (workspace(x.device) if need_ws else None)
+    _check(lib().fp4_quantize_search(_ptr(x), _dtype_code(x), x.shape[0], x.shape[1], fmt, block,
+                                     gmode, _ptr(g), rotate, radius, _ptr(codes), _ptr(scales),
+                                     _ptr(block_mse), mse_kind, _ptr(stats), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(x.device)))
     return Quantized(codes, scales, block_mse, stats, g)
 
 

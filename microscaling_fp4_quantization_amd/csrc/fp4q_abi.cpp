@@ -77,7 +77,8 @@ fp4q_status launched(int rc, const char* msg) {
 fp4q_status quantize_common(const char* fn, const void* x, int32_t xt, int64_t rows, int64_t cols,
                             int32_t block, int32_t fmt, int32_t gmode, float* g, int32_t rotate,
                             uint8_t* codes, uint8_t* scales, float* block_mse, int32_t mse_kind,
-                            fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+                            fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream,
+                            int32_t radius = -1) {
     TRY(check_dtype(fn, xt));
     TRY(check_shape(fn, rows, cols, block, rotate));
     TRY(check_mse(fn, block_mse, mse_kind));
@@ -111,6 +112,7 @@ fp4q_status quantize_common(const char* fn, const void* x, int32_t xt, int64_t r
     j.stats = stats;
     j.ws = ws;
     j.stream = stream;
+    j.radius = radius;
     char msg[256] = {0};
     return launched(fp4q::launch_quantize(j, msg, sizeof msg), msg);
 }
@@ -142,6 +144,21 @@ fp4q_status nvfp4_quantize(const void* x, int32_t xt, int64_t rows, int64_t cols
         return fail(FP4Q_ERR_ARG, "nvfp4_quantize: scale_fmt %d is not UE4M3 (1) or UE5M3 (2)", scale_fmt);
     return quantize_common("nvfp4_quantize", x, xt, rows, cols, block, scale_fmt, gmode, g, rotate,
                            codes, scales, block_mse, mse_kind, stats, ws, ws_bytes, stream);
+}
+
+fp4q_status fp4_quantize_search(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t fmt,
+                                int32_t block, int32_t gmode, float* g, int32_t rotate,
+                                int32_t radius, uint8_t* codes, uint8_t* scales, float* block_mse,
+                                int32_t mse_kind, fp4q_stats* stats, void* ws, size_t ws_bytes,
+                                void* stream) {
+    const char* fn = "fp4_quantize_search";
+    TRY(check_fmt_block(fn, fmt, block));
+    if (fmt == FP4Q_FMT_MXFP4 && gmode != FP4Q_G_NONE)
+        return fail(FP4Q_ERR_ARG, "%s: MXFP4 takes no per-tensor scale (gmode must be NONE)", fn);
+    if (radius < 0 || radius > FP4Q_SEARCH_MAX_RADIUS)
+        return fail(FP4Q_ERR_ARG, "%s: radius %d is not in [0, %d]", fn, radius, FP4Q_SEARCH_MAX_RADIUS);
+    return quantize_common(fn, x, xt, rows, cols, block, fmt, gmode, g, rotate, codes, scales,
+                           block_mse, mse_kind, stats, ws, ws_bytes, stream, radius);
 }
 
 fp4q_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales, int32_t fmt, int32_t block,

@@ -609,6 +609,8 @@ struct QParams {
     float* block_mse;
     int mse_kind;
     int fmt;            // UE kernels: 1 UE4M3, 2 UE5M3
+    int radius;         // scale search: neighbours of the max-based code tried
+    int max_byte;       // scale search: largest valid scale code
     const float* g_in;  // per-tensor scale (device), NULL for g = 1
     // Dynamic mode: per-workgroup |x| maxima of the amax pass; every workgroup
     // reduces them to g, and workgroup 0 also writes g to g_out.
@@ -743,6 +745,108 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
     }
 }
 
+// Scale search on one chunk.  Candidates are the max-based scale code c0 (the
+// code quantize_chunk takes) and its neighbours c0 + j, 0 < |j| <= radius,
+// inside [0, max_byte]; consecutive codes are consecutive scale values in all
+// three formats.  Each is scored by the block's SSE in binary64, with every
+// element coded and dequantized as quantize_chunk does under that code and
+// its error formed in binary64 (x - x_hat of two binary32 values is then
+// exact, so the scores match a sequential sum to rounding far below the
+// margin).  Candidates are visited as j = 0, -1, +1, -2, +2, ... and one
+// replaces the best so far only when its SSE is below best - best * 2^-40, so
+// near-ties keep the code closest to c0.  Outputs are quantize_chunk's, for
+// the chosen code.
+template <int XT, int FMT, int B, int ROT, bool SUMSQ>
+__device__ __forceinline__ void search_chunk(const Raw<XT>& raw, int u, const QOut& o,
+                                             const QParams& p, const UeCtx& ue, int lane,
+                                             int gl, Acc& acc) {
+    constexpr int L = B / kLaneElems;
+    constexpr int kBlocks = kChunk / B;
+    float v[8];
+    unpack<XT>(raw, v);
+    if constexpr (ROT != 0) rotate8<ROT>(v, gl);
+    const float mf = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
+                           fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
+    const uint32_t mbits = group_max<L>(__float_as_uint(mf));
+    const float m = __uint_as_float(mbits);
+    int c0;
+    if constexpr (FMT == kFmtMx) {
+        const uint32_t F = mbits >> 23;
+        c0 = F > 2u ? (int)F - 2 : 0;
+    } else {
+        c0 = (int)ue_scale<FMT>(m, ue.D, ue.rD, ue.s_fast_max, ue.tab).byte;
+    }
+    double best = 0.0;
+    int best_byte = c0;
+    uint32_t best_cw = 0;
+    float best_xm = 0.0f;
+    for (int t = 0; t <= 2 * p.radius; ++t) {  // the same trip count on every lane
+        const int j = t == 0 ? 0 : ((t & 1) ? -((t + 1) >> 1) : (t >> 1));
+        const bool valid = c0 + j >= 0 && c0 + j <= p.max_byte;
+        const int cb = valid ? c0 + j : c0;  // an in-range code; its result is not taken
+        uint32_t cw;
+        float xh[8], xm;
+        if constexpr (FMT == kFmtMx) {
+            const float sc = __uint_as_float((uint32_t)cb << 23);
+            cw = code_word_f32(v, sc);
+            decode_word(cw, sc, xh);
+            xm = requant_mx(m, sc);
+        } else {
+            const float4 e = ue.tab[cb];
+            UeScale s;
+            s.byte = (uint32_t)cb;
+            s.d = e.x;
+            s.r = e.y;
+            s.fast = m <= e.z;
+            s.six = e.w != 0.0f;
+            float y[8];
+            if (s.fast) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = div_rn(v[i], s.d, s.r);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = v[i] / s.d;
+            }
+            cw = code_word_f32(y, 1.0f);
+            decode_word(cw, 1.0f, xh);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xh[i] = xh[i] * s.d;
+            xm = requant_ue(m, s);
+        }
+        double sse = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double e = (double)v[i] - (double)xh[i];
+            sse = fma(e, e, sse);
+        }
+        sse = group_sum<L>(sse);
+        if (valid && (t == 0 || sse < best - best * 0x1p-40)) {
+            best = sse;
+            best_byte = cb;
+            best_cw = cw;
+            best_xm = xm;
+        }
+    }
+    double ss = 0.0;
+    if constexpr (SUMSQ) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fma((double)v[i], (double)v[i], ss);
+        ss = group_sum<L>(ss);
+    }
+    const int blk = u * kBlocks + lane / L;
+    __builtin_amdgcn_raw_buffer_store_b32(best_cw, o.codes, (u * kChunk + lane * kLaneElems) / 2, 0, kStNt);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)best_byte, o.scales, gl == 0 ? blk : kDropped, 0, kStNt);
+    if (p.block_mse) {
+        float mse;
+        if (SUMSQ && p.mse_kind == kMseRel) mse = ss > 0.0 ? (float)(best / ss) : 0.0f;
+        else mse = (float)(best * (1.0 / B));
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mse), o.mse,
+                                              gl == 0 ? blk * 4 : kDropped, 0, kStNt);
+    }
+    const double em = (double)(m - best_xm);
+    add_block(acc, (m > 0.0f) && (best_xm == 0.0f), best, em * em, ss);
+}
+
 // g = RN32(amax / 2688) (1 when that is not positive) from the amax pass's
 // per-workgroup maxima; every workgroup reduces the same values in the same
 // way, so all agree bit for bit.
@@ -762,7 +866,7 @@ __device__ float dynamic_g(const uint32_t* part, int n_part) {
 #ifndef FP4Q_QUANT_WPE
 #define FP4Q_QUANT_WPE 0
 #endif
-template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ>
+template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ, bool SEARCH = false>
 __global__ __launch_bounds__(kThreads)
 #if FP4Q_QUANT_WPE
 __attribute__((amdgpu_waves_per_eu(FP4Q_QUANT_WPE)))
@@ -803,8 +907,12 @@ void k_quantize(QParams p) {
 #endif
 #pragma unroll
         for (int u = 0; u < kQuantUnroll; ++u)
-            if (u < left)
-                quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ>(cur[u], u, o, p, ue, lane, gl, acc);
+            if (u < left) {
+                if constexpr (SEARCH)
+                    search_chunk<XT, FMT, B, ROT, SUMSQ>(cur[u], u, o, p, ue, lane, gl, acc);
+                else
+                    quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ>(cur[u], u, o, p, ue, lane, gl, acc);
+            }
 #if FP4Q_PREFETCH
 #pragma unroll
         for (int u = 0; u < kQuantUnroll; ++u) cur[u] = nxt[u];
@@ -1221,26 +1329,29 @@ int launch_finalize(const StatsOut& so, int G, hipStream_t st, char* msg, size_t
 typedef void (*QuantKernel)(QParams);
 
 template <int XT, int FMT, int B, int ROT>
-QuantKernel pick_quant(bool err, bool sumsq) {
+QuantKernel pick_quant(bool err, bool sumsq, bool search) {
+    if (search) return sumsq ? k_quantize<XT, FMT, B, ROT, true, true, true>
+                             : k_quantize<XT, FMT, B, ROT, true, false, true>;
     if (!err) return k_quantize<XT, FMT, B, ROT, false, false>;
     if (!sumsq) return k_quantize<XT, FMT, B, ROT, true, false>;
     return k_quantize<XT, FMT, B, ROT, true, true>;
 }
 
 template <int XT, int FMT>
-QuantKernel pick_quant_block(int block, int rotate, bool err, bool sumsq) {
+QuantKernel pick_quant_block(int block, int rotate, bool err, bool sumsq, bool search) {
     if constexpr (FMT == kFmtMx) {
-        return rotate ? pick_quant<XT, FMT, 32, 32>(err, sumsq) : pick_quant<XT, FMT, 32, 0>(err, sumsq);
+        return rotate ? pick_quant<XT, FMT, 32, 32>(err, sumsq, search)
+                      : pick_quant<XT, FMT, 32, 0>(err, sumsq, search);
     } else {
         switch (block) {
-            case 8: return pick_quant<XT, FMT, 8, 0>(err, sumsq);
-            case 16: return rotate ? pick_quant<XT, FMT, 16, 16>(err, sumsq)
-                                   : pick_quant<XT, FMT, 16, 0>(err, sumsq);
-            case 32: return rotate ? pick_quant<XT, FMT, 32, 32>(err, sumsq)
-                                   : pick_quant<XT, FMT, 32, 0>(err, sumsq);
-            case 64: return pick_quant<XT, FMT, 64, 0>(err, sumsq);
-            case 128: return pick_quant<XT, FMT, 128, 0>(err, sumsq);
-            default: return pick_quant<XT, FMT, 256, 0>(err, sumsq);
+            case 8: return pick_quant<XT, FMT, 8, 0>(err, sumsq, search);
+            case 16: return rotate ? pick_quant<XT, FMT, 16, 16>(err, sumsq, search)
+                                   : pick_quant<XT, FMT, 16, 0>(err, sumsq, search);
+            case 32: return rotate ? pick_quant<XT, FMT, 32, 32>(err, sumsq, search)
+                                   : pick_quant<XT, FMT, 32, 0>(err, sumsq, search);
+            case 64: return pick_quant<XT, FMT, 64, 0>(err, sumsq, search);
+            case 128: return pick_quant<XT, FMT, 128, 0>(err, sumsq, search);
+            default: return pick_quant<XT, FMT, 256, 0>(err, sumsq, search);
         }
     }
 }
@@ -1341,16 +1452,19 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     // quantize kernel skips it.
     const bool sumsq_in_amax = dynamic && j.stats != nullptr && !rel;
     const bool sumsq = (j.stats != nullptr || rel) && !sumsq_in_amax;
+    const bool search = j.radius >= 0;
+    p.radius = search ? j.radius : 0;
+    p.max_byte = j.fmt == kFmtMx ? 254 : (j.fmt == kFmtUe4m3 ? 0x7E : 0xF7);
     QuantKernel k;
     if (j.fmt == kFmtMx)
-        k = j.xt == 0 ? pick_quant_block<0, kFmtMx>(32, j.rotate, err, sumsq)
-                      : pick_quant_block<1, kFmtMx>(32, j.rotate, err, sumsq);
+        k = j.xt == 0 ? pick_quant_block<0, kFmtMx>(32, j.rotate, err, sumsq, search)
+                      : pick_quant_block<1, kFmtMx>(32, j.rotate, err, sumsq, search);
     else
         k = j.fmt == kFmtUe4m3
-                ? (j.xt == 0 ? pick_quant_block<0, kFmtUe4m3>(j.block, j.rotate, err, sumsq)
-                             : pick_quant_block<1, kFmtUe4m3>(j.block, j.rotate, err, sumsq))
-                : (j.xt == 0 ? pick_quant_block<0, kFmtUe5m3>(j.block, j.rotate, err, sumsq)
-                             : pick_quant_block<1, kFmtUe5m3>(j.block, j.rotate, err, sumsq));
+                ? (j.xt == 0 ? pick_quant_block<0, kFmtUe4m3>(j.block, j.rotate, err, sumsq, search)
+                             : pick_quant_block<1, kFmtUe4m3>(j.block, j.rotate, err, sumsq, search))
+                : (j.xt == 0 ? pick_quant_block<0, kFmtUe5m3>(j.block, j.rotate, err, sumsq, search)
+                             : pick_quant_block<1, kFmtUe5m3>(j.block, j.rotate, err, sumsq, search));
     const Split sq = split_for(chunks, reinterpret_cast<const void*>(k), kQuantCpw);
     const int G = sq.G;
     p.cpw = sq.cpw;

@@ -35,6 +35,7 @@ struct QuantJob {
     void* stats;       // nullable, fp4q_stats layout
     void* ws;
     void* stream;
+    int radius = -1;   // >= 0: per-block scale search over this many neighbours
 };
 
 struct DequantJob {

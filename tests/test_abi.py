@@ -93,6 +93,25 @@ def test_nvfp4_validation(L):
     assert nv(L, gmode=2, g=A16 + 2) == ALIGN
 
 
+def srch(L, x=A16, xt=0, rows=4, cols=64, fmt=1, block=16, gmode=0, g=None, rot=0, radius=1,
+         codes=A16b, scales=A16c, bm=None, kind=0, stats=None, ws=None, wsb=0):
+    return L.fp4_quantize_search(x, xt, rows, cols, fmt, block, gmode, g, rot, radius, codes,
+                                 scales, bm, kind, stats, ws, wsb, None)
+
+
+def test_search_validation(L):
+    assert srch(L, radius=-1) == ARG and "radius" in err(L)
+    assert srch(L, radius=9) == ARG and "radius" in err(L)
+    assert srch(L, fmt=0, block=16) == SHAPE
+    assert srch(L, fmt=0, block=32, gmode=2, g=A16) == ARG and "MXFP4" in err(L)
+    assert srch(L, fmt=2, gmode=1, g=A16, ws=A16b, wsb=WSB) == ARG and "UE5M3" in err(L)
+    assert srch(L, fmt=5) == ARG
+    assert srch(L, x=None) == ARG
+    assert srch(L, stats=A16) == WS
+    assert srch(L, gmode=1, g=A16) == WS
+    assert srch(L, rows=0, radius=3) == OK
+
+
 def test_other_entry_points_validation(L):
     deq = L.fp4_dequantize
     assert deq(A16, A16b, 0, 16, None, 4, 64, 0, A16c, 1, None) == SHAPE  # MXFP4 needs block 32
