@@ -26,7 +26,7 @@ _SRC = os.path.join(_HERE, "fp4_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 FMT_MXFP4, FMT_UE4M3, FMT_UE5M3 = 0, 1, 2
-GMODE_NONE, GMODE_DYNAMIC, GMODE_GIVEN = 0, 1, 2
+GMODE_NONE, GMODE_DYNAMIC, GMODE_GIVEN, GMODE_ROW = 0, 1, 2, 3
 MSE_ABS, MSE_REL = 0, 1
 
 # gcc flags: no contraction of a*b+c into fma and no fast-math, so every
@@ -175,7 +175,8 @@ def quantize(x, fmt: int, block: int, gmode: int = GMODE_NONE, g: float | None =
     Returns a dict with ``codes`` (rows x cols/2 uint8), ``scales``
     (rows x cols/block uint8), ``block_mse`` (float32), ``terms`` (float64
     [non-max, max, zero-rounding, sum x^2]), ``counts`` (int64 [blocks,
-    zero-rounded blocks]) and ``g`` (the per-tensor scale used).
+    zero-rounded blocks]) and ``g`` (the per-tensor scale used; with
+    GMODE_ROW a float32 array of one scale per row).
     """
     a = _f32_2d(x)
     rows, cols = a.shape
@@ -186,14 +187,17 @@ def quantize(x, fmt: int, block: int, gmode: int = GMODE_NONE, g: float | None =
     mse = np.zeros((rows, cols // block), np.float32)
     acc = np.zeros(4, np.float64)
     cnt = np.zeros(2, np.int64)
-    gbuf = np.array([1.0 if g is None else g], np.float32)
+    if gmode == GMODE_ROW:
+        gbuf = np.zeros(max(rows, 1), np.float32)
+    else:
+        gbuf = np.array([1.0 if g is None else g], np.float32)
     rc = load().oracle_quantize(_ptr(a), rows, cols, fmt, block, gmode, _ptr(gbuf), rotate,
                                 _ptr(codes), _ptr(scales), _ptr(mse), mse_kind, _ptr(acc),
                                 _ptr(cnt))
     if rc:
         raise OracleError("quantize: bad arguments")
     return {"codes": codes, "scales": scales, "block_mse": mse, "terms": acc, "counts": cnt,
-            "g": float(gbuf[0])}
+            "g": gbuf[:rows].copy() if gmode == GMODE_ROW else float(gbuf[0])}
 
 
 def quantize_search(x, fmt: int, block: int, gmode: int = GMODE_NONE, g: float | None = None,

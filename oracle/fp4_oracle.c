@@ -52,6 +52,9 @@
  *   R8  Scale search: the max-based code and its neighbours within a radius,
  *       scored by block SSE, visited nearest first, replaced only when better
  *       by more than a relative 2^-40 (see oracle_quantize_search).
+ *   R9  Per-row dynamic scale (activations, one row per token): g_r =
+ *       RN32(amax_r / 2688) from the row's own (rotated) maximum, 1 when that
+ *       is 0; the row is then quantized exactly as under a given g = g_r.
  */
 #include <math.h>
 #include <stddef.h>
@@ -70,6 +73,7 @@
 #define GMODE_NONE 0
 #define GMODE_DYNAMIC 1
 #define GMODE_GIVEN 2
+#define GMODE_ROW 3
 
 #define MSE_ABS 0
 #define MSE_REL 1
@@ -408,6 +412,26 @@ int oracle_quantize(const float* x, int64_t rows, int64_t cols, int fmt, int blo
 {
     if (!valid_shape(fmt, block, rows, cols, rotate)) return ORACLE_BAD_ARG;
     if (fmt != FMT_UE4M3 && gmode != GMODE_NONE) return ORACLE_BAD_ARG;
+    if (gmode == GMODE_ROW) {
+        /* R9: every row under its own dynamic scale, written to g[row]. */
+        if (!g) return ORACLE_BAD_ARG;
+        if (acc) memset(acc, 0, 4 * sizeof(double));
+        if (cnt) memset(cnt, 0, 2 * sizeof(int64_t));
+        int64_t nblk_row = cols / block;
+        for (int64_t r = 0; r < rows; ++r) {
+            double racc[4];
+            int64_t rcnt[2];
+            g[r] = oracle_dynamic_g(oracle_tensor_amax(x + r * cols, 1, cols, rotate));
+            int rc = oracle_quantize(x + r * cols, 1, cols, fmt, block, GMODE_GIVEN, g + r, rotate,
+                                     codes + r * cols / 2, scales + r * nblk_row,
+                                     block_mse ? block_mse + r * nblk_row : NULL, mse_kind,
+                                     racc, rcnt);
+            if (rc) return rc;
+            if (acc) for (int k = 0; k < 4; ++k) acc[k] += racc[k];
+            if (cnt) for (int k = 0; k < 2; ++k) cnt[k] += rcnt[k];
+        }
+        return ORACLE_OK;
+    }
     float gv = 1.0f;
     if (fmt == FMT_UE4M3) {
         if (gmode == GMODE_DYNAMIC) {
