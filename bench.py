@@ -28,6 +28,9 @@ Workloads (--workload):
                scale at block sizes 256, 128, 64, 32, 16 and 8, MSE and split
   qwen14rot    bf16 13824 x 5120 Student-t(4) with 1 % outlier columns x20:
                MXFP4 and dynamic NVFP4, each without and with block rotation
+  act5120      activation matrices of 1, 16, 128, 2048 and 8192 tokens x 5120:
+               NVFP4 + rotation with per-token scales, NVFP4 with the per-tensor
+               dynamic scale, MXFP4 + rotation; time per call for each
   qwen7search  the six default tensors, MXFP4 and dynamic NVFP4 with the per-block
                scale search (radius 1)
   qwen14model  a random-init Qwen2.5-14B-shaped stack (48 layers x 7 projections,
@@ -91,7 +94,7 @@ class Spec:
             s = "MXFP4 b32"
         else:
             s = f"{'UE4M3' if self.scale_fmt == 1 else 'UE5M3'} b{self.block}"
-            s += {0: "", 1: " dynamic g", 2: " given g"}[self.gmode]
+            s += {0: "", 1: " dynamic g", 2: " given g", 3: " per-row g"}[self.gmode]
         if self.rotate:
             s += f" rot{self.rotate}"
         if self.radius is not None:
@@ -101,11 +104,13 @@ class Spec:
 
 class Workload:
     """`sample` = (description, tensors, repeats, spec index) of the oracle's
-    bounded CPU sample."""
+    bounded CPU sample.  `per_call` asks for a time per (tensor, spec) pair in
+    the breakdown (latency-bound workloads)."""
 
-    def __init__(self, name, config, make_tensors, specs, steps, warmup, sample):
+    def __init__(self, name, config, make_tensors, specs, steps, warmup, sample, per_call=False):
         self.name, self.config, self.make_tensors = name, config, make_tensors
         self.specs, self.steps, self.warmup, self.sample = specs, steps, warmup, sample
+        self.per_call = per_call
 
 
 def _qwen7_tensors():
@@ -127,6 +132,11 @@ def _llama8_tensors():
 def _qwen14rot_tensors():
     import fp4_workloads as wl
     return [wl.qwen14_outliers()]
+
+
+def _act5120_tensors():
+    import fp4_workloads as wl
+    return [wl.activations_5120(m) for m in wl.ACT_TOKENS]
 
 
 def _qwen14model_tensors():
@@ -179,6 +189,18 @@ WORKLOADS = {
         _qwen7_tensors,
         [Spec("mx32_search1", "mx", 32, radius=1), Spec("nv16_dyn_search1", "nv", 16, 1, 1, radius=1)],
         20, 2, ("1 of the 6 tensors (18944x3584, sigma 0.01), whole", 1, 1, 1)),
+    "act5120": Workload(
+        "activations-5120-token-shapes",
+        {"tensors": "5 bf16 activation matrices M x 5120, M = 1, 16, 128, 2048, 8192",
+         "format": "NVFP4 b16 + rotation 16 with one dynamic scale per token, NVFP4 b16 with "
+                   "the per-tensor dynamic scale, MXFP4 b32 + rotation 32",
+         "outputs": "codes + scales (the inference use: no MSE)"},
+        _act5120_tensors,
+        [Spec("nv16_rot_rowg", "nv", 16, 1, 3, rotate=16, block_mse=False, stats=False),
+         Spec("nv16_tensor_g", "nv", 16, 1, 1, block_mse=False, stats=False),
+         Spec("mx32_rot", "mx", 32, rotate=32, block_mse=False, stats=False)],
+        50, 5, ("all five matrices, whole, 8 times", 5, 8, 0),
+        per_call=True),
     "qwen14model": Workload(
         "qwen2.5-14b-shaped-model-sweep",
         {"tensors": "336 bf16 (48 layers x q,k,v,o,gate,up,down), N(0, 0.02), 13.2e9 params",
@@ -225,7 +247,7 @@ class Runner:
                         block_mse=torch.empty((r, c // s.block), dtype=torch.float32, device=dev))
                 o = dict(shared[key])
                 o["stats"] = fq.new_stats(dev)
-                o["g"] = torch.ones(1, dtype=torch.float32, device=dev)
+                o["g"] = torch.ones(r if s.gmode == 3 else 1, dtype=torch.float32, device=dev)
                 o["stream"] = key[3]
                 self.out[(ti, si)] = o
 
@@ -294,6 +316,30 @@ def search_gain(fq, torch, run, si):
             "sse_ratio": round(tot[s.radius] / tot[0], 6)}
 
 
+def time_graph(torch, fn, calls=20, replays=10):
+    """us per call of fn, captured `calls` times into one HIP graph and replayed:
+    the GPU time per call without the host's launch overhead."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (calls * replays)
+
+
 def time_region(torch, stream, fn, reps):
     """ms per rep of fn, bracketed by HIP events on `stream`."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -313,7 +359,8 @@ def cpu_baseline(w, xs_host_sample):
     desc, n_tensors, repeat, spec_idx = w.sample
     s = w.specs[spec_idx]
     fmt = oracle.FMT_MXFP4 if s.fmt == "mx" else s.scale_fmt
-    gmode = {0: oracle.GMODE_NONE, 1: oracle.GMODE_DYNAMIC, 2: oracle.GMODE_GIVEN}[s.gmode]
+    gmode = {0: oracle.GMODE_NONE, 1: oracle.GMODE_DYNAMIC, 2: oracle.GMODE_GIVEN,
+             3: oracle.GMODE_ROW}[s.gmode]
     n, el, in_bytes = 0, 0.0, 2
     for x in xs_host_sample[:n_tensors]:
         xf = x.float().numpy() if hasattr(x, "float") else np.asarray(x, np.float32)
@@ -405,7 +452,20 @@ def main():
 
     # Per-spec breakdown: one timed pass of each call type over all tensors.
     breakdown = {}
-    if len(w.specs) > 1:
+    if w.per_call:
+        # Latency-bound calls: timed from a captured HIP graph (GPU time per call),
+        # and back to back from Python (host launch cost included).
+        for ti, x in enumerate(xs):
+            for si, s in enumerate(w.specs):
+                fn = lambda ti=ti, si=si: run.call(ti, si)
+                us = time_graph(torch, fn)
+                us_eager = time_region(torch, stream, fn, 200) * 1e3
+                breakdown[f"{s.tag}_M{x.shape[0]}"] = {
+                    "us_per_call_graph": round(us, 2),
+                    "us_per_call_eager": round(us_eager, 2),
+                    "algorithmic_GBps": round(s.algorithmic_bytes(x.numel(), in_bytes)
+                                              / (us * 1e-6) / 1e9, 1)}
+    elif len(w.specs) > 1:
         for si, s in enumerate(w.specs):
             fn = lambda si=si: [run.call(ti, si) for ti in range(len(xs))]
             ms = time_region(torch, stream, fn, max(1, min(steps, 10)))

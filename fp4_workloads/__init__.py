@@ -18,6 +18,10 @@ Workloads (shapes from the layers the pages study; values synthetic):
   with 4 degrees of freedom scaled to standard deviation 0.02 (the t(4)
   variance is 2), with 51 of the 5120 input columns (1 %, chosen by the seeded
   generator) multiplied by 20.  Seed [4].
+* ``activations_5120``: bf16 activation matrices of M tokens x 5120 (the
+  Qwen2.5-14B hidden size) for M in {1, 16, 128, 2048, 8192}: Student-t(4)
+  times 0.5, each token scaled by 2^k with k uniform in [-8, 8), and 1 % of the
+  channels (chosen by the generator) x16.  Seed [6, M].
 * ``qwen14_model``: a random-init Qwen2.5-14B-shaped layer stack, 48 layers x
   {q 5120x5120, k 1024x5120, v 1024x5120, o 5120x5120, gate 13824x5120,
   up 13824x5120, down 5120x13824}, bf16 N(0, 0.02), seed [5, layer, proj].
@@ -102,6 +106,24 @@ def qwen14_outliers(shape=None):
 def qwen14_layer_tensor(layer: int, proj_idx: int, shape=None):
     shp = QWEN14_PROJ[proj_idx][1] if shape is None else shape
     return to_bf16(normal_f32(shp, 0.02, [5, layer, proj_idx]))
+
+
+ACT_TOKENS = (1, 16, 128, 2048, 8192)
+ACT_HIDDEN = 5120
+
+
+def activations_f32(rows: int, cols: int, seed) -> np.ndarray:
+    """Student-t(4) x 0.5 with a per-token power-of-two magnitude and 1 % outlier
+    channels x16."""
+    rng = np.random.default_rng(seed)
+    a = (rng.standard_t(4, (rows, cols)) * 0.5).astype(np.float32)
+    a *= (2.0 ** rng.integers(-8, 8, (rows, 1))).astype(np.float32)
+    a[:, rng.choice(cols, max(1, cols // 100), replace=False)] *= np.float32(16.0)
+    return a
+
+
+def activations_5120(tokens: int):
+    return to_bf16(activations_f32(tokens, ACT_HIDDEN, [6, tokens]))
 
 
 def qwen14_param_count() -> int:

@@ -62,7 +62,8 @@
  *     launched: on an error nothing is launched or written, and fp4q_last_error()
  *     (thread-local) holds a description.  No C++ exception crosses the ABI.
  *   - rows * cols == 0 is valid: codes/scales/block_mse are untouched, *stats
- *     is set to zeros and, in the dynamic mode, *g to 1.
+ *     is set to zeros and, in the dynamic mode, *g to 1 (with FP4Q_G_ROW,
+ *     g[0..rows) to 1).
  *   - NaN and infinite inputs are outside the contract: codes are unspecified
  *     for them; nothing faults.  With rotation, inputs must also keep the
  *     binary32 butterfly finite, which |x| < 2^100 guarantees.
@@ -105,7 +106,12 @@ typedef enum {
 typedef enum {
     FP4Q_G_NONE = 0,    /* g = 1 */
     FP4Q_G_DYNAMIC = 1, /* g = RN32(amax / 2688), written to *g (device) */
-    FP4Q_G_GIVEN = 2    /* g read from *g (device); must be positive and finite */
+    FP4Q_G_GIVEN = 2,   /* g read from *g (device); must be positive and finite */
+    FP4Q_G_ROW = 3      /* one dynamic scale per row (per token of an activation
+                           matrix): g_r = RN32(amax_r / 2688) over row r (rotated
+                           when rotating), 1 when 0, written to g[0..rows);
+                           UE4M3 only.  One kernel launch; no workspace unless
+                           stats are wanted. */
 } fp4q_gmode;
 
 typedef enum { FP4Q_MSE_ABS = 0, FP4Q_MSE_REL = 1 } fp4q_mse_kind;
@@ -142,7 +148,9 @@ fp4q_status mxfp4_quantize(const void* x, int32_t xt, int64_t rows, int64_t cols
  *   block      8, 16, 32, 64, 128 or 256; cols must be a multiple of it
  *   scale_fmt  FP4Q_FMT_UE4M3 or FP4Q_FMT_UE5M3 (UE5M3 requires gmode NONE)
  *   gmode      fp4q_gmode; g is a device pointer to one float, written in the
- *              dynamic mode and read in the given mode (may be NULL for NONE)
+ *              dynamic mode and read in the given mode (may be NULL for NONE);
+ *              with FP4Q_G_ROW it points to rows floats, all written (may be
+ *              NULL when rows is 0)
  *   rotate     0, or equal to block when block is 16 or 32
  *   ws         needed when stats != NULL or gmode == DYNAMIC
  * Other arguments as for mxfp4_quantize; scales are rows x cols/block bytes.

@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(HERE, "libfp4q.so")
 
 BF16, F32 = 0, 1
 FMT_MXFP4, FMT_UE4M3, FMT_UE5M3 = 0, 1, 2
-G_NONE, G_DYNAMIC, G_GIVEN = 0, 1, 2
+G_NONE, G_DYNAMIC, G_GIVEN, G_ROW = 0, 1, 2, 3
 MSE_ABS, MSE_REL = 0, 1
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
 
@@ -192,12 +192,13 @@ def nvfp4_quantize(x: torch.Tensor, block: int = 16, scale_fmt: int = FMT_UE4M3,
     """UE4M3/UE5M3 block quantize (NVFP4 at block 16) + pack + dequantize + error split.
 
     ``g``: one-element float32 device tensor; written in the dynamic mode (allocated
-    when not given), read in the given mode.
+    when not given), read in the given mode.  With ``G_ROW`` it holds one scale per
+    row (allocated with ``rows`` elements when not given) and is written.
     """
     x = _matrix(x)
     codes, scales, block_mse, stats = _outputs(x, block, codes, scales, block_mse, stats)
     if gmode != G_NONE and g is None:
-        g = torch.empty(1, dtype=torch.float32, device=x.device)
+        g = torch.empty(x.shape[0] if gmode == G_ROW else 1, dtype=torch.float32, device=x.device)
     need_ws = stats is not None or gmode == G_DYNAMIC
     ws = ws if ws is not None else (workspace(x.device) if need_ws else None)
     _check(lib().nvfp4_quantize(_ptr(x), _dtype_code(x), x.shape[0], x.shape[1], block,

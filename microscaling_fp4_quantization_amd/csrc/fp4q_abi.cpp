@@ -82,11 +82,14 @@ fp4q_status quantize_common(const char* fn, const void* x, int32_t xt, int64_t r
     TRY(check_dtype(fn, xt));
     TRY(check_shape(fn, rows, cols, block, rotate));
     TRY(check_mse(fn, block_mse, mse_kind));
-    if (gmode != FP4Q_G_NONE && gmode != FP4Q_G_DYNAMIC && gmode != FP4Q_G_GIVEN)
-        return fail(FP4Q_ERR_ARG, "%s: gmode %d is not NONE (0), DYNAMIC (1) or GIVEN (2)", fn, gmode);
+    if (gmode != FP4Q_G_NONE && gmode != FP4Q_G_DYNAMIC && gmode != FP4Q_G_GIVEN && gmode != FP4Q_G_ROW)
+        return fail(FP4Q_ERR_ARG, "%s: gmode %d is not NONE (0), DYNAMIC (1), GIVEN (2) or ROW (3)", fn, gmode);
     if (fmt == FP4Q_FMT_UE5M3 && gmode != FP4Q_G_NONE)
         return fail(FP4Q_ERR_ARG, "%s: UE5M3 scales take no per-tensor scale (gmode must be NONE)", fn);
-    if (gmode != FP4Q_G_NONE && !g) return fail(FP4Q_ERR_ARG, "%s: gmode %d needs a g pointer", fn, gmode);
+    if (gmode == FP4Q_G_ROW && radius >= 0)
+        return fail(FP4Q_ERR_ARG, "%s: the scale search does not take per-row scales", fn);
+    if (gmode != FP4Q_G_NONE && !g && !(gmode == FP4Q_G_ROW && rows == 0))
+        return fail(FP4Q_ERR_ARG, "%s: gmode %d needs a g pointer", fn, gmode);
     if (g && !aligned(g, 4)) return fail(FP4Q_ERR_ALIGN, "%s: g is not 4-byte aligned", fn);
     const int64_t n = rows * cols;
     if (n > 0) {
@@ -100,6 +103,8 @@ fp4q_status quantize_common(const char* fn, const void* x, int32_t xt, int64_t r
     j.x = x;
     j.xt = xt;
     j.n = n;
+    j.rows = rows;
+    j.cols = cols;
     j.block = block;
     j.fmt = fmt;
     j.gmode = gmode;

@@ -1018,6 +1018,240 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(AParams p) {
     }
 }
 
+// ------------------------------------------------------------ per-row scale
+// Activations, one token per row: every row is quantized (UE4M3) under its own
+// dynamic scale g_r = RN32(amax_r / 2688), 1 when that is 0.  A wave owns whole
+// rows (rows w, w + W, ... on a one-round grid): it reads its row once for the
+// maximum, builds the row's decode-scale table in its own slice of LDS, then
+// reads the row again (now in cache) and quantizes it chunk by chunk exactly as
+// k_quantize does.  No workgroup-wide barrier is needed, so waves may own
+// different numbers of rows.
+struct RowParams {
+    QParams q;      // outputs, mse kind and stats of the whole tensor
+    int64_t rows, cols;
+    float* g_rows;  // rows floats, written
+};
+
+// The kUnroll-chunk group starting at chunk k of a row of `cols` elements;
+// elements past the row's end read as zeros.
+template <int XT>
+__device__ __forceinline__ void load_row_group(Raw<XT> (&raw)[kUnroll], const void* xrow,
+                                               int64_t cols, int64_t k, int lane) {
+    constexpr int E = XT == 0 ? 2 : 4;
+    const int64_t first = k * kChunk;
+    int64_t avail = (int64_t)kUnroll * kChunk;
+    if (avail > cols - first) avail = cols - first;
+    const Rsrc r = make_rsrc(static_cast<const char*>(xrow) + first * E, avail * E);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if constexpr (XT == 0) {
+            raw[u].w = buf_load16(r, u * kChunk * E + lane * 16);
+        } else {
+            raw[u].a = buf_load16(r, u * kChunk * E + lane * 32);
+            raw[u].b = buf_load16(r, u * kChunk * E + lane * 32 + 16);
+        }
+    }
+}
+
+template <int B>
+__device__ __forceinline__ QOut row_outputs(const QParams& p, int64_t row, int64_t cols, int64_t k) {
+    const int64_t first = row * cols + k * kChunk;
+    int64_t avail = (int64_t)kUnroll * kChunk;
+    if (avail > cols - k * kChunk) avail = cols - k * kChunk;
+    QOut o;
+    o.codes = make_rsrc(p.codes + first / 2, avail / 2);
+    o.scales = make_rsrc(p.scales + first / B, avail / B);
+    o.mse = make_rsrc(p.block_mse + first / B, p.block_mse ? avail / B * 4 : 0);
+    return o;
+}
+
+// Wave-local table of the UE4M3 decode scales under g (entries as in
+// build_scale_table).  LDS operations of one wave complete in order; the
+// wavefront-scope fences keep the compiler from moving the table's accesses
+// across the hand-over.
+__device__ __forceinline__ void build_wave_table(float4* tab, float g, float D, int lane) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    for (int c = lane; c < 0x7F; c += kWave) {
+        const float d = ue_decode((uint32_t)c, kFmtUe4m3) * g;
+        const float r = d > 0.0f ? 1.0f / d : 0.0f;
+        float lim = -1.0f;
+        if (d == 0.0f) lim = __builtin_inff();
+        else if (d >= 0x1p-96f && d <= 0x1p100f) lim = d * 4096.0f;
+        const bool six = c >= 8 && d >= 0x1p-126f && D >= 0x1p-126f;
+        tab[c] = make_float4(d, r, lim, six ? 1.0f : 0.0f);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int XT, int B, int ROT, bool ERR, bool SUMSQ>
+__global__ __launch_bounds__(kThreads) void k_quantize_rows(RowParams rp) {
+    constexpr int L = B / kLaneElems;
+    constexpr int E = XT == 0 ? 2 : 4;
+    __shared__ float4 s_tab[kWaves][128];
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int gl = lane & (L - 1);
+    const int64_t W = (int64_t)gridDim.x * kWaves;
+    const int64_t wid = (int64_t)xcd_slice(blockIdx.x, gridDim.x) * kWaves + wave;
+    const int64_t nk = (rp.cols + kChunk - 1) / kChunk;  // chunks per row
+    const QParams& p = rp.q;
+    float4* tab = s_tab[wave];
+    Acc acc;
+    for (int64_t row = wid; row < rp.rows; row += W) {
+        const char* xrow = static_cast<const char*>(p.x) + row * rp.cols * E;
+        // Pass 1: the row's maximum |x| (rotated blocks when rotating).
+        uint32_t mx = 0;
+        Raw<XT> cur[kUnroll];
+        load_row_group<XT>(cur, xrow, rp.cols, 0, lane);
+        for (int64_t k = 0; k < nk; k += kUnroll) {
+            Raw<XT> nxt[kUnroll];
+            if (k + kUnroll < nk) load_row_group<XT>(nxt, xrow, rp.cols, k + kUnroll, lane);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (k + u < nk) {
+                    double unused = 0.0;
+                    mx = max(mx, chunk_absmax_bits<XT, ROT, false>(cur[u], gl, unused));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+        }
+        mx = wave_max(mx);
+        float g = __uint_as_float(mx) / 2688.0f;
+        if (!(g > 0.0f)) g = 1.0f;
+        if (lane == 0) rp.g_rows[row] = g;
+        UeCtx ue;
+        ue.g = g;
+        ue.D = 6.0f * g;
+        ue.rD = 1.0f / ue.D;
+        ue.s_fast_max = (ue.D >= 0x1p-96f && ue.D <= 0x1p100f) ? 4096.0f : -1.0f;
+        build_wave_table(tab, g, ue.D, lane);
+        ue.tab = tab;
+        // Pass 2: quantize the row.
+        load_row_group<XT>(cur, xrow, rp.cols, 0, lane);
+        for (int64_t k = 0; k < nk; k += kUnroll) {
+            Raw<XT> nxt[kUnroll];
+            if (k + kUnroll < nk) load_row_group<XT>(nxt, xrow, rp.cols, k + kUnroll, lane);
+            const QOut o = row_outputs<B>(p, row, rp.cols, k);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                if (k + u < nk)
+                    quantize_chunk<XT, kFmtUe4m3, B, ROT, ERR, SUMSQ>(cur[u], u, o, p, ue, lane, gl, acc);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+        }
+    }
+    if (p.so.stats) {
+        if (gl != 0) acc = Acc{};
+        write_partial(acc, p.so);
+    }
+}
+
+// Rows of at most kRowChunks * kWaves chunks (8192 elements): one workgroup per
+// row, each wave holding up to kRowChunks of the row's chunks (chunks wave,
+// wave + 4, ...) in registers, so the row is read from memory once.  The
+// row maximum and the decode-scale table go through LDS with workgroup
+// barriers, which every wave reaches the same number of times (rows are taken
+// per workgroup).  The next row's loads are issued before the current row is
+// quantized.
+constexpr int kRowChunks = 4;
+
+template <int XT>
+__device__ __forceinline__ void load_row_chunks(Raw<XT> (&raw)[kRowChunks], const void* xrow,
+                                                int64_t cols, int wave, int lane) {
+    constexpr int E = XT == 0 ? 2 : 4;
+    const Rsrc r = make_rsrc(xrow, cols * E);
+#pragma unroll
+    for (int u = 0; u < kRowChunks; ++u) {
+        const int off = (u * kWaves + wave) * kChunk * E;  // past the row: zeros
+        if constexpr (XT == 0) {
+            raw[u].w = buf_load16(r, off + lane * 16);
+        } else {
+            raw[u].a = buf_load16(r, off + lane * 32);
+            raw[u].b = buf_load16(r, off + lane * 32 + 16);
+        }
+    }
+}
+
+template <int XT, int B, int ROT, bool ERR, bool SUMSQ>
+__global__ __launch_bounds__(kThreads) void k_quantize_rows_wg(RowParams rp) {
+    constexpr int L = B / kLaneElems;
+    constexpr int E = XT == 0 ? 2 : 4;
+    __shared__ float4 s_tab[kUeCodes];
+    __shared__ uint32_t s_m[kWaves];
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int gl = lane & (L - 1);
+    const int nk = (int)((rp.cols + kChunk - 1) / kChunk);  // <= kRowChunks * kWaves
+    const QParams& p = rp.q;
+    const int64_t G = gridDim.x;
+    const int64_t first_row = xcd_slice(blockIdx.x, gridDim.x);
+    Acc acc;
+    Raw<XT> cur[kRowChunks];
+    if (first_row < rp.rows)
+        load_row_chunks<XT>(cur, static_cast<const char*>(p.x) + first_row * rp.cols * E, rp.cols,
+                            wave, lane);
+    for (int64_t row = first_row; row < rp.rows; row += G) {
+        uint32_t mx = 0;
+#pragma unroll
+        for (int u = 0; u < kRowChunks; ++u) {
+            if (u * kWaves + wave < nk) {
+                double unused = 0.0;
+                mx = max(mx, chunk_absmax_bits<XT, ROT, false>(cur[u], gl, unused));
+            }
+        }
+        mx = wave_max(mx);
+        if (lane == 0) s_m[wave] = mx;
+        __syncthreads();  // also: every wave is done with the previous row's table
+        uint32_t m = s_m[0];
+        for (int w = 1; w < kWaves; ++w) m = max(m, s_m[w]);
+        float g = __uint_as_float(m) / 2688.0f;
+        if (!(g > 0.0f)) g = 1.0f;
+        if (threadIdx.x == 0) rp.g_rows[row] = g;
+        UeCtx ue;
+        ue.g = g;
+        ue.D = 6.0f * g;
+        ue.rD = 1.0f / ue.D;
+        ue.s_fast_max = (ue.D >= 0x1p-96f && ue.D <= 0x1p100f) ? 4096.0f : -1.0f;
+        build_scale_table(s_tab, g, ue.D, kFmtUe4m3);  // ends in a barrier
+        ue.tab = s_tab;
+        Raw<XT> nxt[kRowChunks];
+        if (row + G < rp.rows)
+            load_row_chunks<XT>(nxt, static_cast<const char*>(p.x) + (row + G) * rp.cols * E,
+                                rp.cols, wave, lane);
+#pragma unroll
+        for (int u = 0; u < kRowChunks; ++u) {
+            const int k = u * kWaves + wave;
+            if (k < nk) {
+                const int64_t first = row * rp.cols + (int64_t)k * kChunk;
+                int64_t avail = rp.cols - (int64_t)k * kChunk;
+                if (avail > kChunk) avail = kChunk;
+                QOut o;
+                o.codes = make_rsrc(p.codes + first / 2, avail / 2);
+                o.scales = make_rsrc(p.scales + first / B, avail / B);
+                o.mse = make_rsrc(p.block_mse + first / B, p.block_mse ? avail / B * 4 : 0);
+                quantize_chunk<XT, kFmtUe4m3, B, ROT, ERR, SUMSQ>(cur[u], 0, o, p, ue, lane, gl, acc);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRowChunks; ++u) cur[u] = nxt[u];
+    }
+    if (p.so.stats) {
+        if (gl != 0) acc = Acc{};
+        write_partial(acc, p.so);
+    }
+}
+
+// Every row of an empty-column tensor gets g = 1.
+__global__ void k_fill_ones(float* g, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        g[i] = 1.0f;
+}
+
 // ------------------------------------------------------------ dequantize
 struct DParams {
     const uint8_t* codes;
@@ -1356,6 +1590,81 @@ QuantKernel pick_quant_block(int block, int rotate, bool err, bool sumsq, bool s
     }
 }
 
+typedef void (*RowKernel)(RowParams);
+
+template <int XT, int B, int ROT>
+RowKernel pick_rows(bool err, bool sumsq, bool wg) {
+    if (wg) {
+        if (!err) return k_quantize_rows_wg<XT, B, ROT, false, false>;
+        if (!sumsq) return k_quantize_rows_wg<XT, B, ROT, true, false>;
+        return k_quantize_rows_wg<XT, B, ROT, true, true>;
+    }
+    if (!err) return k_quantize_rows<XT, B, ROT, false, false>;
+    if (!sumsq) return k_quantize_rows<XT, B, ROT, true, false>;
+    return k_quantize_rows<XT, B, ROT, true, true>;
+}
+
+template <int XT>
+RowKernel pick_rows_block(int block, int rotate, bool err, bool sumsq, bool wg) {
+    switch (block) {
+        case 8: return pick_rows<XT, 8, 0>(err, sumsq, wg);
+        case 16: return rotate ? pick_rows<XT, 16, 16>(err, sumsq, wg) : pick_rows<XT, 16, 0>(err, sumsq, wg);
+        case 32: return rotate ? pick_rows<XT, 32, 32>(err, sumsq, wg) : pick_rows<XT, 32, 0>(err, sumsq, wg);
+        case 64: return pick_rows<XT, 64, 0>(err, sumsq, wg);
+        case 128: return pick_rows<XT, 128, 0>(err, sumsq, wg);
+        default: return pick_rows<XT, 256, 0>(err, sumsq, wg);
+    }
+}
+
+// UE4M3 with one dynamic scale per row (activations): a single kernel, plus the
+// finalize kernel when the tensor terms are wanted.
+int launch_quantize_rows(const QuantJob& j, char* msg, size_t msg_len) {
+    hipStream_t st = static_cast<hipStream_t>(j.stream);
+    if (j.n == 0) {
+        if (j.rows > 0) {
+            hipLaunchKernelGGL(k_fill_ones, dim3(16), dim3(256), 0, st, j.g, j.rows);
+            int rc = report(hipGetLastError(), "fill kernel launch", msg, msg_len);
+            if (rc) return rc;
+        }
+        if (j.stats) {
+            hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, st, j.stats, nullptr);
+            return report(hipGetLastError(), "empty-tensor kernel", msg, msg_len);
+        }
+        return 0;
+    }
+    const bool err = (j.block_mse != nullptr) || (j.stats != nullptr);
+    const bool rel = (j.block_mse != nullptr && j.mse_kind == kMseRel);
+    const bool sumsq = j.stats != nullptr || rel;
+    // Rows that fit in the registers of one workgroup take one workgroup each
+    // (read once); longer rows are read twice by one wave each.
+    const bool wg = (j.cols + kChunk - 1) / kChunk <= (int64_t)kRowChunks * kWaves;
+    const RowKernel k = j.xt == 0 ? pick_rows_block<0>(j.block, j.rotate, err, sumsq, wg)
+                                  : pick_rows_block<1>(j.block, j.rotate, err, sumsq, wg);
+    int64_t G = wg ? j.rows : (j.rows + kWaves - 1) / kWaves;
+    const int64_t cap = resident_groups(reinterpret_cast<const void*>(k), kThreads);
+    if (G > cap) G = cap;
+    if (G > kMaxGroups) G = kMaxGroups;
+    RowParams rp{};
+    QParams& p = rp.q;
+    p.x = j.x;
+    p.n = j.n;
+    p.codes = j.codes;
+    p.scales = j.scales;
+    p.block_mse = j.block_mse;
+    p.mse_kind = j.mse_kind;
+    p.fmt = kFmtUe4m3;
+    p.so.stats = j.stats;
+    p.so.n_blocks = j.n / j.block;
+    if (j.ws) p.so.partials = reinterpret_cast<double*>(static_cast<uint8_t*>(j.ws) + kWsPartials);
+    rp.rows = j.rows;
+    rp.cols = j.cols;
+    rp.g_rows = j.g;
+    hipLaunchKernelGGL(k, dim3((int)G), dim3(kThreads), 0, st, rp);
+    int rc = report(hipGetLastError(), "per-row quantize kernel launch", msg, msg_len);
+    if (rc || !j.stats) return rc;
+    return launch_finalize(p.so, (int)G, st, msg, msg_len);
+}
+
 typedef void (*AmaxKernel)(AParams);
 
 template <bool SUMSQ>
@@ -1418,6 +1727,7 @@ MseKernel pick_mse_block(int block, int rotate, bool sumsq) {
 }  // namespace
 
 int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
+    if (j.gmode == 3) return launch_quantize_rows(j, msg, msg_len);
     hipStream_t st = static_cast<hipStream_t>(j.stream);
     uint8_t* ws = static_cast<uint8_t*>(j.ws);
     const bool dynamic = (j.fmt != kFmtMx) && (j.gmode == 1);

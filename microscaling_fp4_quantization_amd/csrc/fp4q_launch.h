@@ -23,10 +23,11 @@ struct QuantJob {
     const void* x;
     int xt;            // 0 bf16, 1 f32
     int64_t n;         // rows * cols
+    int64_t rows, cols;
     int block;         // 8..256
     int fmt;           // 0 MXFP4, 1 UE4M3, 2 UE5M3
-    int gmode;         // 0 none, 1 dynamic, 2 given
-    float* g;          // device: dynamic out / given in
+    int gmode;         // 0 none, 1 dynamic, 2 given, 3 per row
+    float* g;          // device: dynamic out / given in / one per row out
     int rotate;        // 0, 16, 32
     uint8_t* codes;
     uint8_t* scales;

@@ -88,9 +88,12 @@ def test_nvfp4_validation(L):
     assert nv(L, fmt=0) == ARG and "scale_fmt" in err(L)
     assert nv(L, fmt=2, gmode=1, g=A16, ws=A16b, wsb=WSB) == ARG and "UE5M3" in err(L)
     assert nv(L, gmode=2, g=None) == ARG
-    assert nv(L, gmode=3, g=A16) == ARG
     assert nv(L, gmode=1, g=A16) == WS
     assert nv(L, gmode=2, g=A16 + 2) == ALIGN
+    assert nv(L, gmode=4, g=A16) == ARG and "ROW" in err(L)
+    assert nv(L, gmode=3, g=None) == ARG
+    assert nv(L, fmt=2, gmode=3, g=A16) == ARG and "UE5M3" in err(L)
+    assert nv(L, gmode=3, g=A16, stats=A16b) == WS
 
 
 def srch(L, x=A16, xt=0, rows=4, cols=64, fmt=1, block=16, gmode=0, g=None, rot=0, radius=1,
@@ -110,6 +113,7 @@ def test_search_validation(L):
     assert srch(L, stats=A16) == WS
     assert srch(L, gmode=1, g=A16) == WS
     assert srch(L, rows=0, radius=3) == OK
+    assert srch(L, gmode=3, g=A16) == ARG and "per-row" in err(L)
 
 
 def test_other_entry_points_validation(L):

@@ -1,0 +1,63 @@
+"""The library's calls inside a captured HIP graph: every call launches kernels
+only (no allocation, no memset), so it can be captured.  The graph is replayed
+several times with eager work and synchronisations in between, and every
+replay is checked against the eager result."""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_fp4_quantization_amd as fq
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def test_graph_replays_match_eager():
+    rng = np.random.default_rng(97)
+    xs = [torch.from_numpy((rng.standard_t(4, (64, 5120)) * 0.3).astype(np.float32))
+          .to(torch.bfloat16).to(DEV) for _ in range(2)]
+    x = xs[0].clone()
+    ws = torch.zeros(fq.workspace_bytes(), dtype=torch.uint8, device=DEV)
+    outs = dict(codes=torch.empty((64, 2560), dtype=torch.uint8, device=DEV),
+                scales=torch.empty((64, 320), dtype=torch.uint8, device=DEV),
+                block_mse=torch.empty((64, 320), dtype=torch.float32, device=DEV),
+                stats=fq.new_stats(DEV))
+    g_row = torch.empty(64, dtype=torch.float32, device=DEV)
+    g_t = torch.empty(1, dtype=torch.float32, device=DEV)
+    mx = dict(codes=torch.empty((64, 2560), dtype=torch.uint8, device=DEV),
+              scales=torch.empty((64, 160), dtype=torch.uint8, device=DEV))
+
+    def calls():
+        fq.nvfp4_quantize(x, 16, fq.FMT_UE4M3, fq.G_ROW, g_row, 16, ws=ws, **outs)
+        fq.nvfp4_quantize(x, 16, fq.FMT_UE4M3, fq.G_DYNAMIC, g_t, 0, codes=mx["codes"],
+                          scales=outs["scales"], block_mse=False, stats=False, ws=ws)
+        fq.mxfp4_quantize(x, 32, block_mse=False, stats=False, **mx)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in (outs["codes"], outs["scales"], outs["block_mse"], outs["stats"],
+                                    g_row, g_t, mx["codes"], mx["scales"])]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for rep in range(4):
+        src = xs[rep % 2]
+        x.copy_(src)
+        calls()  # eager
+        want = snapshot()
+        for t in outs.values():
+            t.zero_()
+        g_row.zero_()
+        mx["codes"].zero_()
+        graph.replay()
+        got = snapshot()
+        for a, b in zip(got, want):
+            assert torch.equal(a, b), f"replay {rep}"
+        x.mul_(0.5)  # eager work between replays
+        torch.cuda.synchronize()
