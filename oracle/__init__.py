@@ -91,6 +91,8 @@ def _bind(lib):
     lib.oracle_quantize_search.argtypes = [P, i64, i64, c.c_int, c.c_int, c.c_int, P, c.c_int,
                                            c.c_int, P, P, P, c.c_int, P, P]
     lib.oracle_quantize_search.restype = c.c_int
+    lib.oracle_gemm_mxfp4.argtypes = [P, P, P, P, i64, i64, i64, P]
+    lib.oracle_gemm_mxfp4.restype = c.c_int
     lib.oracle_dequantize.argtypes = [P, P, c.c_int, c.c_int, c.c_float, i64, i64, c.c_int, P]
     lib.oracle_dequantize.restype = c.c_int
     lib.oracle_block_mse.argtypes = [P, P, P, c.c_int, c.c_int, c.c_float, i64, i64, c.c_int,
@@ -222,6 +224,20 @@ def quantize_search(x, fmt: int, block: int, gmode: int = GMODE_NONE, g: float |
         raise OracleError("quantize_search: bad arguments")
     return {"codes": codes, "scales": scales, "block_mse": mse, "terms": acc, "counts": cnt,
             "g": float(gbuf[0])}
+
+
+def gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, m: int, n: int, k: int) -> np.ndarray:
+    """C = A_hat B_hat^T (binary64) of two MXFP4 operands given as codes (rows x k/2)
+    and E8M0 scale bytes (rows x k/32), as quantize() writes them."""
+    ac = np.ascontiguousarray(a_codes, dtype=np.uint8)
+    asc = np.ascontiguousarray(a_scales, dtype=np.uint8)
+    bc = np.ascontiguousarray(b_codes, dtype=np.uint8)
+    bsc = np.ascontiguousarray(b_scales, dtype=np.uint8)
+    out = np.zeros((m, n), np.float64)
+    rc = load().oracle_gemm_mxfp4(_ptr(ac), _ptr(asc), _ptr(bc), _ptr(bsc), m, n, k, _ptr(out))
+    if rc:
+        raise OracleError("gemm_mxfp4: bad arguments")
+    return out
 
 
 def dequantize(codes, scales, fmt: int, block: int, g: float, rows: int, cols: int,

@@ -55,6 +55,8 @@
  *   R9  Per-row dynamic scale (activations, one row per token): g_r =
  *       RN32(amax_r / 2688) from the row's own (rotated) maximum, 1 when that
  *       is 0; the row is then quantized exactly as under a given g = g_r.
+ *   R10 FP4 GEMM: C = A_hat B_hat^T from the exactly dequantized MXFP4 operands,
+ *       summed in binary64 (see oracle_gemm_mxfp4).
  */
 #include <math.h>
 #include <stddef.h>
@@ -552,6 +554,37 @@ int oracle_quantize_search(const float* x, int64_t rows, int64_t cols, int fmt, 
             }
             float mse = block_error(v, best_xh, block, mse_kind, acc, cnt);
             if (block_mse) block_mse[r * nblk_row + k] = mse;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Product of two MXFP4 matrices ([MRGPTQ] Sommario tecnico section 3 item 4
+ * and section 4: the FP4 GEMM that consumes the packed codes and scales).
+ * A (M x K) and B (N x K) are given as codes and E8M0 scale bytes in the
+ * layout oracle_quantize writes (blocks of 32 along K); the result is
+ * C = A_hat * B_hat^T in binary64 from the exactly dequantized values, C row
+ * major M x N.  (Every dequantized value v * 2^E is exact in binary64, so
+ * the only rounding is in the sums.)  R10: the product is taken on the
+ * dequantized operands; the pages give no accumulation order or precision.
+ */
+int oracle_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                      const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, double* c)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return ORACLE_BAD_ARG;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t ea = m * K + k, eb = n * K + k;
+                int ca = (a_codes[ea / 2] >> ((ea % 2) * 4)) & 15;
+                int cb = (b_codes[eb / 2] >> ((eb % 2) * 4)) & 15;
+                double va = ldexp(oracle_e2m1_value(ca), (int)a_scales[m * (K / 32) + k / 32] - 127);
+                double vb = ldexp(oracle_e2m1_value(cb), (int)b_scales[n * (K / 32) + k / 32] - 127);
+                sum += va * vb;
+            }
+            c[m * N + n] = sum;
         }
     }
     return ORACLE_OK;
