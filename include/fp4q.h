@@ -226,6 +226,29 @@ fp4q_status fp4_block_mse(const void* x, int32_t xt, const uint8_t* codes, const
 fp4q_status hadamard_block_rotate(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t n,
                                   float* out, void* stream);
 
+/*
+ * MXFP4 matrix product on the gfx950 scaled matrix cores ("Bridging the
+ * Gap...", Sommario tecnico section 3 item 4 and section 4: the FP4 GEMM that
+ * consumes the packed codes and scales).  C = A_hat * B_hat^T, where A (M x K)
+ * and B (N x K) are MXFP4 matrices exactly as mxfp4_quantize writes them
+ * (codes rows x K/2 bytes, E8M0 scales rows x K/32 bytes, blocks of 32 along
+ * K; without rotation, or with the same rotation applied to both, since the
+ * block Hadamard is orthogonal along K).  For activations times weights, A is
+ * tokens x in-features and B out-features x in-features.
+ *   a_codes, b_codes    device, 16-byte aligned
+ *   a_scales, b_scales  device
+ *   M, N, K             K % 32 == 0, K <= 2^24; M or N == 0 is a no-op;
+ *                       K == 0 writes zeros
+ *   c                   device out, M x N row-major, ct = FP4Q_F32 or FP4Q_BF16
+ *                       (round to nearest even); aligned to its element
+ * Products of E2M1 values and E8M0 scales are exact; the matrix cores add them
+ * in binary32 in 128-element steps, so C differs from the exact product by
+ * rounding of order (K/128 + 1) * 2^-24 of sum |a| |b|.  No workspace.
+ */
+fp4q_status fp4_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
+                           int32_t ct, void* stream);
+
 /* Workspace size in bytes for any call on a rows x cols tensor (a constant
  * upper bound in this version). */
 size_t fp4q_workspace_bytes(int64_t rows, int64_t cols, int32_t block);

@@ -34,8 +34,8 @@ MSE_ABS, MSE_REL = 0, 1
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
 
 EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "fp4_quantize_search", "fp4_dequantize",
-           "fp4_block_mse", "hadamard_block_rotate", "fp4q_workspace_bytes", "fp4q_last_error",
-           "fp4q_abi_version")
+           "fp4_block_mse", "hadamard_block_rotate", "fp4_gemm_mxfp4", "fp4q_workspace_bytes",
+           "fp4q_last_error", "fp4q_abi_version")
 
 
 class Fp4qError(RuntimeError):
@@ -66,6 +66,7 @@ def _bind(l):
     l.fp4_dequantize.argtypes = [P, P, i32, i32, P, i64, i64, i32, P, i32, P]
     l.fp4_quantize_search.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, i32, P, P, P, i32,
                                       P, P, sz, P]
+    l.fp4_gemm_mxfp4.argtypes = [P, P, P, P, i64, i64, i64, P, i32, P]
     l.fp4_block_mse.argtypes = [P, i32, P, P, i32, i32, P, i64, i64, i32, P, i32, P, P, sz, P]
     l.hadamard_block_rotate.argtypes = [P, i32, i64, i64, i32, P, P]
     for name in ("mxfp4_quantize", "nvfp4_quantize", "fp4_dequantize", "fp4_block_mse",
@@ -227,6 +228,24 @@ def fp4_quantize_search(x: torch.Tensor, fmt: int = FMT_UE4M3, block: int = 16,
                                      _ptr(block_mse), mse_kind, _ptr(stats), _ptr(ws),
                                      0 if ws is None else ws.numel(), _stream(x.device)))
     return Quantized(codes, scales, block_mse, stats, g)
+
+
+def fp4_gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor,
+                   b_scales: torch.Tensor, out_dtype=torch.float32,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = A_hat @ B_hat.T for MXFP4 operands as mxfp4_quantize writes them:
+    codes (rows x K/2 uint8) and E8M0 scales (rows x K/32 uint8)."""
+    a_codes, a_scales = _matrix(a_codes, "a_codes"), _matrix(a_scales, "a_scales")
+    b_codes, b_scales = _matrix(b_codes, "b_codes"), _matrix(b_scales, "b_scales")
+    m, k = a_codes.shape[0], a_codes.shape[1] * 2
+    n = b_codes.shape[0]
+    if b_codes.shape[1] * 2 != k or a_scales.shape != (m, k // 32) or b_scales.shape != (n, k // 32):
+        raise ValueError("operand shapes do not match: codes rows x K/2, scales rows x K/32")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_codes.device)
+    _check(lib().fp4_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), m, n,
+                                k, _ptr(out), _dtype_code(out), _stream(a_codes.device)))
+    return out
 
 
 def fp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, fmt: int, block: int,

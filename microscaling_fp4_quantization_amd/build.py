@@ -49,14 +49,19 @@ def build(out: str = LIB, verbose: bool = False) -> str:
     """Compile every HIP source for gfx950 and link libfp4q.so; returns its path."""
     tmp = tempfile.mkdtemp(prefix="fp4q_build_")
     try:
-        k_obj = os.path.join(tmp, "fp4q_kernels.o")
+        sources = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+        objs, jobs = [], []
+        for f in sources:
+            o = os.path.join(tmp, f[:-4] + ".o")
+            objs.append(o)
+            jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, f), "-o", o])
         a_obj = os.path.join(tmp, "fp4q_abi.o")
-        jobs = [[HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "fp4q_kernels.hip"), "-o", k_obj],
-                ["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "fp4q_abi.cpp"), "-o", a_obj]]
-        with ThreadPoolExecutor(2) as ex:
+        objs.append(a_obj)
+        jobs.append(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "fp4q_abi.cpp"), "-o", a_obj])
+        with ThreadPoolExecutor(len(jobs)) as ex:
             list(ex.map(_run, jobs))
         tmp_out = out + ".tmp"
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_out, k_obj, a_obj])
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_out, *objs])
         os.replace(tmp_out, out)
         if verbose:
             print("built", out)

@@ -209,6 +209,31 @@ fp4q_status fp4_block_mse(const void* x, int32_t xt, const uint8_t* codes, const
     return launched(fp4q::launch_block_mse(j, msg, sizeof msg), msg);
 }
 
+fp4q_status fp4_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
+                           int32_t ct, void* stream) {
+    const char* fn = "fp4_gemm_mxfp4";
+    TRY(check_dtype(fn, ct));
+    if (M < 0 || N < 0 || K < 0) return fail(FP4Q_ERR_SHAPE, "%s: negative size", fn);
+    if (K % 32 != 0) return fail(FP4Q_ERR_SHAPE, "%s: K = %lld is not a multiple of 32", fn, (long long)K);
+    if (K > (int64_t)1 << 24) return fail(FP4Q_ERR_SHAPE, "%s: K = %lld exceeds 2^24", fn, (long long)K);
+    if (N > ((int64_t)1 << 30) / (ct == FP4Q_F32 ? 4 : 2) / 128)
+        return fail(FP4Q_ERR_SHAPE, "%s: N = %lld is too large for this output type", fn, (long long)N);
+    if (M > 0 && N > 0) {
+        if (!c) return fail(FP4Q_ERR_ARG, "%s: c must not be NULL", fn);
+        if (!aligned(c, ct == FP4Q_F32 ? 4 : 2)) return fail(FP4Q_ERR_ALIGN, "%s: c is not aligned to its element", fn);
+        if (K > 0) {
+            if (!a_codes || !a_scales || !b_codes || !b_scales)
+                return fail(FP4Q_ERR_ARG, "%s: codes and scales must not be NULL", fn);
+            if (!aligned(a_codes, 16) || !aligned(b_codes, 16))
+                return fail(FP4Q_ERR_ALIGN, "%s: codes must be 16-byte aligned", fn);
+        }
+    }
+    fp4q::GemmJob j{a_codes, a_scales, b_codes, b_scales, M, N, K, c, ct, stream};
+    char msg[256] = {0};
+    return launched(fp4q::launch_gemm(j, msg, sizeof msg), msg);
+}
+
 fp4q_status hadamard_block_rotate(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t n_rot,
                                   float* out, void* stream) {
     const char* fn = "hadamard_block_rotate";

@@ -78,10 +78,22 @@ struct RotateJob {
     void* stream;
 };
 
+struct GemmJob {
+    const uint8_t* a_codes;
+    const uint8_t* a_scales;
+    const uint8_t* b_codes;
+    const uint8_t* b_scales;
+    int64_t M, N, K;
+    void* c;
+    int ct;            // 0 bf16, 1 f32
+    void* stream;
+};
+
 // Each returns 0 on success, else a HIP error code; `msg` gets a description.
 int launch_quantize(const QuantJob& j, char* msg, size_t msg_len);
 int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len);
 int launch_block_mse(const MseJob& j, char* msg, size_t msg_len);
 int launch_rotate(const RotateJob& j, char* msg, size_t msg_len);
+int launch_gemm(const GemmJob& j, char* msg, size_t msg_len);
 
 }  // namespace fp4q

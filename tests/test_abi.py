@@ -116,6 +116,20 @@ def test_search_validation(L):
     assert srch(L, gmode=3, g=A16) == ARG and "per-row" in err(L)
 
 
+def test_gemm_validation(L):
+    gm = L.fp4_gemm_mxfp4
+    assert gm(A16, A16b, A16c, A16, 4, 4, 48, A16b, 1, None) == SHAPE and "multiple of 32" in err(L)
+    assert gm(A16, A16b, A16c, A16, 4, 4, -32, A16b, 1, None) == SHAPE
+    assert gm(A16, A16b, A16c, A16, 4, 4, 1 << 25, A16b, 1, None) == SHAPE
+    assert gm(A16, A16b, A16c, A16, 4, 1 << 30, 64, A16b, 1, None) == SHAPE
+    assert gm(A16, A16b, A16c, A16, 4, 4, 64, None, 1, None) == ARG
+    assert gm(None, A16b, A16c, A16, 4, 4, 64, A16b, 1, None) == ARG
+    assert gm(A16 + 8, A16b, A16c, A16, 4, 4, 64, A16b, 1, None) == ALIGN
+    assert gm(A16, A16b, A16c, A16, 4, 4, 64, A16b + 2, 1, None) == ALIGN
+    assert gm(A16, A16b, A16c, A16, 4, 4, 64, A16b, 5, None) == ARG
+    assert gm(A16, A16b, A16c, A16, 0, 4, 64, A16b, 1, None) == OK
+
+
 def test_other_entry_points_validation(L):
     deq = L.fp4_dequantize
     assert deq(A16, A16b, 0, 16, None, 4, 64, 0, A16c, 1, None) == SHAPE  # MXFP4 needs block 32
