@@ -236,18 +236,31 @@ fp4q_status hadamard_block_rotate(const void* x, int32_t xt, int64_t rows, int64
  * block Hadamard is orthogonal along K).  For activations times weights, A is
  * tokens x in-features and B out-features x in-features.
  *   a_codes, b_codes    device, 16-byte aligned
- *   a_scales, b_scales  device
- *   M, N, K             K % 32 == 0, K <= 2^24; M or N == 0 is a no-op;
- *                       K == 0 writes zeros
+ *   a_scales, b_scales  device, any alignment
+ *   M, N, K             K % 32 == 0, K <= 2^23, M < 2^31, N * sizeof(out
+ *                       element) < 2^23; M or N == 0 is a no-op; K == 0
+ *                       writes zeros
  *   c                   device out, M x N row-major, ct = FP4Q_F32 or FP4Q_BF16
  *                       (round to nearest even); aligned to its element
+ *   ws, ws_bytes        device scratch of at least
+ *                       fp4_gemm_workspace_bytes(M, N, K) bytes, 16-byte
+ *                       aligned (not needed when M, N or K is 0): the scales
+ *                       repacked in matrix-core order.  Owned by the caller;
+ *                       calls that overlap in time need distinct workspaces.
  * Products of E2M1 values and E8M0 scales are exact; the matrix cores add them
- * in binary32 in 128-element steps, so C differs from the exact product by
- * rounding of order (K/128 + 1) * 2^-24 of sum |a| |b|.  No workspace.
+ * in binary32 in 64-element steps, so C differs from the exact product by
+ * rounding of order (K/64 + 1) * 2^-24 of sum |a| |b|.  Errors: FP4Q_ERR_SHAPE
+ * (sizes), FP4Q_ERR_ARG (NULL operand or c, bad ct), FP4Q_ERR_ALIGN,
+ * FP4Q_ERR_WORKSPACE, FP4Q_ERR_HIP (launch failure); nothing is launched on
+ * an error other than FP4Q_ERR_HIP.
  */
 fp4q_status fp4_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                            const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
-                           int32_t ct, void* stream);
+                           int32_t ct, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes fp4_gemm_mxfp4 needs for an M x N x K product: 256 *
+ * (ceil(M/32) + ceil(N/32)) * ceil(K/256); 0 when M, N or K is 0. */
+size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Workspace size in bytes for any call on a rows x cols tensor (a constant
  * upper bound in this version). */

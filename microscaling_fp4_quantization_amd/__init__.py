@@ -34,7 +34,8 @@ MSE_ABS, MSE_REL = 0, 1
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
 
 EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "fp4_quantize_search", "fp4_dequantize",
-           "fp4_block_mse", "hadamard_block_rotate", "fp4_gemm_mxfp4", "fp4q_workspace_bytes",
+           "fp4_block_mse", "hadamard_block_rotate", "fp4_gemm_mxfp4", "fp4_gemm_workspace_bytes",
+           "fp4q_workspace_bytes",
            "fp4q_last_error", "fp4q_abi_version")
 
 
@@ -66,7 +67,9 @@ def _bind(l):
     l.fp4_dequantize.argtypes = [P, P, i32, i32, P, i64, i64, i32, P, i32, P]
     l.fp4_quantize_search.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, i32, P, P, P, i32,
                                       P, P, sz, P]
-    l.fp4_gemm_mxfp4.argtypes = [P, P, P, P, i64, i64, i64, P, i32, P]
+    l.fp4_gemm_mxfp4.argtypes = [P, P, P, P, i64, i64, i64, P, i32, P, sz, P]
+    l.fp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+    l.fp4_gemm_workspace_bytes.restype = sz
     l.fp4_block_mse.argtypes = [P, i32, P, P, i32, i32, P, i64, i64, i32, P, i32, P, P, sz, P]
     l.hadamard_block_rotate.argtypes = [P, i32, i64, i64, i32, P, P]
     for name in ("mxfp4_quantize", "nvfp4_quantize", "fp4_dequantize", "fp4_block_mse",
@@ -230,9 +233,24 @@ def fp4_quantize_search(x: torch.Tensor, fmt: int = FMT_UE4M3, block: int = 16,
     return Quantized(codes, scales, block_mse, stats, g)
 
 
+_gemm_workspaces = {}
+
+
+def gemm_workspace(device, nbytes: int) -> torch.Tensor:
+    """A device workspace of at least `nbytes` for fp4_gemm_mxfp4, kept per
+    device and grown on demand (shared by calls made on one stream)."""
+    key = torch.device(device).index
+    ws = _gemm_workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _gemm_workspaces[key] = ws
+    return ws
+
+
 def fp4_gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor,
                    b_scales: torch.Tensor, out_dtype=torch.float32,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   out: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C = A_hat @ B_hat.T for MXFP4 operands as mxfp4_quantize writes them:
     codes (rows x K/2 uint8) and E8M0 scales (rows x K/32 uint8)."""
     a_codes, a_scales = _matrix(a_codes, "a_codes"), _matrix(a_scales, "a_scales")
@@ -243,8 +261,12 @@ def fp4_gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch
         raise ValueError("operand shapes do not match: codes rows x K/2, scales rows x K/32")
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a_codes.device)
+    need = int(lib().fp4_gemm_workspace_bytes(m, n, k))
+    if ws is None and need:
+        ws = gemm_workspace(a_codes.device, need)
     _check(lib().fp4_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), m, n,
-                                k, _ptr(out), _dtype_code(out), _stream(a_codes.device)))
+                                k, _ptr(out), _dtype_code(out), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(a_codes.device)))
     return out
 
 

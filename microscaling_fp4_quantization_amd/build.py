@@ -9,6 +9,8 @@ C++.  Flags that matter for the arithmetic:
   -fno-gpu-flush-denormals-to-zero, no fast-math: IEEE binary32 and binary64
                          with subnormals and correctly rounded division
   -target-feature -packed-fp32-ops: no packed-FP32 instructions
+The GEMM source also takes -amdgpu-mfma-vgpr-form: matrix-core accumulators
+in ordinary VGPRs, which keeps them in place across the K loop.
 """
 from __future__ import annotations
 
@@ -30,6 +32,7 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contra
              "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function"]
+FILE_FLAGS = {"fp4q_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 
@@ -54,7 +57,7 @@ def build(out: str = LIB, verbose: bool = False) -> str:
         for f in sources:
             o = os.path.join(tmp, f[:-4] + ".o")
             objs.append(o)
-            jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, f), "-o", o])
+            jobs.append([HIPCC, *HIP_FLAGS, *FILE_FLAGS.get(f, []), "-c", os.path.join(CSRC, f), "-o", o])
         a_obj = os.path.join(tmp, "fp4q_abi.o")
         objs.append(a_obj)
         jobs.append(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "fp4q_abi.cpp"), "-o", a_obj])

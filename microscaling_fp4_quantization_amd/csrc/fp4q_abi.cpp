@@ -211,27 +211,39 @@ fp4q_status fp4_block_mse(const void* x, int32_t xt, const uint8_t* codes, const
 
 fp4q_status fp4_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                            const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
-                           int32_t ct, void* stream) {
+                           int32_t ct, void* ws, size_t ws_bytes, void* stream) {
     const char* fn = "fp4_gemm_mxfp4";
     TRY(check_dtype(fn, ct));
     if (M < 0 || N < 0 || K < 0) return fail(FP4Q_ERR_SHAPE, "%s: negative size", fn);
     if (K % 32 != 0) return fail(FP4Q_ERR_SHAPE, "%s: K = %lld is not a multiple of 32", fn, (long long)K);
-    if (K > (int64_t)1 << 24) return fail(FP4Q_ERR_SHAPE, "%s: K = %lld exceeds 2^24", fn, (long long)K);
-    if (N > ((int64_t)1 << 30) / (ct == FP4Q_F32 ? 4 : 2) / 128)
+    if (K > (int64_t)1 << 23) return fail(FP4Q_ERR_SHAPE, "%s: K = %lld exceeds 2^23", fn, (long long)K);
+    const int64_t eb = ct == FP4Q_F32 ? 4 : 2;
+    if (N * eb >= (int64_t)1 << 23)
         return fail(FP4Q_ERR_SHAPE, "%s: N = %lld is too large for this output type", fn, (long long)N);
+    if (M >= (int64_t)1 << 31) return fail(FP4Q_ERR_SHAPE, "%s: M = %lld exceeds 2^31", fn, (long long)M);
     if (M > 0 && N > 0) {
         if (!c) return fail(FP4Q_ERR_ARG, "%s: c must not be NULL", fn);
-        if (!aligned(c, ct == FP4Q_F32 ? 4 : 2)) return fail(FP4Q_ERR_ALIGN, "%s: c is not aligned to its element", fn);
+        if (!aligned(c, (size_t)eb)) return fail(FP4Q_ERR_ALIGN, "%s: c is not aligned to its element", fn);
         if (K > 0) {
             if (!a_codes || !a_scales || !b_codes || !b_scales)
                 return fail(FP4Q_ERR_ARG, "%s: codes and scales must not be NULL", fn);
             if (!aligned(a_codes, 16) || !aligned(b_codes, 16))
                 return fail(FP4Q_ERR_ALIGN, "%s: codes must be 16-byte aligned", fn);
+            const size_t need = fp4q::gemm_workspace_bytes(M, N, K);
+            if (!ws || ws_bytes < need)
+                return fail(FP4Q_ERR_WORKSPACE, "%s: needs a workspace of %zu bytes (got %zu)", fn, need,
+                            ws ? ws_bytes : (size_t)0);
+            if (!aligned(ws, 16)) return fail(FP4Q_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
         }
     }
-    fp4q::GemmJob j{a_codes, a_scales, b_codes, b_scales, M, N, K, c, ct, stream};
+    fp4q::GemmJob j{a_codes, a_scales, b_codes, b_scales, M, N, K, c, ct, ws, stream};
     char msg[256] = {0};
     return launched(fp4q::launch_gemm(j, msg, sizeof msg), msg);
+}
+
+size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return fp4q::gemm_workspace_bytes(M, N, K);
 }
 
 fp4q_status hadamard_block_rotate(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t n_rot,

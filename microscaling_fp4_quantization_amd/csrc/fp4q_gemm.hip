@@ -6,21 +6,40 @@
 // a row.  For an activation-times-weight product A holds the activations
 // (tokens x in-features) and B the weights (out-features x in-features).
 //
-// The hot loop is v_mfma_scale_f32_16x16x128_f8f6f4 with both operands in E2M1
-// (format 4) and a per-lane E8M0 scale for each.  For that instruction lane l
-// supplies row l % 16 of its 16 x 128 operand over the 32-element K block
-// l / 16, as 16 bytes of packed codes, plus that block's scale byte; lane l
-// receives C[4 (l / 16) + i][l % 16], i = 0..3.  A lane's operand is therefore
-// exactly 16 contiguous bytes of one row of the stored codes: the matrices are
-// consumed as the quantizer wrote them, without repacking.
+// The hot loop is v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in E2M1
+// (format 4): lane l supplies row l % 32 of its 32 x 64 operand over the
+// 32-element K block l / 32, as 16 bytes of packed codes, plus that block's
+// scale byte, selected from a 32-bit register by the instruction's byte
+// select.  Lane l receives, in register r, row 8 (r / 4) + 4 (l / 32) + r % 4
+// and column l % 32 of the 32 x 32 result.  (On MI355X this shape sustains
+// about 1.3x the rate of the 16 x 16 x 128 one.)
 //
-// Tiling: a workgroup of 4 waves computes a 128 x 128 tile of C; wave (wm, wn)
-// a 64 x 64 sub-tile as 4 x 4 MFMAs.  K advances 128 at a time through
-// double-buffered LDS stages (codes 128 rows x 64 bytes plus 4 scale bytes per
-// row, for A and for B): the next stage's global loads are issued before the
-// current stage's MFMAs and written to LDS after them.  All global accesses are
-// range-checked buffer operations, so tiles that overhang M, N or K read zeros
-// (code +0, which contributes nothing) and drop their stores.
+// Two kernels per call:
+//  k_pack_scales  rewrites each operand's scale bytes (1/16 of its size) into
+//                 the order the matrix-core lanes consume them, so that a wave
+//                 fetches a K stage's scales for one 32-row operand with one
+//                 contiguous 256-byte load;
+//  k_gemm_mxfp4   a workgroup of 8 waves computes a 256 x 256 tile of C; K
+//                 advances 256 at a time through two LDS stages.
+//
+// Operand codes go from memory to LDS by direct buffer-to-LDS loads (no
+// register staging).  A wave-wide `buffer_load_dwordx4 ... lds` writes its 64
+// lanes' 16 bytes to 1 KB of contiguous LDS, lane l at byte 16 l; one such
+// load moves 8 rows x 128 bytes, each row one whole cache line (the pattern
+// the address units serve fastest: 52 bytes per clock per CU on MI355X,
+// against 27 for half lines).  In LDS a stage is row-major, 128 bytes per
+// row, with row R's eight 16-byte K blocks stored rotated by R / 2 places, so
+// that the 16 lanes served together by one ds_read_b128 hit 16 distinct bank
+// groups.
+//
+// The weight operand B is the instruction's first source and the activations
+// A its second, so the result is a tile of C^T: each lane holds runs of 4
+// consecutive columns of one row of C, written as one store each.
+//
+// All global accesses are range-checked buffer operations over per-tile
+// windows: rows past M or N read zeros (their results are not stored), K
+// blocks past K are fetched from an offset past the window (zeros: code +0),
+// and stores outside C are dropped.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -32,91 +51,79 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((address_space(3))) void* LdsPtr;
 
 constexpr int kWave = 64;
-constexpr int kThreads = 256;
-constexpr int BM = 128, BN = 128, BK = 128;   // workgroup tile and K step
-constexpr int kRowBytes = BK / 2;             // packed codes per tile row per stage
-constexpr int kLdsRow = kRowBytes + 16;       // padded LDS row (spreads the banks)
-constexpr int kFmtE2M1 = 4;                   // MFMA operand format: FP4 E2M1
-constexpr int kDropped = (int)0x80000000;     // an offset past every buffer range
+constexpr int kWaves = 8;
+constexpr int kThreads = kWave * kWaves;
+constexpr int BM = 256, BN = 256;          // workgroup tile: rows of A, rows of B
+constexpr int BK = 256;                    // K elements per stage
+constexpr int kRowStage = BK / 2;          // code bytes per row per stage (one cache line)
+constexpr int kFrag = 32;                  // rows per matrix-core operand
+constexpr int WM = 128, WN = 64;           // wave tile: rows of A, rows of B
+constexpr int FA = WM / kFrag, FB = WN / kFrag;
+constexpr int kStageBytes = (BM + BN) * kRowStage;
+constexpr int kLoads = (BM + BN) / 8 / kWaves;  // code loads per wave per stage
+constexpr int kPackBytes = 256;            // packed scales per 32-row operand per stage
+constexpr int kFmtE2M1 = 4;                // matrix-core operand format: FP4 E2M1
+constexpr int kDropped = (int)0x80000000;  // an offset past every buffer window
+constexpr int kPastWindow = 1 << 30;       // every window is at most 2^30 bytes
 constexpr int kRsrcWord3 = 0x00020000;
+static_assert(BM == BN && kLoads % 2 == 0 && kLoads / 2 * kWaves * 8 == BM, "load plan");
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
 }
 
+// ---------------------------------------------------------------------------
+// Scale packing.  Operand rows are grouped in 32-row fragments f and K in
+// stages s of 256 (8 scale blocks).  Fragment f, stage s owns 256 bytes at
+// (f * S + s) * 256: the dword of lane l holds, in byte t, the scale of row
+// 32 f + l % 32 and K block 8 s + 2 t + l / 32 -- the block that lane l feeds
+// to the instruction of depth t within the stage.  Rows and blocks that do not
+// exist get byte 0 (their codes are read as +0, so the product is +0).
+//
+// One thread per (fragment, stage, fragment row): it reads the row's 8 scale
+// bytes of the stage and writes the dwords of lanes r and r + 32.
+__global__ __launch_bounds__(256) void k_pack_scales(const uint8_t* __restrict__ sc, int64_t rows,
+                                                     int64_t kblocks, int64_t stages, int64_t frags,
+                                                     uint32_t* __restrict__ out) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= frags * stages * kFrag) return;
+    const int r = (int)(idx % kFrag);
+    const int64_t s = (idx / kFrag) % stages, f = idx / (kFrag * stages);
+    const int64_t row = f * kFrag + r;
+    uint32_t even = 0, odd = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int64_t b = 8 * s + 2 * t;
+        const uint32_t lo = row < rows && b < kblocks ? sc[row * kblocks + b] : 0u;
+        const uint32_t hi = row < rows && b + 1 < kblocks ? sc[row * kblocks + b + 1] : 0u;
+        even |= lo << (8 * t);
+        odd |= hi << (8 * t);
+    }
+    uint32_t* dst = out + (f * stages + s) * (kPackBytes / 4);
+    dst[r] = even;
+    dst[r + kFrag] = odd;
+}
+
+// ---------------------------------------------------------------------------
+// The GEMM kernel.
+
 struct GParams {
     const uint8_t* a_codes;
-    const uint8_t* a_scales;
     const uint8_t* b_codes;
-    const uint8_t* b_scales;
+    const uint8_t* a_pack;  // packed scales of A
+    const uint8_t* b_pack;  // packed scales of B
     int64_t M, N, K;
+    int64_t S;              // K stages, ceil(K / 256)
     void* c;
-    int ct;  // 0 bf16, 1 f32
+    int ct;                 // 0 bf16, 1 f32
 };
-
-// One stage of global data held in registers between its load and its LDS
-// write: each thread moves 2 x 16 bytes of codes of A and of B, and one row's
-// 4 scale bytes (of A for threads below 128, of B above).
-struct Stage {
-    u32x4_t a[2], b[2];
-    uint32_t sc;
-};
-
-// The workgroup's operand windows: buffer resources based at its first row of
-// A and of B (so every offset stays within one 128-row slab), sized to the
-// rows that exist.
-struct Tiles {
-    Rsrc a, b, sa, sb;
-};
-
-// Thread t moves rows t / 4 and 64 + t / 4, 16-byte segment t % 4 of the
-// stage's 64 code bytes per row; segments past K read zeros (code +0).
-// Threads t < 128 also move the 4 scale bytes of A's row t, t >= 128 those of
-// B's row t - 128 (as byte loads: a row's scale bytes need not be aligned).
-__device__ __forceinline__ void load_stage(Stage& s, const GParams& p, const Tiles& w,
-                                           int64_t k0) {
-    const int t = threadIdx.x;
-    const int seg = t & 3;
-    const bool kin = k0 + seg * 32 < p.K;  // the segment's 32 elements are inside K
-    const int rowb = (int)(p.K / 2);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = (t >> 2) + h * 64;
-        const int o = kin ? r * rowb + (int)(k0 / 2) + seg * 16 : kDropped;
-        s.a[h] = __builtin_amdgcn_raw_buffer_load_b128(w.a, o, 0, 0);
-        s.b[h] = __builtin_amdgcn_raw_buffer_load_b128(w.b, o, 0, 0);
-    }
-    const int srow = (int)(p.K / 32);
-    const int r = t & 127;
-    uint32_t word = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int off = (k0 / 32 + q) < srow ? r * srow + (int)(k0 / 32) + q : kDropped;
-        const uint32_t byte = t >= 128 ? __builtin_amdgcn_raw_buffer_load_b8(w.sb, off, 0, 0)
-                                       : __builtin_amdgcn_raw_buffer_load_b8(w.sa, off, 0, 0);
-        word |= byte << (8 * q);
-    }
-    s.sc = word;
-}
-
-__device__ __forceinline__ void store_stage(const Stage& s, uint8_t* la, uint8_t* lb,
-                                            uint32_t* lsa, uint32_t* lsb) {
-    const int t = threadIdx.x;
-    const int seg = t & 3;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = (t >> 2) + h * 64;
-        *reinterpret_cast<u32x4_t*>(la + r * kLdsRow + seg * 16) = s.a[h];
-        *reinterpret_cast<u32x4_t*>(lb + r * kLdsRow + seg * 16) = s.b[h];
-    }
-    if (t < 128) lsa[t] = s.sc;
-    else lsb[t - 128] = s.sc;
-}
 
 // Round-to-nearest-even binary32 -> bf16 bits.
 __device__ __forceinline__ uint32_t to_bf16(float f) {
@@ -124,95 +131,249 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
     return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
+// Tile of workgroup g: the 8 XCDs take workgroups round robin, so tiles are
+// renumbered to give each XCD a contiguous run, walked in groups of kGroupM
+// tile rows so that concurrently running tiles share operand rows in its L2.
+constexpr int kGroupM = 4;
+
+__device__ __forceinline__ void tile_of(int64_t g, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                        int64_t& tn) {
+    const int64_t T = tiles_m * tiles_n;
+    const int64_t xcd = g % 8, idx = g / 8, per = T / 8, rem = T % 8;
+    const int64_t t = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int64_t span = (int64_t)kGroupM * tiles_n;
+    const int64_t first = (t / span) * kGroupM;
+    const int64_t gm = tiles_m - first < kGroupM ? tiles_m - first : kGroupM;
+    tm = first + (t % span) % gm;
+    tn = (t % span) / gm;
+}
+
+// Wait for all of this wave's loads (the next stage's codes and scales) and
+// LDS reads, then barrier.  The memory clobber keeps LDS accesses from moving
+// across.
+__device__ __forceinline__ void wait_all_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+struct Ops {
+    v4i a[FA], b[FB];
+};
+
+struct Scales {
+    uint32_t a[FA], b[FB];
+};
+
+// Operands of depth T within a stage: lane l takes row l % 32 of each
+// fragment, K block 2 T + l / 32, stored at position (block + row / 2) % 8.
+template <int T>
+__device__ __forceinline__ void read_ops(Ops& o, const uint8_t* stage, int a_row, int b_row,
+                                         int rot) {
+    const int at = ((2 * T + rot) & 7) * 16;
+#pragma unroll
+    for (int j = 0; j < FA; ++j)
+        o.a[j] = *reinterpret_cast<const v4i*>(stage + (a_row + j * kFrag) * kRowStage + at);
+#pragma unroll
+    for (int i = 0; i < FB; ++i)
+        o.b[i] = *reinterpret_cast<const v4i*>(stage + (BM + b_row + i * kFrag) * kRowStage + at);
+}
+
+template <int T>
+__device__ __forceinline__ void mma(v16f (&acc)[FB][FA], const Ops& o, const Scales& sc) {
+#pragma unroll
+    for (int i = 0; i < FB; ++i) {
+        const v8i b = v8i{o.b[i][0], o.b[i][1], o.b[i][2], o.b[i][3], 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < FA; ++j) {
+            const v8i a = v8i{o.a[j][0], o.a[j][1], o.a[j][2], o.a[j][3], 0, 0, 0, 0};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                b, a, acc[i][j], kFmtE2M1, kFmtE2M1, T, (int)sc.b[i], T, (int)sc.a[j]);
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_a[2][BM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) uint8_t s_b[2][BN * kLdsRow];
-    __shared__ uint32_t s_sa[2][BM];
-    __shared__ uint32_t s_sb[2][BN];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes];
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
-    // Tiles along N vary fastest, so consecutive workgroups share A's rows.
-    const int64_t tiles_n = (p.N + BN - 1) / BN;
-    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * BM;
-    const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * BN;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
+    const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    int64_t tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = tm * BM, n0 = tn * BN;
     const int64_t rows_a = p.M - m0 < BM ? p.M - m0 : BM;
     const int64_t rows_b = p.N - n0 < BN ? p.N - n0 : BN;
-    Tiles w;
-    w.a = make_rsrc(p.a_codes + m0 * (p.K / 2), rows_a * (p.K / 2));
-    w.b = make_rsrc(p.b_codes + n0 * (p.K / 2), rows_b * (p.K / 2));
-    w.sa = make_rsrc(p.a_scales + m0 * (p.K / 32), rows_a * (p.K / 32));
-    w.sb = make_rsrc(p.b_scales + n0 * (p.K / 32), rows_b * (p.K / 32));
+    const int rowb = (int)(p.K / 2);
+    const Rsrc ra = make_rsrc(p.a_codes + m0 * rowb, rows_a * rowb);
+    const Rsrc rb = make_rsrc(p.b_codes + n0 * rowb, rows_b * rowb);
+    // Packed scales of this tile's fragments (at most 8 per side).  Every
+    // offset below fits 32 bits: K <= 2^23, so S <= 2^15 and a window is at
+    // most 2^30 bytes.
+    const int K = (int)p.K, S = (int)p.S;
+    const int pack_frag = S * kPackBytes;
+    const int64_t fa = (rows_a + kFrag - 1) / kFrag, fb = (rows_b + kFrag - 1) / kFrag;
+    const Rsrc rsa = make_rsrc(p.a_pack + (m0 / kFrag) * pack_frag, fa * pack_frag);
+    const Rsrc rsb = make_rsrc(p.b_pack + (n0 / kFrag) * pack_frag, fb * pack_frag);
 
-    v4f acc[4][4];
+    // Code loads: load q of a wave moves rows 8 d .. 8 d + 7, d = wave + 8 (q
+    // % 4), of A (q < 4) or of B; lane l fetches row 8 d + l / 8 into LDS
+    // position l % 8 of that row, which holds K block (l % 8 - row / 2) % 8.
+    // Since row / 2 = 4 d + l / 16 and d = wave (mod 2), the block is the same
+    // for every load of the wave.
+    const int blk = ((lane % 8) - 4 * (wave & 1) - lane / 16) & 7;
+    const int lane_off = (lane / 8) * rowb + blk * 16;
+    auto issue = [&](uint8_t* stage, int s) {
+        const int k0 = s * BK;
+        // Past K (this lane's block): an offset past the window, so zeros.
+        const int base = k0 + blk * 32 < K ? lane_off + k0 / 2 : kPastWindow;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int64_t n_stages = (p.K + BK - 1) / BK;
-    Stage st;
-    load_stage(st, p, w, 0);
-    store_stage(st, s_a[0], s_b[0], s_sa[0], s_sb[0]);
-    const int fr = lane & 15, fk = lane >> 4;  // fragment row and K block of this lane
-    for (int64_t s = 0; s < n_stages; ++s) {
-        const int cur = (int)(s & 1);
-        __syncthreads();  // stage s is in LDS; every wave is done with stage s - 1
-        const bool more = s + 1 < n_stages;
-        if (more) load_stage(st, p, w, (s + 1) * BK);
-        v8i af[4], bf[4];
-        int sa[4], sb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ra_row = wm * 64 + i * 16 + fr;
-            const v4i v = *reinterpret_cast<const v4i*>(&s_a[cur][ra_row * kLdsRow + fk * 16]);
-            af[i] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-            sa[i] = (int)((s_sa[cur][ra_row] >> (8 * fk)) & 0xFFu);
-            const int rb_row = wn * 64 + i * 16 + fr;
-            const v4i w = *reinterpret_cast<const v4i*>(&s_b[cur][rb_row * kLdsRow + fk * 16]);
-            bf[i] = v8i{w[0], w[1], w[2], w[3], 0, 0, 0, 0};
-            sb[i] = (int)((s_sb[cur][rb_row] >> (8 * fk)) & 0xFFu);
+        for (int q = 0; q < kLoads; ++q) {
+            const bool is_a = q < kLoads / 2;
+            const int d = wave + kWaves * (q % (kLoads / 2));
+            const int off = base + 8 * d * rowb;
+            uint8_t* dst = stage + (is_a ? 0 : BM * kRowStage) + d * 8 * kRowStage;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (LdsPtr)dst, 16, off, 0, 0, 0);
         }
+    };
+    // Scales of stage s: one dword per lane per fragment (past the last
+    // stage: an offset past the window, so zeros).
+    const int sa_off = wm * FA * pack_frag + lane * 4, sb_off = wn * FB * pack_frag + lane * 4;
+    auto load_scales = [&](Scales& sc, int s) {
+        const int so = s < S ? s * kPackBytes : kPastWindow;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < FA; ++j)
+            sc.a[j] = __builtin_amdgcn_raw_buffer_load_b32(rsa, sa_off + j * pack_frag + so, 0, 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af[i], bf[j], acc[i][j], kFmtE2M1, kFmtE2M1, 0, sa[i], 0, sb[j]);
-        if (more) store_stage(st, s_a[cur ^ 1], s_b[cur ^ 1], s_sa[cur ^ 1], s_sb[cur ^ 1]);
+        for (int i = 0; i < FB; ++i)
+            sc.b[i] = __builtin_amdgcn_raw_buffer_load_b32(rsb, sb_off + i * pack_frag + so, 0, 0);
+    };
+
+    v16f acc[FB][FA];
+#pragma unroll
+    for (int i = 0; i < FB; ++i)
+#pragma unroll
+        for (int j = 0; j < FA; ++j) acc[i][j] = v16f{};
+
+    const int a_row = wm * WM + lane % kFrag;  // within the tile
+    const int b_row = wn * WN + lane % kFrag;
+    const int rot = lane / kFrag + ((lane % kFrag) >> 1);
+
+    // Stage s: codes in buffer s % 2, scales in registers.  Each step first
+    // starts the loads of stage s + 1 (into the buffer stage s - 1 left), then
+    // runs stage s, then waits for stage s + 1 and meets the other waves.
+    // Stages past K load zeros; an odd stage count gets one such stage, which
+    // adds +0 to sums that started at +0 and so changes no bit.
+    const int ns2 = S + (S & 1);
+    Scales sc0, sc1;
+    issue(lds, 0);
+    load_scales(sc0, 0);
+    wait_all_barrier();
+    auto step = [&](int s, const Scales& cur, Scales& nxt) {
+        const uint8_t* here = lds + (s & 1) * kStageBytes;
+        issue(lds + ((s + 1) & 1) * kStageBytes, s + 1);
+        load_scales(nxt, s + 1);
+        Ops o0, o1;
+        read_ops<0>(o0, here, a_row, b_row, rot);
+        __builtin_amdgcn_sched_barrier(0);
+        read_ops<1>(o1, here, a_row, b_row, rot);
+        __builtin_amdgcn_sched_barrier(0);
+        mma<0>(acc, o0, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        read_ops<2>(o0, here, a_row, b_row, rot);
+        __builtin_amdgcn_sched_barrier(0);
+        mma<1>(acc, o1, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        read_ops<3>(o1, here, a_row, b_row, rot);
+        __builtin_amdgcn_sched_barrier(0);
+        mma<2>(acc, o0, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        mma<3>(acc, o1, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_all_barrier();
+    };
+    for (int s = 0; s < ns2; s += 2) {
+        step(s, sc0, sc1);
+        step(s + 1, sc1, sc0);
     }
 
-    // Lane l holds C[row0 + 4 (l / 16) + r][col0 + l % 16] of each 16 x 16 tile.
+    // Lane l, register r of result (i, j): row m = j * 32 + l % 32 of the wave
+    // tile, columns n = i * 32 + 8 (r / 4) + 4 (l / 32) + r % 4.
     const int eb = p.ct == 1 ? 4 : 2;
     const Rsrc rc = make_rsrc(static_cast<char*>(p.c) + m0 * p.N * eb, rows_a * p.N * eb);
+    const bool vec = (p.N & 3) == 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < FA; ++j) {
+        const int row = wm * WM + j * kFrag + lane % kFrag;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 64 + j * 16 + fr;
+        for (int i = 0; i < FB; ++i) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = wm * 64 + i * 16 + 4 * fk + r;  // within the tile
-                const bool in = row < rows_a && col < p.N;
-                const int off = in ? (int)((row * p.N + col) * eb) : kDropped;
-                if (p.ct == 1)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, off, 0, 0);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)to_bf16(acc[i][j][r]), rc,
-                                                          off, 0, 0);
+            for (int g = 0; g < 4; ++g) {
+                const int64_t col = n0 + wn * WN + i * kFrag + 8 * g + 4 * (lane / kFrag);
+                const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                    acc[i][j][4 * g + 3]};
+                if (vec) {
+                    const int off = row < rows_a && col < p.N ? (int)((row * p.N + col) * eb) : kDropped;
+                    if (p.ct == 1)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                    __float_as_uint(v[3])},
+                            rc, off, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            u32x2_t{to_bf16(v[0]) | (to_bf16(v[1]) << 16),
+                                    to_bf16(v[2]) | (to_bf16(v[3]) << 16)},
+                            rc, off, 0, 0);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int off = row < rows_a && col + r < p.N ? (int)((row * p.N + col + r) * eb)
+                                                                      : kDropped;
+                        if (p.ct == 1)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), rc, off, 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)to_bf16(v[r]), rc, off,
+                                                                  0, 0);
+                    }
+                }
             }
         }
     }
 }
 
+int64_t frags_of(int64_t rows) { return (rows + kFrag - 1) / kFrag; }
+
 }  // namespace
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const int64_t S = (K + BK - 1) / BK;
+    return (size_t)((frags_of(M) + frags_of(N)) * S * kPackBytes);
+}
 
 int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
     if (j.M == 0 || j.N == 0) return 0;
-    GParams p{j.a_codes, j.a_scales, j.b_codes, j.b_scales, j.M, j.N, j.K, j.c, j.ct};
+    const hipStream_t stream = static_cast<hipStream_t>(j.stream);
+    const int64_t S = (j.K + BK - 1) / BK;
+    uint8_t* a_pack = static_cast<uint8_t*>(j.ws);
+    uint8_t* b_pack = a_pack + frags_of(j.M) * S * kPackBytes;
+    const int64_t kb = j.K / 32;
     const int64_t tiles = ((j.M + BM - 1) / BM) * ((j.N + BN - 1) / BN);
-    hipLaunchKernelGGL(k_gemm_mxfp4, dim3((unsigned)tiles), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(j.stream), p);
+    if (tiles > INT32_MAX || (frags_of(j.M) + frags_of(j.N)) * S * kFrag / 256 > INT32_MAX) {
+        snprintf(msg, msg_len, "gemm: %lld x %lld x %lld needs more workgroups than one launch holds",
+                 (long long)j.M, (long long)j.N, (long long)j.K);
+        return (int)hipErrorInvalidConfiguration;
+    }
+    const struct {
+        const uint8_t* sc;
+        int64_t rows;
+        uint8_t* out;
+    } packs[2] = {{j.a_scales, j.M, a_pack}, {j.b_scales, j.N, b_pack}};
+    for (const auto& pk : packs) {
+        const int64_t threads = frags_of(pk.rows) * S * kFrag;
+        if (threads == 0) continue;
+        hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                           pk.sc, pk.rows, kb, S, frags_of(pk.rows), reinterpret_cast<uint32_t*>(pk.out));
+    }
+    GParams p{j.a_codes, j.b_codes, a_pack, b_pack, j.M, j.N, j.K, S, j.c, j.ct};
+    hipLaunchKernelGGL(k_gemm_mxfp4, dim3((unsigned)tiles), dim3(kThreads), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) return 0;
     snprintf(msg, msg_len, "gemm kernel launch: %s", hipGetErrorString(e));

@@ -86,8 +86,11 @@ struct GemmJob {
     int64_t M, N, K;
     void* c;
     int ct;            // 0 bf16, 1 f32
+    void* ws;          // gemm_workspace_bytes(M, N, K) bytes: packed scales
     void* stream;
 };
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // Each returns 0 on success, else a HIP error code; `msg` gets a description.
 int launch_quantize(const QuantJob& j, char* msg, size_t msg_len);

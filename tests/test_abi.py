@@ -117,17 +117,32 @@ def test_search_validation(L):
 
 
 def test_gemm_validation(L):
-    gm = L.fp4_gemm_mxfp4
-    assert gm(A16, A16b, A16c, A16, 4, 4, 48, A16b, 1, None) == SHAPE and "multiple of 32" in err(L)
-    assert gm(A16, A16b, A16c, A16, 4, 4, -32, A16b, 1, None) == SHAPE
-    assert gm(A16, A16b, A16c, A16, 4, 4, 1 << 25, A16b, 1, None) == SHAPE
-    assert gm(A16, A16b, A16c, A16, 4, 1 << 30, 64, A16b, 1, None) == SHAPE
-    assert gm(A16, A16b, A16c, A16, 4, 4, 64, None, 1, None) == ARG
-    assert gm(None, A16b, A16c, A16, 4, 4, 64, A16b, 1, None) == ARG
-    assert gm(A16 + 8, A16b, A16c, A16, 4, 4, 64, A16b, 1, None) == ALIGN
-    assert gm(A16, A16b, A16c, A16, 4, 4, 64, A16b + 2, 1, None) == ALIGN
-    assert gm(A16, A16b, A16c, A16, 4, 4, 64, A16b, 5, None) == ARG
-    assert gm(A16, A16b, A16c, A16, 0, 4, 64, A16b, 1, None) == OK
+    gm = lambda a, sa, b, sb, m, n, k, c, ct, ws=A16, wsb=1 << 20: L.fp4_gemm_mxfp4(
+        a, sa, b, sb, m, n, k, c, ct, ws, wsb, None)
+    assert gm(A16, A16b, A16c, A16, 4, 4, 48, A16b, 1) == SHAPE and "multiple of 32" in err(L)
+    assert gm(A16, A16b, A16c, A16, 4, 4, -32, A16b, 1) == SHAPE
+    assert gm(A16, A16b, A16c, A16, 4, 4, 1 << 24, A16b, 1) == SHAPE and "2^23" in err(L)
+    assert gm(A16, A16b, A16c, A16, 4, 1 << 21, 64, A16b, 1) == SHAPE
+    assert gm(A16, A16b, A16c, A16, 1 << 31, 4, 64, A16b, 1) == SHAPE
+    assert gm(A16, A16b, A16c, A16, 4, 4, 64, None, 1) == ARG
+    assert gm(None, A16b, A16c, A16, 4, 4, 64, A16b, 1) == ARG
+    assert gm(A16 + 8, A16b, A16c, A16, 4, 4, 64, A16b, 1) == ALIGN
+    assert gm(A16, A16b, A16c, A16, 4, 4, 64, A16b + 2, 1) == ALIGN
+    assert gm(A16, A16b, A16c, A16, 4, 4, 64, A16b, 5) == ARG
+    assert gm(A16, A16b, A16c, A16, 4, 4, 64, A16b, 1, ws=None) == WS and "workspace" in err(L)
+    need = L.fp4_gemm_workspace_bytes(4, 4, 64)
+    assert need == 256 * 2
+    assert gm(A16, A16b, A16c, A16, 4, 4, 64, A16b, 1, wsb=need - 1) == WS
+    assert gm(A16, A16b, A16c, A16, 4, 4, 64, A16b, 1, ws=A16 + 4, wsb=need) == ALIGN
+    assert gm(A16, A16b, A16c, A16, 0, 4, 64, A16b, 1, ws=None, wsb=0) == OK
+
+
+def test_gemm_workspace_bytes(L):
+    wb = L.fp4_gemm_workspace_bytes
+    assert wb(0, 5, 64) == 0 and wb(5, 5, 0) == 0
+    assert wb(1, 1, 32) == 2 * 256
+    assert wb(33, 64, 257 * 32) == (2 + 2) * 33 * 256
+    assert wb(8192, 18944, 3584) == (256 + 592) * 14 * 256
 
 
 def test_other_entry_points_validation(L):

@@ -43,7 +43,7 @@ def bound(ac, asc, bc, bsc, m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 16, 128), (128, 128, 256), (130, 70, 96), (1, 300, 256),
-                                   (257, 129, 32)])
+                                   (257, 129, 32), (130, 70, 128), (257, 300, 256), (300, 517, 256)])
 def test_gemm_exact_when_sums_are_exact(m, n, k):
     rng = np.random.default_rng([41, m, n, k])
     ac = rng.integers(0, 256, (m, k // 2), dtype=np.uint8)
@@ -56,7 +56,7 @@ def test_gemm_exact_when_sums_are_exact(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 32), (64, 512, 4096), (200, 333, 1056), (128, 256, 3584),
-                                   (33, 1000, 8192)])
+                                   (33, 1000, 8192), (300, 517, 384), (520, 300, 512), (777, 1031, 1152)])
 def test_gemm_within_bound(m, n, k):
     ac, asc = operand(m, k, [42, m, k])
     bc, bsc = operand(n, k, [43, n, k])
@@ -68,8 +68,8 @@ def test_gemm_within_bound(m, n, k):
     assert np.all(err <= tol), f"at {i}: got {got[i]!r} want {want[i]!r} tol {tol[i]!r}"
 
 
-def test_gemm_bf16_output():
-    m, n, k = 96, 160, 512
+@pytest.mark.parametrize("m,n,k", [(96, 160, 512), (130, 158, 384), (70, 90, 96)])
+def test_gemm_bf16_output(m, n, k):
     ac, asc = operand(m, k, 44)
     bc, bsc = operand(n, k, 45)
     got = run(ac, asc, bc, bsc, torch.bfloat16)
