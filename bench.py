@@ -36,6 +36,13 @@ Workloads (--workload):
   qwen14model  a random-init Qwen2.5-14B-shaped stack (48 layers x 7 projections,
                13.2e9 bf16 parameters, 26.4 GB) quantized whole to MXFP4 and to
                dynamic NVFP4, relative per-block MSE and per-tensor split
+  gemm         a W4A4 Qwen2.5-7B MLP forward over 8192 tokens on MXFP4 operands:
+               quantize the activations X (8192 x 3584) and H (8192 x 18944) to
+               MXFP4, then the gate and up products (8192 x 18944 x 3584) and the
+               down product (8192 x 3584 x 18944) against MXFP4 weights quantized
+               beforehand, bf16 outputs.  Reported in TFLOP/s of the three products
+               over the whole step; `roofline` is one up-projection call (scale
+               packing + product) against the dense FP4 matrix-core peak.
 """
 import argparse
 import hashlib
@@ -212,6 +219,119 @@ WORKLOADS = {
 }
 
 
+# ------------------------------------------------------------------ GEMM workload
+GEMM_TOKENS = 8192
+GEMM_METRIC = ("TFLOP/s of MXFP4 x MXFP4 products (W4A4 Qwen2.5-7B MLP, 8192 tokens, "
+               "activation quantization included); % of dense FP4 matrix-core peak")
+MFMA_FP4_PEAK_TFLOPS = 10100.0
+GEMM_SAMPLE_ROWS = 8
+
+
+def gemm_main(args, steps, warmup):
+    import numpy as np
+    import torch
+    import microscaling_fp4_quantization_amd as fq
+    import fp4_workloads as wl
+
+    dev = torch.device("cuda:0")
+    hidden, inter = wl.QWEN7_SHAPES[1]
+    T = GEMM_TOKENS
+    x_host = wl.activations_f32(T, hidden, [7, T, hidden])
+    acts = {"x": wl.to_bf16(x_host).to(dev),
+            "h": wl.to_bf16(wl.activations_f32(T, inter, [7, T, inter])).to(dev)}
+    w_host = {"gate": wl.qwen7_mlp(0, 0), "up": wl.qwen7_mlp(0, 1), "down": wl.qwen7_mlp(1, 2)}
+    weights = {}
+    for name, w in w_host.items():
+        q = fq.mxfp4_quantize(w.to(dev), 0, block_mse=False, stats=False)
+        weights[name] = (q.codes, q.scales)
+    qa = {k: fq.mxfp4_quantize(v, 0, block_mse=False, stats=False) for k, v in acts.items()}
+    prods = [("gate", "x"), ("up", "x"), ("down", "h")]
+    outs = {n: torch.empty((T, weights[n][0].shape[0]), dtype=torch.bfloat16, device=dev)
+            for n, _ in prods}
+    need = max(fq.lib().fp4_gemm_workspace_bytes(T, weights[n][0].shape[0], acts[a].shape[1])
+               for n, a in prods)
+    ws = fq.gemm_workspace(dev, need)
+    flops = {n: 2.0 * T * weights[n][0].shape[0] * acts[a].shape[1] for n, a in prods}
+
+    def quantize(a):
+        fq.mxfp4_quantize(acts[a], 0, codes=qa[a].codes, scales=qa[a].scales, block_mse=False,
+                          stats=False)
+
+    def gemm(n, a):
+        fq.fp4_gemm_mxfp4(qa[a].codes, qa[a].scales, weights[n][0], weights[n][1],
+                          torch.bfloat16, out=outs[n], ws=ws)
+
+    def step():
+        quantize("x")
+        gemm("gate", "x")
+        gemm("up", "x")
+        quantize("h")
+        gemm("down", "h")
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    t_wall = time.perf_counter()
+    ms_step = time_region(torch, stream, step, steps)
+    t_wall = time.perf_counter() - t_wall
+    total_flops = sum(flops.values())
+    value = total_flops / (ms_step * 1e-3) / 1e12
+
+    reps = max(10, steps)
+    breakdown = {}
+    for n, a in prods:
+        ms = time_region(torch, stream, lambda n=n, a=a: gemm(n, a), reps)
+        breakdown[f"gemm_{n}"] = {"shape_MxNxK": f"{T}x{weights[n][0].shape[0]}x{acts[a].shape[1]}",
+                                  "us_per_call": round(ms * 1e3, 2),
+                                  "TFLOPs": round(flops[n] / (ms * 1e-3) / 1e12, 1)}
+    for a in ("x", "h"):
+        ms = time_region(torch, stream, lambda a=a: quantize(a), reps)
+        breakdown[f"quantize_{a}"] = {"shape": "x".join(map(str, acts[a].shape)),
+                                      "us_per_call": round(ms * 1e3, 2),
+                                      "input_GBps": round(acts[a].numel() * 2 / (ms * 1e-3) / 1e9, 1)}
+    up = breakdown["gemm_up"]
+    achieved = flops["up"] / (up["us_per_call"] * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP4_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP4_PEAK_TFLOPS, 4),
+                "traffic": None,
+                "kernel": "fp4_gemm_mxfp4 up projection (k_pack_scales x2 + k_gemm_mxfp4)",
+                "us_per_launch": up["us_per_call"], "algorithmic_flops_per_launch": flops["up"]}
+    line = {
+        "metric": GEMM_METRIC,
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4-e2m1 x fp4-e2m1, f32 accumulate",
+        "data": "synthetic (seeded numpy PCG64, rounded to bf16, then MXFP4)",
+        "config": {"workload": "qwen2.5-7b-mlp-w4a4-gemm", "tokens": T, "hidden": hidden,
+                   "intermediate": inter, "format": "MXFP4 operands (E2M1, E8M0 per 32), bf16 C",
+                   "flops_per_step": total_flops},
+        "roofline": roofline,
+        "step_breakdown": {"wall_s_timed_region": round(t_wall, 3), **breakdown},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        r = GEMM_SAMPLE_ROWS
+        qx = oracle.quantize(np.ascontiguousarray(x_host[:r]), oracle.FMT_MXFP4, 32)
+        qw = oracle.quantize(w_host["up"].float().numpy(), oracle.FMT_MXFP4, 32)
+        t = time.perf_counter()
+        oracle.gemm_mxfp4(qx["codes"], qx["scales"], qw["codes"], qw["scales"], r, inter, hidden)
+        el = time.perf_counter() - t
+        line["cpu_baseline"] = {
+            "value": round(2.0 * r * inter * hidden / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the up projection for the first {r} tokens ({r}x{inter}x{hidden}), "
+                      "single-threaded C oracle in binary64",
+            "seconds": round(el, 2)}
+    print(json.dumps(line), flush=True)
+
+
 # ------------------------------------------------------------------ running
 class Runner:
     """Device buffers and calls for every (tensor, spec) pair of a workload.
@@ -386,7 +506,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="qwen7", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="qwen7", choices=sorted(WORKLOADS) + ["gemm"])
     ap.add_argument("--streams", type=int, default=2,
                     help="HIP streams the step's independent calls are spread over")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -398,6 +518,10 @@ def main():
               "(the path shards by rows with one max- and one sum-all-reduce; see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "gemm":
+        gemm_main(args, args.steps if args.steps is not None else 20,
+                  args.warmup if args.warmup is not None else 3)
+        return
     w = WORKLOADS[args.workload]
     steps = args.steps if args.steps is not None else w.steps
     warmup = args.warmup if args.warmup is not None else w.warmup

@@ -34,7 +34,10 @@
 //
 // The weight operand B is the instruction's first source and the activations
 // A its second, so the result is a tile of C^T: each lane holds runs of 4
-// consecutive columns of one row of C, written as one store each.
+// consecutive columns of one row of C.  The finished tile is staged through
+// the (then idle) LDS and stored as whole row segments, 16 bytes per lane:
+// stores of 32 rows x 16 bytes straight from the accumulators cost the GEMM
+// a quarter of its time at these shapes.
 //
 // All global accesses are range-checked buffer operations over per-tile
 // windows: rows past M or N read zeros (their results are not stored), K
@@ -73,6 +76,11 @@ constexpr int kFmtE2M1 = 4;                // matrix-core operand format: FP4 E2
 constexpr int kDropped = (int)0x80000000;  // an offset past every buffer window
 constexpr int kPastWindow = 1 << 30;       // every window is at most 2^30 bytes
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the stores of C: non-temporal.  C is written once and not
+// read back here; cached, it evicts the operand rows the other tiles of the
+// XCD are about to read (measured: a fifth of the time of a 8192 x 18944 x
+// 3584 product).
+constexpr int kStoreNT = 2;
 static_assert(BM == BN && kLoads % 2 == 0 && kLoads / 2 * kWaves * 8 == BM, "load plan");
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
@@ -191,6 +199,104 @@ __device__ __forceinline__ void mma(v16f (&acc)[FB][FA], const Ops& o, const Sca
     }
 }
 
+// Four results in the output format: EB = 4 binary32, EB = 2 bf16 (round to
+// nearest even), packed in 16 or 8 bytes.
+template <int EB>
+struct Quad;
+template <>
+struct Quad<4> {
+    typedef u32x4_t T;
+    static __device__ __forceinline__ T pack(float a, float b, float c, float d) {
+        return u32x4_t{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+    }
+};
+template <>
+struct Quad<2> {
+    typedef u32x2_t T;
+    static __device__ __forceinline__ T pack(float a, float b, float c, float d) {
+        return u32x2_t{to_bf16(a) | (to_bf16(b) << 16), to_bf16(c) | (to_bf16(d) << 16)};
+    }
+};
+
+// Epilogue through LDS, for rows of C that are whole 16-byte units: the tile
+// is written to LDS row-major (in passes of as many rows as 128 KB holds),
+// then stored with each lane moving 16 contiguous bytes, so that a store
+// covers whole cache lines.  In LDS the 4-column group k of row r sits at
+// group k ^ (r % 32): the 32 rows a wave writes at once then fall in distinct
+// banks, and a 16-byte read holds the same two groups, possibly swapped.
+template <int EB>
+__device__ __forceinline__ void store_tile(const v16f (&acc)[FB][FA], uint8_t* lds, Rsrc rc, int wave,
+                                           int wm, int wn, int lane, int64_t rows_a, int64_t n0,
+                                           int64_t N) {
+    constexpr int kPitch = BN * EB;                   // LDS bytes per row
+    constexpr int kRowsPass = 2 * kStageBytes / kPitch;  // 256 (bf16) or 128 (f32)
+    constexpr int kPasses = BM / kRowsPass;
+    constexpr int kRowsInstr = 1024 / kPitch;         // rows per wave-wide 1 KB store
+    constexpr int kInstr = kRowsPass / kRowsInstr / kWaves;
+    typedef typename Quad<EB>::T QT;
+    static_assert(kRowsPass % WM == 0 && kInstr * kRowsInstr * kWaves == kRowsPass, "epilogue plan");
+#pragma unroll
+    for (int h = 0; h < kPasses; ++h) {
+        if (wm * WM / kRowsPass == h) {
+#pragma unroll
+            for (int j = 0; j < FA; ++j) {
+                const int r = wm * WM + j * kFrag + lane % kFrag - h * kRowsPass;
+#pragma unroll
+                for (int i = 0; i < FB; ++i)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int grp = (wn * WN + i * kFrag + 8 * g) / 4 + lane / kFrag;
+                        *reinterpret_cast<QT*>(lds + r * kPitch + (grp ^ (r & 31)) * 4 * EB) =
+                            Quad<EB>::pack(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                           acc[i][j][4 * g + 3]);
+                    }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < kInstr; ++k) {
+            const int r = (wave * kInstr + k) * kRowsInstr + lane / (kPitch / 16);
+            const int q = lane % (kPitch / 16);  // 16-byte unit within the row
+            u32x4_t v;
+            if (EB == 4) {
+                v = *reinterpret_cast<const u32x4_t*>(lds + r * kPitch + ((q ^ (r & 31)) * 16));
+            } else {
+                const int grp = (2 * q) ^ (r & 31);
+                v = *reinterpret_cast<const u32x4_t*>(lds + r * kPitch + (grp >> 1) * 16);
+                if (r & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
+            }
+            const int64_t row = h * kRowsPass + r, col = n0 + q * (16 / EB);
+            const int off = row < rows_a && col < N ? (int)(row * N * EB + col * EB) : kDropped;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, kStoreNT);
+        }
+        if (h + 1 < kPasses) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+}
+
+// Epilogue straight from the accumulators, element by element (rows of C
+// that are not whole 16-byte units).
+__device__ __forceinline__ void store_direct(const v16f (&acc)[FB][FA], Rsrc rc, int ct, int wm, int wn,
+                                             int lane, int64_t rows_a, int64_t n0, int64_t N) {
+    const int eb = ct == 1 ? 4 : 2;
+#pragma unroll
+    for (int j = 0; j < FA; ++j) {
+        const int row = wm * WM + j * kFrag + lane % kFrag;
+#pragma unroll
+        for (int i = 0; i < FB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t col = n0 + wn * WN + i * kFrag + 8 * (r / 4) + 4 * (lane / kFrag) + r % 4;
+                const int off = row < rows_a && col < N ? (int)((row * N + col) * eb) : kDropped;
+                if (ct == 1)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rc, off, 0,
+                                                          kStoreNT);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)to_bf16(acc[i][j][r]), rc, off, 0,
+                                                          kStoreNT);
+            }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes];
     const int lane = threadIdx.x % kWave;
@@ -297,45 +403,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
 
     // Lane l, register r of result (i, j): row m = j * 32 + l % 32 of the wave
     // tile, columns n = i * 32 + 8 (r / 4) + 4 (l / 32) + r % 4.
-    const int eb = p.ct == 1 ? 4 : 2;
-    const Rsrc rc = make_rsrc(static_cast<char*>(p.c) + m0 * p.N * eb, rows_a * p.N * eb);
-    const bool vec = (p.N & 3) == 0;
-#pragma unroll
-    for (int j = 0; j < FA; ++j) {
-        const int row = wm * WM + j * kFrag + lane % kFrag;
-#pragma unroll
-        for (int i = 0; i < FB; ++i) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t col = n0 + wn * WN + i * kFrag + 8 * g + 4 * (lane / kFrag);
-                const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                    acc[i][j][4 * g + 3]};
-                if (vec) {
-                    const int off = row < rows_a && col < p.N ? (int)((row * p.N + col) * eb) : kDropped;
-                    if (p.ct == 1)
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                                    __float_as_uint(v[3])},
-                            rc, off, 0, 0);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b64(
-                            u32x2_t{to_bf16(v[0]) | (to_bf16(v[1]) << 16),
-                                    to_bf16(v[2]) | (to_bf16(v[3]) << 16)},
-                            rc, off, 0, 0);
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int off = row < rows_a && col + r < p.N ? (int)((row * p.N + col + r) * eb)
-                                                                      : kDropped;
-                        if (p.ct == 1)
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), rc, off, 0, 0);
-                        else
-                            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)to_bf16(v[r]), rc, off,
-                                                                  0, 0);
-                    }
-                }
-            }
-        }
+    const Rsrc rc = make_rsrc(static_cast<char*>(p.c) + m0 * p.N * (p.ct == 1 ? 4 : 2),
+                              rows_a * p.N * (p.ct == 1 ? 4 : 2));
+    if (((p.N * (p.ct == 1 ? 4 : 2)) & 15) == 0) {
+        if (p.ct == 1) store_tile<4>(acc, lds, rc, wave, wm, wn, lane, rows_a, n0, p.N);
+        else store_tile<2>(acc, lds, rc, wave, wm, wn, lane, rows_a, n0, p.N);
+    } else {
+        store_direct(acc, rc, p.ct, wm, wn, lane, rows_a, n0, p.N);
     }
 }
 

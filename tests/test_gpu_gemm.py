@@ -6,9 +6,11 @@ Bar: with K <= 256 and scale bytes in [125, 129] every partial sum is exact in
 binary32 (products are multiples of 2^-6 below 2^10, sums below 2^18), so C
 must equal the oracle bit for bit; this pins the operand layout.  Otherwise
 |C - C_oracle| <= (K/128 + 2) * 2^-23 * (|A_hat| |B_hat|^T): one binary32
-rounding per 128-element matrix-core step plus the accumulation, with a
-factor 2 of headroom.  bf16 output is the binary32 result rounded to nearest
-even, checked against the same bound plus half a bf16 ulp.
+rounding (at most 2^-24 of the partial sum) per 64-element matrix-core
+instruction, with a factor 2 of headroom.  bf16 output is the binary32 result
+rounded to nearest even, checked against the same bound plus half a bf16 ulp.
+Shapes cover both epilogues (rows of C in whole 16-byte units, or not), ragged
+M, N and K tails and odd K-stage counts.
 """
 import numpy as np
 import pytest
@@ -68,7 +70,7 @@ def test_gemm_within_bound(m, n, k):
     assert np.all(err <= tol), f"at {i}: got {got[i]!r} want {want[i]!r} tol {tol[i]!r}"
 
 
-@pytest.mark.parametrize("m,n,k", [(96, 160, 512), (130, 158, 384), (70, 90, 96)])
+@pytest.mark.parametrize("m,n,k", [(96, 160, 512), (130, 158, 384), (70, 90, 96), (300, 264, 384)])
 def test_gemm_bf16_output(m, n, k):
     ac, asc = operand(m, k, 44)
     bc, bsc = operand(n, k, 45)
