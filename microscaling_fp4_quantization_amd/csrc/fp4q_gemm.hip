@@ -69,9 +69,12 @@ constexpr int kRowStage = BK / 2;          // code bytes per row per stage (one 
 constexpr int kFrag = 32;                  // rows per matrix-core operand
 constexpr int WM = 128, WN = 64;           // wave tile: rows of A, rows of B
 constexpr int FA = WM / kFrag, FB = WN / kFrag;
-constexpr int kStageBytes = (BM + BN) * kRowStage;
 constexpr int kLoads = (BM + BN) / 8 / kWaves;  // code loads per wave per stage
 constexpr int kPackBytes = 256;            // packed scales per 32-row operand per stage
+constexpr int kCodeBytes = (BM + BN) * kRowStage;  // a stage's codes in LDS (64 KB)
+constexpr int kScaleBytes = (BM + BN) / kFrag * kPackBytes;  // and its scales (4 KB)
+constexpr int kStageBytes = kCodeBytes + kScaleBytes;
+constexpr int kEpiBytes = 2 * kCodeBytes;  // LDS the epilogue stages the tile through
 constexpr int kFmtE2M1 = 4;                // matrix-core operand format: FP4 E2M1
 constexpr int kDropped = (int)0x80000000;  // an offset past every buffer window
 constexpr int kPastWindow = 1 << 30;       // every window is at most 2^30 bytes
@@ -82,6 +85,7 @@ constexpr int kRsrcWord3 = 0x00020000;
 // 3584 product).
 constexpr int kStoreNT = 2;
 static_assert(BM == BN && kLoads % 2 == 0 && kLoads / 2 * kWaves * 8 == BM, "load plan");
+static_assert(BM / kFrag == kWaves, "one scale load per wave per operand");
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
@@ -163,6 +167,25 @@ __device__ __forceinline__ void wait_all_barrier() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Wait until at most N of this wave's loads are in flight, then barrier.  A
+// workgroup fence would wait for all of them (the later stage too).  The wait
+// is the compiler's builtin, so that it knows the scale registers loaded
+// before those N have landed (and adds no wait of its own for them).
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+    static_assert(N >= 0 && N < 16, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt(N), expcnt and lgkmcnt unconstrained
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Wait for this wave's LDS reads, then barrier: afterwards no wave reads the
+// stage buffer any more.  (The compiler's builtin again, so that its own
+// bookkeeping of outstanding LDS reads agrees.)
+__device__ __forceinline__ void lds_reads_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt unconstrained
+    asm volatile("s_barrier" ::: "memory");
+}
+
 struct Ops {
     v4i a[FA], b[FB];
 };
@@ -170,6 +193,18 @@ struct Ops {
 struct Scales {
     uint32_t a[FA], b[FB];
 };
+
+// Scales of a stage from LDS: the packed dwords of the wave's A fragments
+// (wm * FA + j) and B fragments (wn * FB + i), lane l's at 4 l.
+__device__ __forceinline__ void read_scales(Scales& sc, const uint8_t* stage, int wm, int wn, int lane) {
+    const uint8_t* p = stage + kCodeBytes + lane * 4;
+#pragma unroll
+    for (int j = 0; j < FA; ++j)
+        sc.a[j] = *reinterpret_cast<const uint32_t*>(p + (wm * FA + j) * kPackBytes);
+#pragma unroll
+    for (int i = 0; i < FB; ++i)
+        sc.b[i] = *reinterpret_cast<const uint32_t*>(p + (BM / kFrag + wn * FB + i) * kPackBytes);
+}
 
 // Operands of depth T within a stage: lane l takes row l % 32 of each
 // fragment, K block 2 T + l / 32, stored at position (block + row / 2) % 8.
@@ -185,17 +220,15 @@ __device__ __forceinline__ void read_ops(Ops& o, const uint8_t* stage, int a_row
         o.b[i] = *reinterpret_cast<const v4i*>(stage + (BM + b_row + i * kFrag) * kRowStage + at);
 }
 
-template <int T>
-__device__ __forceinline__ void mma(v16f (&acc)[FB][FA], const Ops& o, const Scales& sc) {
+// The 4 instructions of depth T for B fragment I (one per A fragment).
+template <int T, int I>
+__device__ __forceinline__ void mma_half(v16f (&acc)[FB][FA], const Ops& o, const Scales& sc) {
+    const v8i b = v8i{o.b[I][0], o.b[I][1], o.b[I][2], o.b[I][3], 0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < FB; ++i) {
-        const v8i b = v8i{o.b[i][0], o.b[i][1], o.b[i][2], o.b[i][3], 0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < FA; ++j) {
-            const v8i a = v8i{o.a[j][0], o.a[j][1], o.a[j][2], o.a[j][3], 0, 0, 0, 0};
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                b, a, acc[i][j], kFmtE2M1, kFmtE2M1, T, (int)sc.b[i], T, (int)sc.a[j]);
-        }
+    for (int j = 0; j < FA; ++j) {
+        const v8i a = v8i{o.a[j][0], o.a[j][1], o.a[j][2], o.a[j][3], 0, 0, 0, 0};
+        acc[I][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            b, a, acc[I][j], kFmtE2M1, kFmtE2M1, T, (int)sc.b[I], T, (int)sc.a[j]);
     }
 }
 
@@ -229,7 +262,7 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[FB][FA], uint8_t* l
                                            int wm, int wn, int lane, int64_t rows_a, int64_t n0,
                                            int64_t N) {
     constexpr int kPitch = BN * EB;                   // LDS bytes per row
-    constexpr int kRowsPass = 2 * kStageBytes / kPitch;  // 256 (bf16) or 128 (f32)
+    constexpr int kRowsPass = kEpiBytes / kPitch;     // 256 (bf16) or 128 (f32)
     constexpr int kPasses = BM / kRowsPass;
     constexpr int kRowsInstr = 1024 / kPitch;         // rows per wave-wide 1 KB store
     constexpr int kInstr = kRowsPass / kRowsInstr / kWaves;
@@ -299,6 +332,12 @@ __device__ __forceinline__ void store_direct(const v16f (&acc)[FB][FA], Rsrc rc,
 
 __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes];
+    // Fetch the epilogue's arguments now: a scalar load still in flight in
+    // the K loop would force every LDS-read wait there to drain completely
+    // (scalar loads complete out of order on the same counter).
+    void* c_ptr = p.c;
+    int ct = p.ct;
+    asm volatile("" : "+s"(c_ptr), "+s"(ct));
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
@@ -327,30 +366,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
     // for every load of the wave.
     const int blk = ((lane % 8) - 4 * (wave & 1) - lane / 16) & 7;
     const int lane_off = (lane / 8) * rowb + blk * 16;
-    auto issue = [&](uint8_t* stage, int s) {
+    // Offset base of this lane's loads for stage s (past K: an offset past
+    // the window, so zeros).
+    auto dma_base = [&](int s) {
         const int k0 = s * BK;
-        // Past K (this lane's block): an offset past the window, so zeros.
-        const int base = k0 + blk * 32 < K ? lane_off + k0 / 2 : kPastWindow;
-#pragma unroll
-        for (int q = 0; q < kLoads; ++q) {
-            const bool is_a = q < kLoads / 2;
-            const int d = wave + kWaves * (q % (kLoads / 2));
-            const int off = base + 8 * d * rowb;
-            uint8_t* dst = stage + (is_a ? 0 : BM * kRowStage) + d * 8 * kRowStage;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (LdsPtr)dst, 16, off, 0, 0, 0);
-        }
+        return k0 + blk * 32 < K ? lane_off + k0 / 2 : kPastWindow;
     };
-    // Scales of stage s: one dword per lane per fragment (past the last
-    // stage: an offset past the window, so zeros).
-    const int sa_off = wm * FA * pack_frag + lane * 4, sb_off = wn * FB * pack_frag + lane * 4;
-    auto load_scales = [&](Scales& sc, int s) {
-        const int so = s < S ? s * kPackBytes : kPastWindow;
-#pragma unroll
-        for (int j = 0; j < FA; ++j)
-            sc.a[j] = __builtin_amdgcn_raw_buffer_load_b32(rsa, sa_off + j * pack_frag + so, 0, 0);
-#pragma unroll
-        for (int i = 0; i < FB; ++i)
-            sc.b[i] = __builtin_amdgcn_raw_buffer_load_b32(rsb, sb_off + i * pack_frag + so, 0, 0);
+    auto issue_one = [&](uint8_t* stage, int base, int q) {
+        const bool is_a = q < kLoads / 2;
+        const int d = wave + kWaves * (q % (kLoads / 2));
+        uint8_t* dst = stage + (is_a ? 0 : BM * kRowStage) + d * 8 * kRowStage;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (LdsPtr)dst, 16, base + 8 * d * rowb,
+                                                 0, 0, 0);
+    };
+    // Scale loads: load r of wave w moves the packed scales of fragment w of
+    // A (r = 0) or of B (r = 1) for one stage, 256 contiguous bytes.
+    const int sa_off = wave * pack_frag + lane * 4;
+    auto scale_base = [&](int s) { return s < S ? s * kPackBytes : kPastWindow; };
+    auto issue_scale = [&](uint8_t* stage, int base, int r) {
+        uint8_t* dst = stage + kCodeBytes + (r * (BM / kFrag) + wave) * kPackBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r == 0 ? rsa : rsb, (LdsPtr)dst, 4, sa_off + base, 0,
+                                                 0, 0);
     };
 
     v16f acc[FB][FA];
@@ -363,53 +399,94 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
     const int b_row = wn * WN + lane % kFrag;
     const int rot = lane / kFrag + ((lane % kFrag) >> 1);
 
-    // Stage s: codes in buffer s % 2, scales in registers.  Each step first
-    // starts the loads of stage s + 1 (into the buffer stage s - 1 left), then
-    // runs stage s, then waits for stage s + 1 and meets the other waves.
-    // Stages past K load zeros; an odd stage count gets one such stage, which
-    // adds +0 to sums that started at +0 and so changes no bit.
-    const int ns2 = S + (S & 1);
-    Scales sc0, sc1;
-    issue(lds, 0);
-    load_scales(sc0, 0);
-    wait_all_barrier();
-    auto step = [&](int s, const Scales& cur, Scales& nxt) {
-        const uint8_t* here = lds + (s & 1) * kStageBytes;
-        issue(lds + ((s + 1) & 1) * kStageBytes, s + 1);
-        load_scales(nxt, s + 1);
-        Ops o0, o1;
-        read_ops<0>(o0, here, a_row, b_row, rot);
-        __builtin_amdgcn_sched_barrier(0);
-        read_ops<1>(o1, here, a_row, b_row, rot);
-        __builtin_amdgcn_sched_barrier(0);
-        mma<0>(acc, o0, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        read_ops<2>(o0, here, a_row, b_row, rot);
-        __builtin_amdgcn_sched_barrier(0);
-        mma<1>(acc, o1, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        read_ops<3>(o1, here, a_row, b_row, rot);
-        __builtin_amdgcn_sched_barrier(0);
-        mma<2>(acc, o0, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        mma<3>(acc, o1, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_all_barrier();
+    // Stage s lives in LDS buffer s % 2 (codes and packed scales).  Each wave
+    // moves 10 loads per stage: L0..L7 the code loads q0..q7, L8 and L9 the
+    // scale loads of A and B.  Per stage s:
+    //  A  wait for stage s (own loads) and barrier;
+    //     read the scales and the operands of depths 0 and 1; run depths 0
+    //     and 1, reading depths 2 and 3 meanwhile and issuing L5..L9 of stage
+    //     s + 1 (every LDS read of stage s is then issued);
+    //  B  barrier: buffer s % 2 is free.  Run depths 2 and 3, issuing L0..L4
+    //     of stage s + 2 into it.
+    // B sits mid-stage so that the stage's LDS reads (about as long as half
+    // the stage's matrix work) run beside two depths of instructions, and
+    // the loads are spread one or two per 4 instructions, so no wave stalls
+    // on a full load queue.  The loads issued after stage s + 1's last one
+    // are always L0..L4 of stage s + 2, hence vmcnt(5) at A.  Loads of the
+    // stages past the last (S and S + 1) read zeros.
+    auto issue_load = [&](uint8_t* stage, int s, int L) {
+        if (L < kLoads) issue_one(stage, dma_base(s), L);
+        else issue_scale(stage, scale_base(s), L - kLoads);
     };
-    for (int s = 0; s < ns2; s += 2) {
-        step(s, sc0, sc1);
-        step(s + 1, sc1, sc0);
-    }
+    constexpr int kLate = 5;  // loads of a stage issued in the stage before it
+#pragma unroll
+    for (int L = 0; L < kLoads + 2; ++L) issue_load(lds, 0, L);
+#pragma unroll
+    for (int L = 0; L < kLate; ++L) issue_load(lds + kStageBytes, 1, L);
+    auto step = [&](int s) {
+        uint8_t* here = lds + (s & 1) * kStageBytes;
+        uint8_t* other = lds + ((s + 1) & 1) * kStageBytes;
+        wait_loads_barrier<kLate>();
+        Scales sc;
+        Ops r0, r1, r2;
+        // At most 15 LDS reads in flight (the width of the wait counter).
+        read_scales(sc, here, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        read_ops<0>(r0, here, a_row, b_row, rot);
+        __builtin_amdgcn_sched_barrier(0);
+        read_ops<1>(r1, here, a_row, b_row, rot);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_half<0, 0>(acc, r0, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_load(other, s + 1, 5);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_half<0, 1>(acc, r0, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_load(other, s + 1, 6);
+        read_ops<2>(r2, here, a_row, b_row, rot);
+        read_ops<3>(r0, here, a_row, b_row, rot);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_half<1, 0>(acc, r1, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_load(other, s + 1, 7);
+        issue_load(other, s + 1, 8);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_half<1, 1>(acc, r1, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_load(other, s + 1, 9);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_reads_barrier();
+        mma_half<2, 0>(acc, r2, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_load(here, s + 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_half<2, 1>(acc, r2, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_load(here, s + 2, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_half<3, 0>(acc, r0, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_load(here, s + 2, 2);
+        issue_load(here, s + 2, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_half<3, 1>(acc, r0, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_load(here, s + 2, 4);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int s = 0; s < S; ++s) step(s);
+    // The zero stages S and S + 1 are still landing; LDS is reused below.
+    wait_all_barrier();
 
     // Lane l, register r of result (i, j): row m = j * 32 + l % 32 of the wave
     // tile, columns n = i * 32 + 8 (r / 4) + 4 (l / 32) + r % 4.
-    const Rsrc rc = make_rsrc(static_cast<char*>(p.c) + m0 * p.N * (p.ct == 1 ? 4 : 2),
-                              rows_a * p.N * (p.ct == 1 ? 4 : 2));
-    if (((p.N * (p.ct == 1 ? 4 : 2)) & 15) == 0) {
-        if (p.ct == 1) store_tile<4>(acc, lds, rc, wave, wm, wn, lane, rows_a, n0, p.N);
+    const int eb = ct == 1 ? 4 : 2;
+    const Rsrc rc = make_rsrc(static_cast<char*>(c_ptr) + m0 * p.N * eb, rows_a * p.N * eb);
+    if (((p.N * eb) & 15) == 0) {
+        if (ct == 1) store_tile<4>(acc, lds, rc, wave, wm, wn, lane, rows_a, n0, p.N);
         else store_tile<2>(acc, lds, rc, wave, wm, wn, lane, rows_a, n0, p.N);
     } else {
-        store_direct(acc, rc, p.ct, wm, wn, lane, rows_a, n0, p.N);
+        store_direct(acc, rc, ct, wm, wn, lane, rows_a, n0, p.N);
     }
 }
 
