@@ -15,10 +15,10 @@
 // about 1.3x the rate of the 16 x 16 x 128 one.)
 //
 // Two kernels per call:
-//  k_pack_scales  rewrites each operand's scale bytes (1/16 of its size) into
-//                 the order the matrix-core lanes consume them, so that a wave
-//                 fetches a K stage's scales for one 32-row operand with one
-//                 contiguous 256-byte load;
+//  k_pack_scales  rewrites each operand's scale bytes (one per 32 elements) into
+//                 the order the matrix-core lanes consume them, so that a K
+//                 stage's scales for one 32-row operand are one contiguous
+//                 256-byte load;
 //  k_gemm_mxfp4   a workgroup of 8 waves computes a 256 x 256 tile of C; K
 //                 advances 256 at a time through two LDS stages.
 //
@@ -99,28 +99,43 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
 // to the instruction of depth t within the stage.  Rows and blocks that do not
 // exist get byte 0 (their codes are read as +0, so the product is +0).
 //
-// One thread per (fragment, stage, fragment row): it reads the row's 8 scale
-// bytes of the stage and writes the dwords of lanes r and r + 32.
-__global__ __launch_bounds__(256) void k_pack_scales(const uint8_t* __restrict__ sc, int64_t rows,
-                                                     int64_t kblocks, int64_t stages, int64_t frags,
-                                                     uint32_t* __restrict__ out) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= frags * stages * kFrag) return;
-    const int r = (int)(idx % kFrag);
-    const int64_t s = (idx / kFrag) % stages, f = idx / (kFrag * stages);
-    const int64_t row = f * kFrag + r;
-    uint32_t even = 0, odd = 0;
+// One workgroup per (fragment, run of 16 stages): it copies the fragment's
+// 32 rows x 128 scale bytes of those stages into LDS (each row's bytes are
+// contiguous in memory), then writes the 16 x 256 packed bytes, which are
+// contiguous too.
+constexpr int kPackStages = 16;
+constexpr int kPackThreads = 256;
+
+__global__ __launch_bounds__(kPackThreads) void k_pack_scales(const uint8_t* __restrict__ sc,
+                                                              int64_t rows, int64_t kblocks,
+                                                              int64_t stages, int64_t frags,
+                                                              uint32_t* __restrict__ out) {
+    __shared__ uint8_t tile[kFrag][kPackStages * 8 + 4];  // padded rows
+    const int64_t runs = (stages + kPackStages - 1) / kPackStages;
+    const int64_t f = blockIdx.x / runs;
+    const int64_t s0 = (blockIdx.x % runs) * kPackStages;
+    const int t = threadIdx.x;
+    // Load: thread t moves row t / 8, bytes 16 (t % 8) .. + 15 of the run.
+    {
+        const int r = t / 8, c0 = (t % 8) * 16;
+        const int64_t row = f * kFrag + r;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int64_t b = 8 * s + 2 * t;
-        const uint32_t lo = row < rows && b < kblocks ? sc[row * kblocks + b] : 0u;
-        const uint32_t hi = row < rows && b + 1 < kblocks ? sc[row * kblocks + b + 1] : 0u;
-        even |= lo << (8 * t);
-        odd |= hi << (8 * t);
+        for (int c = 0; c < 16; ++c) {
+            const int64_t b = 8 * s0 + c0 + c;
+            tile[r][c0 + c] = row < rows && b < kblocks ? sc[row * kblocks + b] : (uint8_t)0;
+        }
     }
-    uint32_t* dst = out + (f * stages + s) * (kPackBytes / 4);
-    dst[r] = even;
-    dst[r + kFrag] = odd;
+    __syncthreads();
+    // Store: dword d of the run is lane d % 64 of stage s0 + d / 64: row
+    // d % 32, bytes of blocks 2 u + (d % 64) / 32, u = 0..3.
+    const int n_st = (int)(stages - s0 < kPackStages ? stages - s0 : kPackStages);
+    uint32_t* dst = out + (f * stages + s0) * (kPackBytes / 4);
+    for (int d = t; d < n_st * 64; d += kPackThreads) {
+        const int st = d / 64, lane = d % 64, r = lane % kFrag, h = lane / kFrag;
+        const uint8_t* src = &tile[r][st * 8 + h];
+        dst[d] = (uint32_t)src[0] | ((uint32_t)src[2] << 8) | ((uint32_t)src[4] << 16) |
+                 ((uint32_t)src[6] << 24);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -507,7 +522,7 @@ int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
     uint8_t* b_pack = a_pack + frags_of(j.M) * S * kPackBytes;
     const int64_t kb = j.K / 32;
     const int64_t tiles = ((j.M + BM - 1) / BM) * ((j.N + BN - 1) / BN);
-    if (tiles > INT32_MAX || (frags_of(j.M) + frags_of(j.N)) * S * kFrag / 256 > INT32_MAX) {
+    if (tiles > INT32_MAX || (frags_of(j.M) + frags_of(j.N)) * ((S + kPackStages - 1) / kPackStages) > INT32_MAX) {
         snprintf(msg, msg_len, "gemm: %lld x %lld x %lld needs more workgroups than one launch holds",
                  (long long)j.M, (long long)j.N, (long long)j.K);
         return (int)hipErrorInvalidConfiguration;
@@ -518,10 +533,10 @@ int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
         uint8_t* out;
     } packs[2] = {{j.a_scales, j.M, a_pack}, {j.b_scales, j.N, b_pack}};
     for (const auto& pk : packs) {
-        const int64_t threads = frags_of(pk.rows) * S * kFrag;
-        if (threads == 0) continue;
-        hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                           pk.sc, pk.rows, kb, S, frags_of(pk.rows), reinterpret_cast<uint32_t*>(pk.out));
+        const int64_t groups = frags_of(pk.rows) * ((S + kPackStages - 1) / kPackStages);
+        if (groups == 0) continue;
+        hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)groups), dim3(kPackThreads), 0, stream, pk.sc,
+                           pk.rows, kb, S, frags_of(pk.rows), reinterpret_cast<uint32_t*>(pk.out));
     }
     GParams p{j.a_codes, j.b_codes, a_pack, b_pack, j.M, j.N, j.K, S, j.c, j.ct};
     hipLaunchKernelGGL(k_gemm_mxfp4, dim3((unsigned)tiles), dim3(kThreads), 0, stream, p);
