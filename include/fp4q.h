@@ -245,11 +245,16 @@ fp4q_status hadamard_block_rotate(const void* x, int32_t xt, int64_t rows, int64
  *   ws, ws_bytes        device scratch of at least
  *                       fp4_gemm_workspace_bytes(M, N, K) bytes, 16-byte
  *                       aligned (not needed when M, N or K is 0): the scales
- *                       repacked in matrix-core order.  Owned by the caller;
- *                       calls that overlap in time need distinct workspaces.
+ *                       repacked in matrix-core order and, for products with
+ *                       too few 256 x 256 tiles to fill the chip (small M),
+ *                       the binary32 partial products of K ranges.  Owned by
+ *                       the caller; calls that overlap in time need distinct
+ *                       workspaces.
  * Products of E2M1 values and E8M0 scales are exact; the matrix cores add them
- * in binary32 in 64-element steps, so C differs from the exact product by
- * rounding of order (K/64 + 1) * 2^-24 of sum |a| |b|.  Errors: FP4Q_ERR_SHAPE
+ * in binary32 in 64-element steps (partial products of K ranges are added in
+ * binary64 and rounded once), so C differs from the exact product by rounding
+ * of order (K/64 + 1) * 2^-24 of sum |a| |b|.  Results are the same on every
+ * run for a given shape.  Errors: FP4Q_ERR_SHAPE
  * (sizes), FP4Q_ERR_ARG (NULL operand or c, bad ct), FP4Q_ERR_ALIGN,
  * FP4Q_ERR_WORKSPACE, FP4Q_ERR_HIP (launch failure); nothing is launched on
  * an error other than FP4Q_ERR_HIP.
@@ -259,7 +264,9 @@ fp4q_status fp4_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            int32_t ct, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes fp4_gemm_mxfp4 needs for an M x N x K product: 256 *
- * (ceil(M/32) + ceil(N/32)) * ceil(K/256); 0 when M, N or K is 0. */
+ * (ceil(M/32) + ceil(N/32)) * ceil(K/256), rounded up to 256, plus
+ * 4 * M * N per K range when K is split (a function of M, N and K only);
+ * 0 when M, N or K is 0. */
 size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Workspace size in bytes for any call on a rows x cols tensor (a constant

@@ -48,6 +48,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <algorithm>
+
 #include "fp4q_launch.h"
 
 namespace fp4q {
@@ -151,6 +153,8 @@ struct GParams {
     int64_t S;              // K stages, ceil(K / 256)
     void* c;
     int ct;                 // 0 bf16, 1 f32
+    int splits;             // K ranges per tile (1: C directly)
+    float* partial;         // splits > 1: binary32 partial products, splits x M x N
 };
 
 // Round-to-nearest-even binary32 -> bf16 bits.
@@ -352,14 +356,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
     // the K loop would force every LDS-read wait there to drain completely
     // (scalar loads complete out of order on the same counter).
     void* c_ptr = p.c;
+    float* partial = p.partial;
     int ct = p.ct;
-    asm volatile("" : "+s"(c_ptr), "+s"(ct));
+    asm volatile("" : "+s"(c_ptr), "+s"(partial), "+s"(ct));
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
     const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    // Workgroup g computes K range `split` of tile g / splits.
+    const int splits = p.splits, split = (int)(blockIdx.x % splits);
     int64_t tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    tile_of(blockIdx.x / splits, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = tm * BM, n0 = tn * BN;
     const int64_t rows_a = p.M - m0 < BM ? p.M - m0 : BM;
     const int64_t rows_b = p.N - n0 < BN ? p.N - n0 : BN;
@@ -370,6 +377,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
     // offset below fits 32 bits: K <= 2^23, so S <= 2^15 and a window is at
     // most 2^30 bytes.
     const int K = (int)p.K, S = (int)p.S;
+    const int per = (S + splits - 1) / splits;  // stages of each K range
+    const int s_lo = split * per, s_hi = s_lo + per < S ? s_lo + per : S;
     const int pack_frag = S * kPackBytes;
     const int64_t fa = (rows_a + kFrag - 1) / kFrag, fb = (rows_b + kFrag - 1) / kFrag;
     const Rsrc rsa = make_rsrc(p.a_pack + (m0 / kFrag) * pack_frag, fa * pack_frag);
@@ -382,11 +391,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
     // for every load of the wave.
     const int blk = ((lane % 8) - 4 * (wave & 1) - lane / 16) & 7;
     const int lane_off = (lane / 8) * rowb + blk * 16;
-    // Offset base of this lane's loads for stage s (past K: an offset past
-    // the window, so zeros).
+    // Offset base of this lane's loads for stage s (past K or past this
+    // workgroup's K range: an offset past the window, so zeros).
     auto dma_base = [&](int s) {
         const int k0 = s * BK;
-        return k0 + blk * 32 < K ? lane_off + k0 / 2 : kPastWindow;
+        // One compare against a limit that is 0 past the range (a select of
+        // the limit, not of the compare, so that no branch splits the loop).
+        const int klim = s < s_hi ? K : 0;
+        return k0 + blk * 32 < klim ? lane_off + k0 / 2 : kPastWindow;
     };
     auto issue_one = [&](uint8_t* stage, int base, int q) {
         const bool is_a = q < kLoads / 2;
@@ -398,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
     // Scale loads: load r of wave w moves the packed scales of fragment w of
     // A (r = 0) or of B (r = 1) for one stage, 256 contiguous bytes.
     const int sa_off = wave * pack_frag + lane * 4;
-    auto scale_base = [&](int s) { return s < S ? s * kPackBytes : kPastWindow; };
+    auto scale_base = [&](int s) { return s < s_hi ? s * kPackBytes : kPastWindow; };
     auto issue_scale = [&](uint8_t* stage, int base, int r) {
         uint8_t* dst = stage + kCodeBytes + (r * (BM / kFrag) + wave) * kPackBytes;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r == 0 ? rsa : rsb, (LdsPtr)dst, 4, sa_off + base, 0,
@@ -429,16 +441,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
     // the loads are spread one or two per 4 instructions, so no wave stalls
     // on a full load queue.  The loads issued after stage s + 1's last one
     // are always L0..L4 of stage s + 2, hence vmcnt(5) at A.  Loads of the
-    // stages past the last (S and S + 1) read zeros.
+    // two stages past the workgroup's range read zeros.
     auto issue_load = [&](uint8_t* stage, int s, int L) {
         if (L < kLoads) issue_one(stage, dma_base(s), L);
         else issue_scale(stage, scale_base(s), L - kLoads);
     };
     constexpr int kLate = 5;  // loads of a stage issued in the stage before it
 #pragma unroll
-    for (int L = 0; L < kLoads + 2; ++L) issue_load(lds, 0, L);
+    for (int L = 0; L < kLoads + 2; ++L) issue_load(lds + (s_lo & 1) * kStageBytes, s_lo, L);
 #pragma unroll
-    for (int L = 0; L < kLate; ++L) issue_load(lds + kStageBytes, 1, L);
+    for (int L = 0; L < kLate; ++L) issue_load(lds + ((s_lo + 1) & 1) * kStageBytes, s_lo + 1, L);
     auto step = [&](int s) {
         uint8_t* here = lds + (s & 1) * kStageBytes;
         uint8_t* other = lds + ((s + 1) & 1) * kStageBytes;
@@ -490,9 +502,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
         issue_load(here, s + 2, 4);
         __builtin_amdgcn_sched_barrier(0);
     };
-    for (int s = 0; s < S; ++s) step(s);
-    // The zero stages S and S + 1 are still landing; LDS is reused below.
+    for (int s = s_lo; s < s_hi; ++s) step(s);
+    // The zero stages past the range are still landing; LDS is reused below.
     wait_all_barrier();
+
+    if (splits > 1) {
+        // Binary32 partial product of this K range, reduced by k_splitk_reduce.
+        float* part = partial + (int64_t)split * p.M * p.N;
+        const Rsrc rp = make_rsrc(part + m0 * p.N, rows_a * p.N * 4);
+        if (((p.N * 4) & 15) == 0) store_tile<4>(acc, lds, rp, wave, wm, wn, lane, rows_a, n0, p.N);
+        else store_direct(acc, rp, 1, wm, wn, lane, rows_a, n0, p.N);
+        return;
+    }
 
     // Lane l, register r of result (i, j): row m = j * 32 + l % 32 of the wave
     // tile, columns n = i * 32 + 8 (r / 4) + 4 (l / 32) + r % 4.
@@ -508,11 +529,90 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
 
 int64_t frags_of(int64_t rows) { return (rows + kFrag - 1) / kFrag; }
 
+// C = sum over the K ranges of their binary32 partial products, added in
+// binary64 in range order and rounded once to binary32 (then to bf16 for a
+// bf16 C): one rounding more than the accumulation's own, the same for every
+// run.  Four elements per thread, grid-stride.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partial, int splits,
+                                                       int64_t count, void* c, int ct) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+    for (int64_t e0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; e0 < count; e0 += stride) {
+        const int n = count - e0 < 4 ? (int)(count - e0) : 4;
+        double s[4] = {0.0, 0.0, 0.0, 0.0};
+        if (n == 4 && (count & 3) == 0) {
+            // Groups of 8 ranges: their loads issue together, the adds stay
+            // in range order.
+            for (int i0 = 0; i0 < splits; i0 += 8) {
+                float4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (i0 + u < splits)
+                        v[u] = *reinterpret_cast<const float4*>(partial + (int64_t)(i0 + u) * count + e0);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (i0 + u < splits) {
+                        s[0] += v[u].x;
+                        s[1] += v[u].y;
+                        s[2] += v[u].z;
+                        s[3] += v[u].w;
+                    }
+            }
+        } else {
+            for (int i = 0; i < splits; ++i)
+                for (int q = 0; q < n; ++q) s[q] += partial[(int64_t)i * count + e0 + q];
+        }
+        for (int q = 0; q < n; ++q) {
+            const float f = (float)s[q];
+            if (ct == 1) static_cast<float*>(c)[e0 + q] = f;
+            else static_cast<uint16_t*>(c)[e0 + q] = (uint16_t)to_bf16(f);
+        }
+    }
+}
+
+// K ranges per tile.  When the tiles alone fill less than two waves of
+// workgroups over the chip (256 CUs, one workgroup each), K is split so that
+// the modelled time -- rounds of workgroups x (stages per range + 2 for the
+// prologue and epilogue), plus the partial products' round trip through
+// memory -- is least.  A function of the shape only, so that the workspace
+// size is too.
+constexpr int kChipGroups = 256;
+constexpr double kStageBytes_Mem = 6.75e6;   // bytes of memory traffic in one stage's time
+constexpr int64_t kMaxPartialBytes = (int64_t)1 << 28;
+
+int splits_for(int64_t M, int64_t N, int64_t K) {
+    const int64_t S = (K + BK - 1) / BK;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (S < 2 || tiles >= 2 * kChipGroups || N * 4 >= ((int64_t)1 << 23)) return 1;
+    auto cost = [&](int64_t sp) {
+        const int64_t per = (S + sp - 1) / sp;
+        const int64_t rounds = (tiles * sp + kChipGroups - 1) / kChipGroups;
+        return (double)(rounds * (per + 2)) + (sp > 1 ? (double)sp * M * N * 8 / kStageBytes_Mem : 0.0);
+    };
+    int64_t best = 1;
+    double best_cost = cost(1);
+    for (int64_t sp = 2; sp <= S && sp <= 64; ++sp) {
+        const int64_t per = (S + sp - 1) / sp;
+        const int64_t eff = (S + per - 1) / per;  // ranges that are not empty
+        if (eff != sp || sp * M * N * 4 > kMaxPartialBytes) continue;
+        const double c = cost(sp);
+        if (c < best_cost) {
+            best_cost = c;
+            best = sp;
+        }
+    }
+    return (int)best;
+}
+
+int64_t packed_bytes(int64_t M, int64_t N, int64_t K) {
+    return (frags_of(M) + frags_of(N)) * ((K + BK - 1) / BK) * kPackBytes;
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    const int64_t S = (K + BK - 1) / BK;
-    return (size_t)((frags_of(M) + frags_of(N)) * S * kPackBytes);
+    const int sp = splits_for(M, N, K);
+    const int64_t packed = (packed_bytes(M, N, K) + 255) / 256 * 256;
+    return (size_t)(packed + (sp > 1 ? (int64_t)sp * M * N * 4 : 0));
 }
 
 int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
@@ -539,8 +639,17 @@ int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
         hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)groups), dim3(kPackThreads), 0, stream, pk.sc,
                            pk.rows, kb, S, frags_of(pk.rows), reinterpret_cast<uint32_t*>(pk.out));
     }
-    GParams p{j.a_codes, j.b_codes, a_pack, b_pack, j.M, j.N, j.K, S, j.c, j.ct};
-    hipLaunchKernelGGL(k_gemm_mxfp4, dim3((unsigned)tiles), dim3(kThreads), 0, stream, p);
+    const int sp = splits_for(j.M, j.N, j.K);
+    float* partial = reinterpret_cast<float*>(static_cast<uint8_t*>(j.ws) +
+                                              (packed_bytes(j.M, j.N, j.K) + 255) / 256 * 256);
+    GParams p{j.a_codes, j.b_codes, a_pack, b_pack, j.M, j.N, j.K, S, j.c, j.ct, sp, partial};
+    hipLaunchKernelGGL(k_gemm_mxfp4, dim3((unsigned)(tiles * sp)), dim3(kThreads), 0, stream, p);
+    if (sp > 1) {
+        const int64_t count = j.M * j.N;
+        const int64_t groups = std::min<int64_t>((count + 1023) / 1024, 8192);
+        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)groups), dim3(256), 0, stream, partial, sp,
+                           count, j.c, j.ct);
+    }
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) return 0;
     snprintf(msg, msg_len, "gemm kernel launch: %s", hipGetErrorString(e));

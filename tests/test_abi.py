@@ -138,11 +138,24 @@ def test_gemm_validation(L):
 
 
 def test_gemm_workspace_bytes(L):
+    """Packed scales: 256 B per 32-row fragment of A and B per 256-wide K stage,
+    padded to 256 B; then, when K is split into ranges, one binary32 M x N
+    partial product per range (at most one range per stage)."""
     wb = L.fp4_gemm_workspace_bytes
     assert wb(0, 5, 64) == 0 and wb(5, 5, 0) == 0
     assert wb(1, 1, 32) == 2 * 256
-    assert wb(33, 64, 257 * 32) == (2 + 2) * 33 * 256
-    assert wb(8192, 18944, 3584) == (256 + 592) * 14 * 256
+    assert wb(8192, 18944, 3584) == (256 + 592) * 14 * 256   # enough tiles: no split
+    for m, n, k in [(33, 64, 257 * 32), (1, 18944, 3584), (16, 3584, 18944), (300, 517, 384),
+                    (256, 18944, 3584), (1024, 18944, 3584)]:
+        stages = -(-k // 256)
+        packed = -(-((-(-m // 32) + -(-n // 32)) * stages * 256) // 256) * 256
+        extra = wb(m, n, k) - packed
+        assert extra >= 0 and extra % (m * n * 4) == 0, (m, n, k)
+        splits = extra // (m * n * 4)
+        assert splits == 0 or 2 <= splits <= stages, (m, n, k, splits)
+    # Decode-sized products split K; a full-chip one does not.
+    assert wb(1, 18944, 3584) > (1 + 592) * 14 * 256
+    assert wb(1024, 18944, 3584) == (32 + 592) * 14 * 256
 
 
 def test_other_entry_points_validation(L):

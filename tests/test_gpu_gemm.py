@@ -57,8 +57,12 @@ def test_gemm_exact_when_sums_are_exact(m, n, k):
     np.testing.assert_array_equal(got, want.astype(np.float32))
 
 
+# Most of these split K into ranges (few tiles): the partial products are
+# summed in binary64 and rounded once, which the bound already covers.
 @pytest.mark.parametrize("m,n,k", [(1, 1, 32), (64, 512, 4096), (200, 333, 1056), (128, 256, 3584),
-                                   (33, 1000, 8192), (300, 517, 384), (520, 300, 512), (777, 1031, 1152)])
+                                   (33, 1000, 8192), (300, 517, 384), (520, 300, 512), (777, 1031, 1152),
+                                   (1, 300, 2048), (16, 1000, 4096), (5, 520, 1056), (33, 260, 8192),
+                                   (3, 257, 2048)])
 def test_gemm_within_bound(m, n, k):
     ac, asc = operand(m, k, [42, m, k])
     bc, bsc = operand(n, k, [43, n, k])
@@ -70,7 +74,8 @@ def test_gemm_within_bound(m, n, k):
     assert np.all(err <= tol), f"at {i}: got {got[i]!r} want {want[i]!r} tol {tol[i]!r}"
 
 
-@pytest.mark.parametrize("m,n,k", [(96, 160, 512), (130, 158, 384), (70, 90, 96), (300, 264, 384)])
+@pytest.mark.parametrize("m,n,k", [(96, 160, 512), (130, 158, 384), (70, 90, 96), (300, 264, 384),
+                                   (7, 264, 3072), (9, 131, 1024)])
 def test_gemm_bf16_output(m, n, k):
     ac, asc = operand(m, k, 44)
     bc, bsc = operand(n, k, 45)
@@ -105,3 +110,38 @@ def test_gemm_qwen7_up_projection_sampled_columns():
     want = oracle.gemm_mxfp4(ac, asc, bc, bsc, m, len(cols), k)
     tol = bound(ac, asc, bc, bsc, m, len(cols), k)
     assert np.all(np.abs(got[:, cols] - want) <= tol)
+
+
+def sampled(m, n, k, seeds, cols, out_dtype=torch.float32, w=None):
+    """The kernel computes the whole m x n product, the oracle `cols` sampled
+    output columns of it."""
+    ac, asc = operand(m, k, seeds[0], spread=2)
+    if w is None:
+        bc, bsc = operand(n, k, seeds[1], spread=2)
+    else:
+        wq = oracle.quantize(w, oracle.FMT_MXFP4, 32)
+        bc, bsc = wq["codes"], wq["scales"]
+    got = run(ac, asc, bc, bsc, out_dtype)
+    sel = np.sort(np.random.default_rng(seeds[2]).choice(n, cols, replace=False))
+    want = oracle.gemm_mxfp4(ac, asc, bc[sel], bsc[sel], m, len(sel), k)
+    tol = bound(ac, asc, bc[sel], bsc[sel], m, len(sel), k)
+    if out_dtype == torch.bfloat16:
+        tol = tol + np.abs(want) * 2.0 ** -8
+    err = np.abs(got[:, sel] - want)
+    i = np.unravel_index(np.argmax(err - tol), err.shape)
+    assert np.all(err <= tol), f"at {i}: got {got[:, sel][i]!r} want {want[i]!r} tol {tol[i]!r}"
+
+
+def test_gemm_many_tiles_bf16_sampled():
+    """2048 x 2048 x 512 in bf16: enough tiles that K is not split."""
+    print("  case 2048x2048x512 bf16", flush=True)
+    sampled(2048, 2048, 512, (48, 49, 50), 64, torch.bfloat16)
+
+
+def test_gemm_decode_down_projection_sampled():
+    """16 tokens x 18944 times the 3584 x 18944 down-projection: few tiles and
+    a long K, the split-K path at a decode shape."""
+    import fp4_workloads as wl
+    print("  case 16x3584x18944", flush=True)
+    w = wl.qwen7_mlp(1, 1).float().numpy()
+    sampled(16, 3584, 18944, (51, None, 52), 48, w=w)
