@@ -57,24 +57,121 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GB/s of bf16 input quantized+packed+MSE'd (MXFP4/NVFP4); % of HBM peak"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "microscaling_fp4_quantization_amd", "csrc", "fp4q_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_nvfp4_qwen7_traffic.json")
+CSRC = os.path.join(ROOT, "microscaling_fp4_quantization_amd", "csrc")
+# Per workload: the roofline kernel's source file and its committed traffic record.
+TRAFFIC = {
+    "qwen7": (os.path.join(CSRC, "fp4q_kernels.hip"),
+              os.path.join(ROOT, "profiles", "quantize_nvfp4_qwen7_traffic.json")),
+    "gemm": (os.path.join(CSRC, "fp4q_gemm.hip"),
+             os.path.join(ROOT, "profiles", "gemm_mxfp4_qwen7_traffic.json")),
+}
 
 
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(workload="qwen7") -> str:
+    return hashlib.sha256(open(TRAFFIC[workload][0], "rb").read()).hexdigest()[:16]
 
 
-def read_traffic():
+def read_traffic(workload="qwen7"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(TRAFFIC[workload][1]))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(workload):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+# What one roofline "launch" is in each workload's counter runs: the kernels
+# of one call (name fragment, grid size in work items or None for any), the
+# bytes of the calibration copy, and the call's algorithmic bytes.
+def _traffic_plan(workload):
+    if workload == "qwen7":
+        n = 18944 * 3584
+        return {"parts": [("k_quantize<0, 1, 16, 0, true, false, false>", None)],
+                "label": "k_quantize<bf16, UE, 16, no rotation, err, no sumsq> (one launch)",
+                "calib_bytes": n * 2, "alg_bytes": int(n * (2 + 0.5 + 1 / 16 + 4 / 16)),
+                "run": "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibration-copy"}
+    if workload == "gemm":
+        T, H, I = GEMM_TOKENS, 3584, 18944
+        tiles = -(-T // 256) * -(-I // 256)
+        return {"parts": [("k_gemm_mxfp4", tiles * 512), ("k_pack_scales", -(-T // 32) * 256),
+                          ("k_pack_scales", -(-I // 32) * 256)],
+                "label": "fp4_gemm_mxfp4 up projection 8192x18944x3584: k_gemm_mxfp4 + 2 k_pack_scales",
+                "calib_bytes": I * H // 2,
+                "alg_bytes": T * H // 2 + T * H // 32 + I * H // 2 + I * H // 32 + T * I * 2,
+                "run": "python -u bench.py --workload gemm --steps 2 --warmup 1 --no-cpu-baseline "
+                       "--calibration-copy"}
+    raise SystemExit(f"no traffic plan for workload {workload}")
+
+
+def write_traffic(workload, fetch_dir, write_dir):
+    """Turn two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; csv output, -o
+    run) into the workload's traffic record and summary under profiles/.
+    The counters read KiB per dispatch; each is scaled by what it reads for
+    the calibration copy (the last `copyBuffer` dispatch) of known size."""
+    import csv
+    plan = _traffic_plan(workload)
+
+    def load(d, counter):
+        out = []
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if r["Counter_Name"] == counter:
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]),
+                            float(r["Counter_Value"])))
+        return out
+
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = load(d, counter)
+        copies = [r for r in rows if "copyBuffer" in r[1]]
+        if not copies:
+            raise SystemExit(f"{d}: no calibration copy dispatch")
+        calib_kib = max(copies)[3]
+        parts = []
+        for frag, grid in plan["parts"]:
+            vals = [r[3] for r in rows if frag in r[1] and (grid is None or r[2] == grid)]
+            if not vals:
+                raise SystemExit(f"{d}: no dispatch of {frag} (grid {grid})")
+            parts.append((frag, grid, len(vals), sum(vals) / len(vals)))
+        res[counter] = (calib_kib, parts)
+    f_cal, f_parts = res["FETCH_SIZE"]
+    w_cal, w_parts = res["WRITE_SIZE"]
+    f_scale = plan["calib_bytes"] / (f_cal * 1024)
+    w_scale = plan["calib_bytes"] / (w_cal * 1024)
+    f_kib = sum(p[3] for p in f_parts)
+    w_kib = sum(p[3] for p in w_parts)
+    hbm = int(round(f_kib * 1024 * f_scale + w_kib * 1024 * w_scale))
+    src, out_json = TRAFFIC[workload]
+    cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/traffic_{workload}/{c} -o run -- "
+            + plan["run"] for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    rec = {"kernel": plan["label"], "kernel_source_sha256_16": kernel_source_hash(workload),
+           "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": plan["alg_bytes"],
+           "commands": cmds}
+    json.dump(rec, open(out_json, "w"), indent=1)
+    lines = [f"# HBM traffic per launch: bench.py workload `{workload}`", "",
+             "Commands (from the repository root on the MI355X box), one counter per run, then",
+             f"`python bench.py --workload {workload} --write-traffic gpurun_out/traffic_{workload}"
+             f"/FETCH_SIZE gpurun_out/traffic_{workload}/WRITE_SIZE` to write this file:", "", "```",
+             *cmds, "```", "",
+             f"The calibration copy moves {plan['calib_bytes']:,} bytes each way; the counters read "
+             f"{f_cal:,.1f} KiB (fetch) and {w_cal:,.1f} KiB (write) for it, so the scales are "
+             f"x{f_scale:.4f} (fetch) and x{w_scale:.4f} (write).", "",
+             "| kernel | grid (work items) | dispatches | FETCH_SIZE KiB (mean) | WRITE_SIZE KiB (mean) |",
+             "|---|---|---|---|---|"]
+    for fp, wp in zip(f_parts, w_parts):
+        lines.append(f"| `{fp[0]}` | {fp[1] if fp[1] else 'any'} | {fp[2]} | {fp[3]:,.1f} | {wp[3]:,.1f} |")
+    lines += ["", f"Per launch ({plan['label']}): {f_kib * 1024 * f_scale / 1e6:.2f} MB read and "
+                  f"{w_kib * 1024 * w_scale / 1e6:.2f} MB written, {hbm / 1e6:.2f} MB in all, against "
+                  f"{plan['alg_bytes'] / 1e6:.2f} MB algorithmic (ratio {hbm / plan['alg_bytes']:.4f}).  "
+                  f"Taken on kernel source sha256[:16] = {rec['kernel_source_sha256_16']} "
+                  f"({os.path.relpath(src, ROOT)}); bench.py reports this traffic only while the "
+                  "source is unchanged."]
+    open(out_json[:-5] + ".md", "w").write("\n".join(lines) + "\n")
+    print(json.dumps(rec))
 
 
 # ------------------------------------------------------------------ workloads
@@ -291,9 +388,14 @@ def gemm_main(args, steps, warmup):
                                       "input_GBps": round(acts[a].numel() * 2 / (ms * 1e-3) / 1e9, 1)}
     up = breakdown["gemm_up"]
     achieved = flops["up"] / (up["us_per_call"] * 1e-6) / 1e12
+    if args.calibration_copy:
+        src = weights["up"][0]
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP4_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP4_PEAK_TFLOPS, 4),
-                "traffic": None,
+                "traffic": read_traffic("gemm"),
                 "kernel": "fp4_gemm_mxfp4 up projection (k_pack_scales x2 + k_gemm_mxfp4)",
                 "us_per_launch": up["us_per_call"], "algorithmic_flops_per_launch": flops["up"]}
     line = {
@@ -512,7 +614,13 @@ def main():
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain device copy of the first tensor (a kernel of "
                          "known traffic, for scaling rocprofv3 byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the workload's traffic record under profiles/ from two "
+                         "rocprofv3 counter runs, then exit (no GPU needed)")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.workload, *args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by rows with one max- and one sum-all-reduce; see DESIGN.md)",
