@@ -690,7 +690,7 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
         else cw = code_word_f32(v, sc);
         if constexpr (ERR) {
             decode_word(cw, sc, xh);
-            xh_m = requant_mx(m, sc);
+            if (p.so.stats) xh_m = requant_mx(m, sc);
         }
     } else {
         const UeScale s = ue_scale<FMT>(m, ue.D, ue.rD, ue.s_fast_max, ue.tab);
@@ -708,9 +708,11 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
             decode_word(cw, 1.0f, xh);
 #pragma unroll
             for (int i = 0; i < 8; ++i) xh[i] = xh[i] * s.d;
-            xh_m = 6.0f * s.d;  // the decoded code 6, as for the elements
-            if (__builtin_amdgcn_ballot_w64(!s.six)) {
-                if (!s.six) xh_m = requant_ue(m, s);
+            if (p.so.stats) {
+                xh_m = 6.0f * s.d;  // the decoded code 6, as for the elements
+                if (__builtin_amdgcn_ballot_w64(!s.six)) {
+                    if (!s.six) xh_m = requant_ue(m, s);
+                }
             }
         }
     }
@@ -739,9 +741,12 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
                                                   gl == 0 ? blk * 4 : kDropped, 0, kStNt);
         }
         // Zero-filled lanes past the end form all-zero blocks, which add 0 to
-        // every term and are not zero-rounded (m = 0).
-        const double em = (double)(m - xh_m);
-        add_block(acc, (m > 0.0f) && (xh_m == 0.0f), sse, em * em, ss);
+        // every term and are not zero-rounded (m = 0).  Without tensor stats
+        // the terms are not formed at all (a wave-uniform branch).
+        if (p.so.stats) {
+            const double em = (double)(m - xh_m);
+            add_block(acc, (m > 0.0f) && (xh_m == 0.0f), sse, em * em, ss);
+        }
     }
 }
 
@@ -790,7 +795,7 @@ __device__ __forceinline__ void search_chunk(const Raw<XT>& raw, int u, const QO
             const float sc = __uint_as_float((uint32_t)cb << 23);
             cw = code_word_f32(v, sc);
             decode_word(cw, sc, xh);
-            xm = requant_mx(m, sc);
+            xm = p.so.stats ? requant_mx(m, sc) : 0.0f;
         } else {
             const float4 e = ue.tab[cb];
             UeScale s;
@@ -811,7 +816,7 @@ __device__ __forceinline__ void search_chunk(const Raw<XT>& raw, int u, const QO
             decode_word(cw, 1.0f, xh);
 #pragma unroll
             for (int i = 0; i < 8; ++i) xh[i] = xh[i] * s.d;
-            xm = requant_ue(m, s);
+            xm = p.so.stats ? requant_ue(m, s) : 0.0f;
         }
         double sse = 0.0;
 #pragma unroll
@@ -843,8 +848,10 @@ __device__ __forceinline__ void search_chunk(const Raw<XT>& raw, int u, const QO
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mse), o.mse,
                                               gl == 0 ? blk * 4 : kDropped, 0, kStNt);
     }
-    const double em = (double)(m - best_xm);
-    add_block(acc, (m > 0.0f) && (best_xm == 0.0f), best, em * em, ss);
+    if (p.so.stats) {
+        const double em = (double)(m - best_xm);
+        add_block(acc, (m > 0.0f) && (best_xm == 0.0f), best, em * em, ss);
+    }
 }
 
 // g = RN32(amax / 2688) (1 when that is not positive) from the amax pass's
@@ -1537,13 +1544,17 @@ struct Split {
     int64_t cpw;
 };
 
-// Fixed ranges of `cpw` chunks per wave when that grid fits the workspace's
-// partial slots, else the balanced one-round split.
+// cpw > 0: fixed ranges of `cpw` chunks per wave (short-lived workgroups that
+// the dispatcher hands out in order), more per wave where the tensor would
+// otherwise need more workgroups than the workspace has partial slots.
+// cpw = 0: the balanced one-round split.  cpw < 0: the one-round sweep.
 Split split_for(int64_t chunks, const void* kernel, int cpw, int waves = kWaves) {
     if (cpw < 0) return {grid_for_chunks(chunks, kernel, waves), cpw};
     if (cpw > 0) {
-        const int64_t G = (chunks + (int64_t)waves * cpw - 1) / ((int64_t)waves * cpw);
-        if (G <= kMaxGroups) return {(int)G, cpw};
+        const int64_t min_cpw = (chunks + (int64_t)waves * kMaxGroups - 1) / ((int64_t)waves * kMaxGroups);
+        const int64_t c = cpw > min_cpw ? cpw : min_cpw;
+        const int64_t G = (chunks + (int64_t)waves * c - 1) / ((int64_t)waves * c);
+        return {(int)(G > 0 ? G : 1), c};
     }
     return {grid_for_chunks(chunks, kernel, waves), 0};
 }
