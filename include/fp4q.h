@@ -250,6 +250,9 @@ fp4q_status hadamard_block_rotate(const void* x, int32_t xt, int64_t rows, int64
  *                       the binary32 partial products of K ranges.  Owned by
  *                       the caller; calls that overlap in time need distinct
  *                       workspaces.
+ * Decode-sized products (M <= 32, K % 128 == 0, both scale arrays 4-byte
+ * aligned) run a kernel that streams B once, 32 rows of B per wave, with the
+ * same arithmetic contract below; other shapes run the 256 x 256 tile kernel.
  * Products of E2M1 values and E8M0 scales are exact; the matrix cores add them
  * in binary32 in 64-element steps (partial products of K ranges are added in
  * binary64 and rounded once), so C differs from the exact product by rounding
@@ -265,8 +268,9 @@ fp4q_status fp4_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, cons
 
 /* Workspace bytes fp4_gemm_mxfp4 needs for an M x N x K product: 256 *
  * (ceil(M/32) + ceil(N/32)) * ceil(K/256), rounded up to 256, plus
- * 4 * M * N per K range when K is split (a function of M, N and K only);
- * 0 when M, N or K is 0. */
+ * 4 * M * N per K range when K is split (the larger of the two kernels'
+ * range counts, so a function of M, N and K only, whatever the alignment of
+ * the scale arrays); 0 when M, N or K is 0. */
 size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Workspace size in bytes for any call on a rows x cols tensor (a constant

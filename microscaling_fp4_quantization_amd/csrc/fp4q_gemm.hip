@@ -15,13 +15,17 @@
 // SIMD, as here, this shape sustained 6.3 PFLOP/s on MI355X where the
 // 16 x 16 x 128 one sustained 5.4, for the same operand bytes per flop.)
 //
-// Two kernels per call:
+// Kernels:
 //  k_pack_scales  rewrites each operand's scale bytes (one per 32 elements) into
 //                 the order the matrix-core lanes consume them, so that a K
 //                 stage's scales for one 32-row operand are one contiguous
 //                 256-byte load;
 //  k_gemm_mxfp4   a workgroup of 8 waves computes a 256 x 256 tile of C; K
-//                 advances 256 at a time through two LDS stages.
+//                 advances 256 at a time through two LDS stages;
+//  k_gemm_decode  products of at most 32 rows of A: one pass over B, 32 rows of
+//                 B and a range of K per wave (no scale packing);
+//  k_splitk_reduce  adds the binary32 partial products of K ranges when a
+//                 product is split along K.
 //
 // Operand codes go from memory to LDS by direct buffer-to-LDS loads (no
 // register staging).  A wave-wide `buffer_load_dwordx4 ... lds` writes its 64
@@ -529,6 +533,193 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
 
 int64_t frags_of(int64_t rows) { return (rows + kFrag - 1) / kFrag; }
 
+// ---------------------------------------------------------------------------
+// Decode-sized products: M <= 32 rows of A (a batch of tokens), any N and K.
+// The product is a pass over B, so the work is cut into units of one 32-row
+// fragment of B and one range of K segments (256 elements each), one unit per
+// wave; the waves of a workgroup share nothing but the launch.  A unit
+// streams its segments through three LDS buffers of its own (two segments in
+// flight while the third is read): B's 32 rows and A's rows (8 AR of them,
+// AR = ceil(M / 8); the others read a zero slot) by direct buffer-to-LDS
+// loads, 8 rows x 128 bytes per instruction, rotated as in the tile kernel,
+// and each operand's 32 rows x 8 scale bytes by one dword-wide direct load
+// (so the scale rows must start on 4-byte boundaries: K a multiple of 128 and
+// both scale arrays 4-byte aligned; other shapes take the tile kernel).
+//
+// Within a segment the instruction of depth t takes from lane l (row l % 32,
+// half h = l / 32) the 16 bytes 64 h + 16 t of the row's 128, i.e. the
+// 32-element block 4 h + t of the segment, for both operands alike: every
+// K block meets its partner once, so the sum is the same dot product, and a
+// lane's four scale bytes for the segment are consecutive (one LDS dword,
+// byte t for depth t).
+//
+// A unit ends with a 32 x 32 binary32 tile (rows of B by rows of A).  With
+// one K range per fragment it is C; otherwise it is the range's partial
+// product, and k_splitk_reduce adds the ranges in binary64 and rounds once.
+#ifndef FP4Q_DEC_WAVES
+#define FP4Q_DEC_WAVES 4
+#endif
+#ifndef FP4Q_DEC_BUFS
+#define FP4Q_DEC_BUFS 3
+#endif
+constexpr int kDecWaves = FP4Q_DEC_WAVES;  // units per workgroup
+constexpr int kDecBufs = FP4Q_DEC_BUFS;    // LDS buffers per unit
+constexpr int kDecMaxM = 32;
+
+template <int AR>
+struct DecLayout {
+    static constexpr int kB = kFrag * kRowStage;       // B codes, 4 KB
+    static constexpr int kA = AR * 8 * kRowStage;      // A codes
+    static constexpr int kBs = kFrag * 8;              // B scale bytes
+    static constexpr int kAs = kFrag * 8;              // A scale bytes
+    static constexpr int kBuf = kB + kA + kBs + kAs;
+    static constexpr int kZero = kDecBufs * kBuf;      // 16 zero bytes
+    static constexpr int kUnit = kZero + 16;
+    static constexpr int kLoads = 4 + AR + 2;          // direct loads per segment
+    static_assert(kBuf % 16 == 0 && (kDecBufs - 1) * kLoads < 64, "decode layout");
+};
+
+struct DecParams {
+    const uint8_t* a_codes;
+    const uint8_t* a_scales;
+    const uint8_t* b_codes;
+    const uint8_t* b_scales;
+    int64_t M, N, K;
+    int S;           // K segments, ceil(K / 256)
+    int splits;      // K ranges per fragment
+    int64_t units;   // fragments of B x splits
+    void* c;         // splits == 1
+    int ct;          // 0 bf16, 1 f32
+    float* partial;  // splits > 1: splits x M x N binary32
+};
+
+// s_waitcnt vmcnt(N) for N < 64 (the count's high bits sit at bits 14-15),
+// expcnt and lgkmcnt unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Depth T of a segment: scale byte T of each lane's dword.
+template <int T>
+__device__ __forceinline__ v16f mma_dec(v16f acc, v4i b, v4i a, int sb, int sa) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v8i{b[0], b[1], b[2], b[3], 0, 0, 0, 0},
+                                                           v8i{a[0], a[1], a[2], a[3], 0, 0, 0, 0}, acc,
+                                                           kFmtE2M1, kFmtE2M1, T, sb, T, sa);
+}
+
+template <int AR>
+__global__ __launch_bounds__(kDecWaves * kWave) void k_gemm_decode(DecParams p) {
+    typedef DecLayout<AR> L;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kDecWaves * L::kUnit];
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t unit = (int64_t)blockIdx.x * kDecWaves + wave;
+    if (unit >= p.units) return;  // the whole wave; no workgroup barrier follows
+    const int splits = p.splits, split = (int)(unit % splits);
+    const int64_t n0 = unit / splits * kFrag;
+    const int64_t rows_b = p.N - n0 < kFrag ? p.N - n0 : kFrag;
+    const int rowb = (int)(p.K / 2), kb = (int)(p.K / 32), S = p.S;
+    const int per = (S + splits - 1) / splits;
+    const int s_lo = split * per, s_hi = s_lo + per < S ? s_lo + per : S;
+    // Windows: this fragment's rows of B, all M rows of A (rows past them read
+    // zeros).  Every offset fits 32 bits: K <= 2^23 and at most 32 rows.
+    const Rsrc rb = make_rsrc(p.b_codes + n0 * rowb, rows_b * rowb);
+    const Rsrc ra = make_rsrc(p.a_codes, p.M * rowb);
+    const Rsrc rbs = make_rsrc(p.b_scales + n0 * kb, rows_b * kb);
+    const Rsrc ras = make_rsrc(p.a_scales, p.M * kb);
+    uint8_t* base = lds + wave * L::kUnit;
+    *reinterpret_cast<u32x4_t*>(base + L::kZero) = u32x4_t{0u, 0u, 0u, 0u};  // lanes write the same zeros
+
+    // Direct loads.  Code instruction q moves rows 8 q .. 8 q + 7: lane l
+    // fetches row 8 q + l / 8 into LDS slot l % 8 of that row, which holds
+    // the row's 16-byte piece (l % 8 - row / 2) mod 8; row / 2 = 4 q + l / 16.
+    // The scale instruction of an operand moves its 32 rows' 8 bytes of the
+    // segment, dword l % 2 of row l / 2 per lane.  Pieces and blocks past K
+    // (or segments past the unit's range) take an offset past the window:
+    // zeros.
+    const int crow = lane / 8, cslot = lane % 8;
+    auto issue = [&](int s, uint8_t* buf) {
+        const int klim = s < s_hi ? rowb : 0;
+        const int slim = s < s_hi ? kb : 0;
+#pragma unroll
+        for (int q = 0; q < 4 + AR; ++q) {
+            const bool is_b = q < 4;
+            const int qq = is_b ? q : q - 4;
+            const int piece = (cslot - 4 * (qq & 1) - lane / 16) & 7;
+            const int pos = 128 * s + 16 * piece;
+            const int off = pos < klim ? (8 * qq + crow) * rowb + pos : kDropped;
+            uint8_t* dst = buf + (is_b ? 0 : L::kB) + qq * 8 * kRowStage;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_b ? rb : ra, (LdsPtr)dst, 16, off, 0, 0, 0);
+        }
+        const int spos = 8 * s + 4 * (lane % 2);
+        const int soff = spos < slim ? (lane / 2) * kb + spos : kDropped;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (LdsPtr)(buf + L::kB + L::kA), 4, soff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (LdsPtr)(buf + L::kB + L::kA + L::kBs), 4, soff, 0, 0, 0);
+    };
+
+    // Reads: lane l takes row r = l % 32, half h = l / 32; depth t's piece
+    // 4 h + t sits in slot (4 h + t + r / 2) mod 8.  A rows past 8 AR read the
+    // zero slot.
+    const int r = lane % kFrag, h = lane / kFrag;
+    const bool a_real = r < 8 * AR;
+    constexpr int kAhead = kDecBufs - 1;  // segments in flight while one is read
+    v16f acc = {};
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) issue(s_lo + i, base + i * L::kBuf);
+    int cur = 0;
+    for (int s = s_lo; s < s_hi; ++s) {
+        const int nxt = cur == 0 ? kAhead : cur - 1;  // (cur + kAhead) mod kDecBufs
+        issue(s + kAhead, base + nxt * L::kBuf);
+        wait_vm<kAhead * L::kLoads>();
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* buf = base + cur * L::kBuf;
+        v4i bo[4], ao[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int slot = (4 * h + t + r / 2) & 7;
+            bo[t] = *reinterpret_cast<const v4i*>(buf + r * kRowStage + 16 * slot);
+            ao[t] = *reinterpret_cast<const v4i*>(a_real ? buf + L::kB + r * kRowStage + 16 * slot
+                                                         : base + L::kZero);
+        }
+        const int sb = *reinterpret_cast<const int*>(buf + L::kB + L::kA + r * 8 + 4 * h);
+        const int sa = *reinterpret_cast<const int*>(buf + L::kB + L::kA + L::kBs + r * 8 + 4 * h);
+        acc = mma_dec<0>(acc, bo[0], ao[0], sb, sa);
+        acc = mma_dec<1>(acc, bo[1], ao[1], sb, sa);
+        acc = mma_dec<2>(acc, bo[2], ao[2], sb, sa);
+        acc = mma_dec<3>(acc, bo[3], ao[3], sb, sa);
+        __builtin_amdgcn_sched_barrier(0);
+        cur = cur == kAhead ? 0 : cur + 1;
+    }
+    wait_vm<0>();  // the trailing (empty) loads, before the wave's LDS is left
+
+    // Register e of lane l: row of B 8 (e / 4) + 4 h + e % 4, row of A l % 32.
+    const int64_t m = lane % kFrag;
+    if (splits == 1) {
+        const int eb = p.ct == 1 ? 4 : 2;
+        const Rsrc rc = make_rsrc(p.c, p.M * p.N * eb);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t n = n0 + 8 * (e / 4) + 4 * h + e % 4;
+            const int off = m < p.M && n < p.N ? (int)((m * p.N + n) * eb) : kDropped;
+            if (p.ct == 1)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[e]), rc, off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)to_bf16(acc[e]), rc, off, 0, 0);
+        }
+    } else {
+        const Rsrc rp = make_rsrc(p.partial + split * p.M * p.N, p.M * p.N * 4);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t n = n0 + 8 * (e / 4) + 4 * h + e % 4;
+            const int off = m < p.M && n < p.N ? (int)((m * p.N + n) * 4) : kDropped;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[e]), rp, off, 0, 0);
+        }
+    }
+}
+
+
 // C = sum over the K ranges of their binary32 partial products, added in
 // binary64 in range order and rounded once to binary32 (then to bf16 for a
 // bf16 C): one rounding more than the accumulation's own, the same for every
@@ -607,18 +798,91 @@ int64_t packed_bytes(int64_t M, int64_t N, int64_t K) {
     return (frags_of(M) + frags_of(N)) * ((K + BK - 1) / BK) * kPackBytes;
 }
 
+// The decode kernel takes products of at most 32 rows of A whose scale rows
+// start on 4-byte boundaries.  Its K ranges per fragment of B: one (C is
+// written directly) when the fragments alone give half of kDecUnits units;
+// else enough for about kDecUnits units, each range at least two segments,
+// all ranges non-empty, the partials within kMaxPartialBytes.  The reduction
+// is a second launch, which costs about as much as doubling the units gains
+// (measured on Qwen2.5-7B projections: 18944 x 3584 weights are fastest
+// with 592 units and no split, 3584 x 18944 with 8 ranges, 896 units).  A
+// function of the shape only.
+#ifndef FP4Q_DEC_UNITS
+#define FP4Q_DEC_UNITS 896
+#endif
+constexpr int64_t kDecUnits = FP4Q_DEC_UNITS;
+constexpr int64_t kDecMaxSplits = 16;
+
+bool decode_shape(int64_t M, int64_t K) { return M <= kDecMaxM && K % 128 == 0; }
+
+int decode_splits(int64_t M, int64_t N, int64_t K) {
+    const int64_t S = (K + BK - 1) / BK, F = frags_of(N);
+    if (2 * F >= kDecUnits) return 1;
+    int64_t sp = (kDecUnits + F - 1) / F;
+    if (sp > S / 2) sp = S / 2;
+    if (sp > kDecMaxSplits) sp = kDecMaxSplits;
+    while (sp > 1 && sp * M * N * 4 > kMaxPartialBytes) --sp;
+    if (sp < 2) return 1;
+    const int64_t per = (S + sp - 1) / sp;
+    return (int)((S + per - 1) / per);
+}
+
+// Partial products in the workspace, after the packed scales: the larger of
+// the two kernels' needs, so that the size depends on the shape only.
+int workspace_splits(int64_t M, int64_t N, int64_t K) {
+    const int tile = splits_for(M, N, K);
+    const int dec = decode_shape(M, K) ? decode_splits(M, N, K) : 1;
+    const int sp = tile > dec ? tile : dec;
+    return sp > 1 ? sp : 0;
+}
+
+template <int AR>
+void launch_decode_ar(const DecParams& p, unsigned groups, hipStream_t stream) {
+    hipLaunchKernelGGL(k_gemm_decode<AR>, dim3(groups), dim3(kDecWaves * kWave), 0, stream, p);
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    const int sp = splits_for(M, N, K);
     const int64_t packed = (packed_bytes(M, N, K) + 255) / 256 * 256;
-    return (size_t)(packed + (sp > 1 ? (int64_t)sp * M * N * 4 : 0));
+    return (size_t)(packed + (int64_t)workspace_splits(M, N, K) * M * N * 4);
 }
 
 int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
     if (j.M == 0 || j.N == 0) return 0;
     const hipStream_t stream = static_cast<hipStream_t>(j.stream);
     const int64_t S = (j.K + BK - 1) / BK;
+    float* partial_area = reinterpret_cast<float*>(static_cast<uint8_t*>(j.ws) +
+                                                   (packed_bytes(j.M, j.N, j.K) + 255) / 256 * 256);
+    if (decode_shape(j.M, j.K) && reinterpret_cast<uintptr_t>(j.a_scales) % 4 == 0 &&
+        reinterpret_cast<uintptr_t>(j.b_scales) % 4 == 0) {
+        const int sp = decode_splits(j.M, j.N, j.K);
+        const int64_t units = frags_of(j.N) * sp;
+        const int64_t groups = (units + kDecWaves - 1) / kDecWaves;
+        if (groups > INT32_MAX) {
+            snprintf(msg, msg_len, "gemm: %lld x %lld x %lld needs more workgroups than one launch holds",
+                     (long long)j.M, (long long)j.N, (long long)j.K);
+            return (int)hipErrorInvalidConfiguration;
+        }
+        const DecParams p{j.a_codes, j.a_scales, j.b_codes, j.b_scales, j.M, j.N, j.K, (int)S, sp, units,
+                          j.c, j.ct, partial_area};
+        switch ((j.M + 7) / 8) {
+            case 1: launch_decode_ar<1>(p, (unsigned)groups, stream); break;
+            case 2: launch_decode_ar<2>(p, (unsigned)groups, stream); break;
+            case 3: launch_decode_ar<3>(p, (unsigned)groups, stream); break;
+            default: launch_decode_ar<4>(p, (unsigned)groups, stream); break;
+        }
+        if (sp > 1) {
+            const int64_t count = j.M * j.N;
+            const int64_t rg = std::min<int64_t>((count + 1023) / 1024, 8192);
+            hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)rg), dim3(256), 0, stream, partial_area, sp,
+                               count, j.c, j.ct);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e == hipSuccess) return 0;
+        snprintf(msg, msg_len, "gemm decode kernel launch: %s", hipGetErrorString(e));
+        return (int)e;
+    }
     uint8_t* a_pack = static_cast<uint8_t*>(j.ws);
     uint8_t* b_pack = a_pack + frags_of(j.M) * S * kPackBytes;
     const int64_t kb = j.K / 32;
@@ -640,8 +904,7 @@ int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
                            pk.rows, kb, S, frags_of(pk.rows), reinterpret_cast<uint32_t*>(pk.out));
     }
     const int sp = splits_for(j.M, j.N, j.K);
-    float* partial = reinterpret_cast<float*>(static_cast<uint8_t*>(j.ws) +
-                                              (packed_bytes(j.M, j.N, j.K) + 255) / 256 * 256);
+    float* partial = partial_area;
     GParams p{j.a_codes, j.b_codes, a_pack, b_pack, j.M, j.N, j.K, S, j.c, j.ct, sp, partial};
     hipLaunchKernelGGL(k_gemm_mxfp4, dim3((unsigned)(tiles * sp)), dim3(kThreads), 0, stream, p);
     if (sp > 1) {

@@ -6,12 +6,11 @@
 // spans L = b / 8 lanes of one wavefront and a 64-lane wave covers a 512-element
 // chunk with perfectly coalesced loads and 4-byte code stores.  Block maxima and
 // error sums are reduced across the L lanes with DPP quad permutes and row
-// mirrors; nothing goes through LDS on the hot path.  The grid is one round of
-// resident workgroups; each wave owns one contiguous run of chunks (all runs
-// within one chunk of the same length), takes kUnroll chunks per iteration
-// with every load issued before any use, and the runs are numbered so that
-// each XCD streams one contiguous eighth of the tensor.  Memory is reached
-// through range-checked buffer resources, so ragged ends need no branches.
+// mirrors; nothing goes through LDS on the hot path.  Waves take groups of
+// chunks with every load of a group issued before any use (the split between
+// waves is chosen per kernel, see wave_range), numbered so that each XCD
+// streams one contiguous part of the tensor.  Memory is reached through
+// range-checked buffer resources, so ragged ends need no branches.
 //
 // Arithmetic (the rules the pages leave open are stated in include/fp4q.h):
 //   MXFP4: the E8M0 byte is the block maximum's binary32 exponent field minus 2

@@ -10,7 +10,10 @@ rounding (at most 2^-24 of the partial sum) per 64-element matrix-core
 instruction, with a factor 2 of headroom.  bf16 output is the binary32 result
 rounded to nearest even, checked against the same bound plus half a bf16 ulp.
 Shapes cover both epilogues (rows of C in whole 16-byte units, or not), ragged
-M, N and K tails and odd K-stage counts.
+M, N and K tails and odd K-stage counts, and both kernels: products of at
+most 32 rows of A with K a multiple of 128 and 4-byte-aligned scale arrays
+take the decode kernel (one K range per fragment of B, or several added by
+the reduction), the others the tile kernel.
 """
 import numpy as np
 import pytest
@@ -62,7 +65,8 @@ def test_gemm_exact_when_sums_are_exact(m, n, k):
 @pytest.mark.parametrize("m,n,k", [(1, 1, 32), (64, 512, 4096), (200, 333, 1056), (128, 256, 3584),
                                    (33, 1000, 8192), (300, 517, 384), (520, 300, 512), (777, 1031, 1152),
                                    (1, 300, 2048), (16, 1000, 4096), (5, 520, 1056), (33, 260, 8192),
-                                   (3, 257, 2048)])
+                                   (3, 257, 2048), (20, 520, 1024), (32, 264, 1024), (25, 33, 384),
+                                   (12, 600, 128), (32, 15000, 512)])
 def test_gemm_within_bound(m, n, k):
     ac, asc = operand(m, k, [42, m, k])
     bc, bsc = operand(n, k, [43, n, k])
@@ -75,7 +79,7 @@ def test_gemm_within_bound(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(96, 160, 512), (130, 158, 384), (70, 90, 96), (300, 264, 384),
-                                   (7, 264, 3072), (9, 131, 1024)])
+                                   (7, 264, 3072), (9, 131, 1024), (3, 200, 256), (17, 15000, 768)])
 def test_gemm_bf16_output(m, n, k):
     ac, asc = operand(m, k, 44)
     bc, bsc = operand(n, k, 45)
@@ -145,3 +149,32 @@ def test_gemm_decode_down_projection_sampled():
     print("  case 16x3584x18944", flush=True)
     w = wl.qwen7_mlp(1, 1).float().numpy()
     sampled(16, 3584, 18944, (51, None, 52), 48, w=w)
+
+
+def test_gemm_decode_up_projection_sampled():
+    """8 tokens x 3584 times the 18944 x 3584 up-projection: enough fragments
+    of B that the decode kernel writes C directly (no K split)."""
+    import fp4_workloads as wl
+    print("  case 8x18944x3584", flush=True)
+    w = wl.qwen7_mlp(0, 1).float().numpy()
+    sampled(8, 18944, 3584, (53, None, 54), 64, torch.bfloat16, w=w)
+
+
+def test_gemm_decode_unaligned_scales():
+    """Scale arrays that do not start on a 4-byte boundary send a decode-sized
+    product to the tile kernel; both must meet the bound, on the same data."""
+    m, n, k = 6, 300, 1024
+    ac, asc = operand(m, k, 55)
+    bc, bsc = operand(n, k, 56)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    want = oracle.gemm_mxfp4(ac, asc, bc, bsc, m, n, k)
+    tol = bound(ac, asc, bc, bsc, m, n, k)
+    outs = []
+    for shift in (0, 1):
+        sa = torch.zeros(asc.size + shift, dtype=torch.uint8, device=DEV)
+        sb = torch.zeros(bsc.size + shift, dtype=torch.uint8, device=DEV)
+        sa[shift:] = t(asc).reshape(-1)
+        sb[shift:] = t(bsc).reshape(-1)
+        got = fq.fp4_gemm_mxfp4(t(ac), sa[shift:].view(m, k // 32), t(bc), sb[shift:].view(n, k // 32))
+        outs.append(got.cpu().numpy())
+        assert np.all(np.abs(outs[-1] - want) <= tol), shift
