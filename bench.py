@@ -663,7 +663,9 @@ def main():
         # computed), per-block MSE and no stats, a call launches exactly one
         # kernel: the same k_quantize instantiation the step runs (in the dynamic
         # mode the amax pass supplies sum x^2, so the step's quantize kernel omits
-        # it too).
+        # it too).  The step's launches also form the tensor terms and reduce the
+        # amax partials, so they run on the one-round grid; these run on
+        # short-lived workgroups, and skip the tensor-term arithmetic.
         reps = max(10, steps)
         run.step(given=True)
         us_launch = time_region(torch, stream, lambda: run.step(given=True), reps) * 1e3 / len(xs)

@@ -85,10 +85,23 @@ constexpr int kAmaxUnroll = FP4Q_AUNROLL;   // ... of the amax pre-pass
 #define FP4Q_GRID_ROUNDS 1
 #endif
 constexpr int kMinChunksPerWave = FP4Q_MIN_CHUNKS_PER_WAVE;
-// Chunks per wave of the fixed split (0 = balanced one-round split) for the
-// quantize, amax and other streaming kernels.
+// Work split of the streaming kernels (see split_for): chunks per wave of
+// short-lived workgroups (> 0), the balanced one-round split (0) or the
+// one-round sweep (< 0).  Launches that leave per-workgroup partials (tensor
+// stats) or reduce the amax pass in every workgroup (dynamic g) take the
+// one-round grid: with short-lived workgroups those would be repeated by
+// thousands of workgroups (measured: NVFP4 with stats 45 -> 54 us per 67.9 M
+// elements).  UE-scale quantization, dequantization, rotation and block MSE
+// without them take short-lived workgroups, which the dispatcher hands out in
+// order as slots free up (interleaved medians on 67.9 M elements, two boxes:
+// NVFP4 with per-block MSE 36.0-39.0 -> 34.8-35.4 us, fp32 dequantization
+// 88.9 -> 80.1, rotation 97.4 -> 84.6, block MSE 40.3 -> 37.1); MXFP4
+// quantization keeps the sweep (codes only: 31.2 against 33.2 us).
 #ifndef FP4Q_QCPW
 #define FP4Q_QCPW -1
+#endif
+#ifndef FP4Q_QCPW_LIGHT
+#define FP4Q_QCPW_LIGHT 4
 #endif
 #ifndef FP4Q_ACPW
 #define FP4Q_ACPW 8
@@ -96,7 +109,11 @@ constexpr int kMinChunksPerWave = FP4Q_MIN_CHUNKS_PER_WAVE;
 #ifndef FP4Q_SCPW
 #define FP4Q_SCPW 0
 #endif
-constexpr int kQuantCpw = FP4Q_QCPW, kAmaxCpw = FP4Q_ACPW, kStreamCpw = FP4Q_SCPW;
+#ifndef FP4Q_SCPW_LIGHT
+#define FP4Q_SCPW_LIGHT 4
+#endif
+constexpr int kQuantCpw = FP4Q_QCPW, kQuantCpwLight = FP4Q_QCPW_LIGHT, kAmaxCpw = FP4Q_ACPW;
+constexpr int kStreamCpw = FP4Q_SCPW, kStreamCpwLight = FP4Q_SCPW_LIGHT;
 // The amax pre-pass has no per-workgroup set-up, so it runs larger workgroups
 // of short-lived waves: fewer per-workgroup maxima for the quantize kernel to
 // reduce at the same wave count.
@@ -1785,7 +1802,8 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
                              : pick_quant_block<1, kFmtUe4m3>(j.block, j.rotate, err, sumsq, search))
                 : (j.xt == 0 ? pick_quant_block<0, kFmtUe5m3>(j.block, j.rotate, err, sumsq, search)
                              : pick_quant_block<1, kFmtUe5m3>(j.block, j.rotate, err, sumsq, search));
-    const Split sq = split_for(chunks, reinterpret_cast<const void*>(k), kQuantCpw);
+    const bool light = j.stats == nullptr && !dynamic && j.fmt != kFmtMx;
+    const Split sq = split_for(chunks, reinterpret_cast<const void*>(k), light ? kQuantCpwLight : kQuantCpw);
     const int G = sq.G;
     p.cpw = sq.cpw;
     int G_amax = 0;
@@ -1826,7 +1844,7 @@ int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len) {
     else
         k = j.ot == 1 ? pick_dequant_block<kFmtUe4m3, 1>(j.block, j.rotate)
                       : pick_dequant_block<kFmtUe4m3, 0>(j.block, j.rotate);
-    const Split sp = split_for(chunks, reinterpret_cast<const void*>(k), kStreamCpw);
+    const Split sp = split_for(chunks, reinterpret_cast<const void*>(k), kStreamCpwLight);
     p.cpw = sp.cpw;
     hipLaunchKernelGGL(k, dim3(sp.G), dim3(kThreads), 0, st, p);
     return report(hipGetLastError(), "dequantize kernel launch", msg, msg_len);
@@ -1867,7 +1885,8 @@ int launch_block_mse(const MseJob& j, char* msg, size_t msg_len) {
     else
         k = j.xt == 0 ? pick_mse_block<0, kFmtUe4m3>(j.block, j.rotate, sumsq)
                       : pick_mse_block<1, kFmtUe4m3>(j.block, j.rotate, sumsq);
-    const Split sp = split_for(chunks, reinterpret_cast<const void*>(k), kStreamCpw);
+    const Split sp = split_for(chunks, reinterpret_cast<const void*>(k),
+                               j.stats == nullptr ? kStreamCpwLight : kStreamCpw);
     const int G = sp.G;
     p.cpw = sp.cpw;
     hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
@@ -1884,7 +1903,7 @@ int launch_rotate(const RotateJob& j, char* msg, size_t msg_len) {
     void (*k)(RParams);
     if (j.xt == 0) k = j.rotate == 16 ? k_rotate<0, 16> : k_rotate<0, 32>;
     else k = j.rotate == 16 ? k_rotate<1, 16> : k_rotate<1, 32>;
-    const Split sp = split_for(chunks, reinterpret_cast<const void*>(k), kStreamCpw);
+    const Split sp = split_for(chunks, reinterpret_cast<const void*>(k), kStreamCpwLight);
     p.cpw = sp.cpw;
     hipLaunchKernelGGL(k, dim3(sp.G), dim3(kThreads), 0, st, p);
     return report(hipGetLastError(), "rotate kernel launch", msg, msg_len);
