@@ -345,8 +345,13 @@ def gemm_main(args, steps, warmup):
     prods = [("gate", "x"), ("up", "x"), ("down", "h")]
     outs = {n: torch.empty((T, weights[n][0].shape[0]), dtype=torch.bfloat16, device=dev)
             for n, _ in prods}
-    need = max(fq.lib().fp4_gemm_workspace_bytes(T, weights[n][0].shape[0], acts[a].shape[1])
-               for n, a in prods)
+    # Decode-sized products (a few tokens against the same weights) for the
+    # breakdown: the first rows of the quantized activations.
+    decode = [(tok, n, a) for tok in (1, 16) for n, a in (("up", "x"), ("down", "h"))]
+    need = max([fq.lib().fp4_gemm_workspace_bytes(T, weights[n][0].shape[0], acts[a].shape[1])
+                for n, a in prods] +
+               [fq.lib().fp4_gemm_workspace_bytes(tok, weights[n][0].shape[0], acts[a].shape[1])
+                for tok, n, a in decode])
     ws = fq.gemm_workspace(dev, need)
     flops = {n: 2.0 * T * weights[n][0].shape[0] * acts[a].shape[1] for n, a in prods}
 
@@ -381,6 +386,19 @@ def gemm_main(args, steps, warmup):
         breakdown[f"gemm_{n}"] = {"shape_MxNxK": f"{T}x{weights[n][0].shape[0]}x{acts[a].shape[1]}",
                                   "us_per_call": round(ms * 1e3, 2),
                                   "TFLOPs": round(flops[n] / (ms * 1e-3) / 1e12, 1)}
+    for tok, n, a in decode:
+        wc, wsc = weights[n]
+        cd = torch.empty((tok, wc.shape[0]), dtype=torch.bfloat16, device=dev)
+        fn = lambda tok=tok, n=n, a=a, cd=cd: fq.fp4_gemm_mxfp4(
+            qa[a].codes[:tok], qa[a].scales[:tok], weights[n][0], weights[n][1], torch.bfloat16,
+            out=cd, ws=ws)
+        fn()
+        ms = time_region(torch, stream, fn, max(50, steps))
+        wbytes = wc.numel() + wsc.numel()
+        breakdown[f"decode_{n}_{tok}tok"] = {
+            "shape_MxNxK": f"{tok}x{wc.shape[0]}x{acts[a].shape[1]}",
+            "us_per_call": round(ms * 1e3, 2),
+            "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1)}
     for a in ("x", "h"):
         ms = time_region(torch, stream, lambda a=a: quantize(a), reps)
         breakdown[f"quantize_{a}"] = {"shape": "x".join(map(str, acts[a].shape)),

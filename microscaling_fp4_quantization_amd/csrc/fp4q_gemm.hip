@@ -537,7 +537,8 @@ int64_t frags_of(int64_t rows) { return (rows + kFrag - 1) / kFrag; }
 // Decode-sized products: M <= 32 rows of A (a batch of tokens), any N and K.
 // The product is a pass over B, so the work is cut into units of one 32-row
 // fragment of B and one range of K segments (256 elements each), one unit per
-// wave; the waves of a workgroup share nothing but the launch.  A unit
+// wave; the waves of a workgroup (4, or 1 when A has more than 8 rows) share
+// nothing but the launch.  A unit
 // streams its segments through three LDS buffers of its own (two segments in
 // flight while the third is read): B's 32 rows and A's rows (8 AR of them,
 // AR = ceil(M / 8); the others read a zero slot) by direct buffer-to-LDS
@@ -556,14 +557,15 @@ int64_t frags_of(int64_t rows) { return (rows + kFrag - 1) / kFrag; }
 // A unit ends with a 32 x 32 binary32 tile (rows of B by rows of A).  With
 // one K range per fragment it is C; otherwise it is the range's partial
 // product, and k_splitk_reduce adds the ranges in binary64 and rounds once.
-#ifndef FP4Q_DEC_WAVES
-#define FP4Q_DEC_WAVES 4
-#endif
 #ifndef FP4Q_DEC_BUFS
 #define FP4Q_DEC_BUFS 3
 #endif
-constexpr int kDecWaves = FP4Q_DEC_WAVES;  // units per workgroup
 constexpr int kDecBufs = FP4Q_DEC_BUFS;    // LDS buffers per unit
+// Units (waves) per workgroup: 4 for one row group of A, else 1.  Measured
+// (Qwen2.5-7B projections, 1 / 16 / 32 tokens): one-wave workgroups spread
+// the units over more CUs and won 0.1-1.5 us at 16 and 32 tokens, but lost
+// 1.1 us at 1 token x 3584 x 18944.
+constexpr int dec_waves(int ar) { return ar == 1 ? 4 : 1; }
 constexpr int kDecMaxM = 32;
 
 template <int AR>
@@ -609,13 +611,13 @@ __device__ __forceinline__ v16f mma_dec(v16f acc, v4i b, v4i a, int sb, int sa) 
                                                            kFmtE2M1, kFmtE2M1, T, sb, T, sa);
 }
 
-template <int AR>
-__global__ __launch_bounds__(kDecWaves * kWave) void k_gemm_decode(DecParams p) {
+template <int AR, int W>
+__global__ __launch_bounds__(W * kWave) void k_gemm_decode(DecParams p) {
     typedef DecLayout<AR> L;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kDecWaves * L::kUnit];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[W * L::kUnit];
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t unit = (int64_t)blockIdx.x * kDecWaves + wave;
+    const int64_t unit = (int64_t)blockIdx.x * W + wave;
     if (unit >= p.units) return;  // the whole wave; no workgroup barrier follows
     const int splits = p.splits, split = (int)(unit % splits);
     const int64_t n0 = unit / splits * kFrag;
@@ -837,8 +839,10 @@ int workspace_splits(int64_t M, int64_t N, int64_t K) {
 }
 
 template <int AR>
-void launch_decode_ar(const DecParams& p, unsigned groups, hipStream_t stream) {
-    hipLaunchKernelGGL(k_gemm_decode<AR>, dim3(groups), dim3(kDecWaves * kWave), 0, stream, p);
+void launch_decode_ar(const DecParams& p, hipStream_t stream) {
+    constexpr int W = dec_waves(AR);
+    const int64_t groups = (p.units + W - 1) / W;
+    hipLaunchKernelGGL((k_gemm_decode<AR, W>), dim3((unsigned)groups), dim3(W * kWave), 0, stream, p);
 }
 
 }  // namespace
@@ -858,8 +862,7 @@ int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
         reinterpret_cast<uintptr_t>(j.b_scales) % 4 == 0) {
         const int sp = decode_splits(j.M, j.N, j.K);
         const int64_t units = frags_of(j.N) * sp;
-        const int64_t groups = (units + kDecWaves - 1) / kDecWaves;
-        if (groups > INT32_MAX) {
+        if (units > INT32_MAX) {
             snprintf(msg, msg_len, "gemm: %lld x %lld x %lld needs more workgroups than one launch holds",
                      (long long)j.M, (long long)j.N, (long long)j.K);
             return (int)hipErrorInvalidConfiguration;
@@ -867,10 +870,10 @@ int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
         const DecParams p{j.a_codes, j.a_scales, j.b_codes, j.b_scales, j.M, j.N, j.K, (int)S, sp, units,
                           j.c, j.ct, partial_area};
         switch ((j.M + 7) / 8) {
-            case 1: launch_decode_ar<1>(p, (unsigned)groups, stream); break;
-            case 2: launch_decode_ar<2>(p, (unsigned)groups, stream); break;
-            case 3: launch_decode_ar<3>(p, (unsigned)groups, stream); break;
-            default: launch_decode_ar<4>(p, (unsigned)groups, stream); break;
+            case 1: launch_decode_ar<1>(p, stream); break;
+            case 2: launch_decode_ar<2>(p, stream); break;
+            case 3: launch_decode_ar<3>(p, stream); break;
+            default: launch_decode_ar<4>(p, stream); break;
         }
         if (sp > 1) {
             const int64_t count = j.M * j.N;
