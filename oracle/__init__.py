@@ -93,6 +93,8 @@ def _bind(lib):
     lib.oracle_quantize_search.restype = c.c_int
     lib.oracle_gemm_mxfp4.argtypes = [P, P, P, P, i64, i64, i64, P]
     lib.oracle_gemm_mxfp4.restype = c.c_int
+    lib.oracle_gemm_nvfp4.argtypes = [P, P, c.c_float, P, P, c.c_float, i64, i64, i64, P]
+    lib.oracle_gemm_nvfp4.restype = c.c_int
     lib.oracle_dequantize.argtypes = [P, P, c.c_int, c.c_int, c.c_float, i64, i64, c.c_int, P]
     lib.oracle_dequantize.restype = c.c_int
     lib.oracle_block_mse.argtypes = [P, P, P, c.c_int, c.c_int, c.c_float, i64, i64, c.c_int,
@@ -237,6 +239,23 @@ def gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, m: int, n: int, k: int) -> 
     rc = load().oracle_gemm_mxfp4(_ptr(ac), _ptr(asc), _ptr(bc), _ptr(bsc), m, n, k, _ptr(out))
     if rc:
         raise OracleError("gemm_mxfp4: bad arguments")
+    return out
+
+
+def gemm_nvfp4(a_codes, a_scales, ga: float, b_codes, b_scales, gb: float, m: int, n: int,
+               k: int) -> np.ndarray:
+    """C = A_hat B_hat^T (binary64) of two NVFP4 operands: codes (rows x k/2), UE4M3
+    scale bytes per 16 elements (rows x k/16) and a per-tensor scale each, the
+    elements dequantized as dequantize() does."""
+    ac = np.ascontiguousarray(a_codes, dtype=np.uint8)
+    asc = np.ascontiguousarray(a_scales, dtype=np.uint8)
+    bc = np.ascontiguousarray(b_codes, dtype=np.uint8)
+    bsc = np.ascontiguousarray(b_scales, dtype=np.uint8)
+    out = np.zeros((m, n), np.float64)
+    rc = load().oracle_gemm_nvfp4(_ptr(ac), _ptr(asc), float(ga), _ptr(bc), _ptr(bsc), float(gb),
+                                  m, n, k, _ptr(out))
+    if rc:
+        raise OracleError("gemm_nvfp4: bad arguments")
     return out
 
 

@@ -57,6 +57,11 @@
  *       is 0; the row is then quantized exactly as under a given g = g_r.
  *   R10 FP4 GEMM: C = A_hat B_hat^T from the exactly dequantized MXFP4 operands,
  *       summed in binary64 (see oracle_gemm_mxfp4).
+ *   R11 NVFP4 GEMM: the same product of two NVFP4 operands (blocks of 16,
+ *       UE4M3 scale bytes, a per-tensor g each), taken on their dequantized
+ *       binary32 values x_hat = RN32(v * RN32(s_hat * g)) -- the values
+ *       oracle_dequantize returns -- and summed in binary64 (see
+ *       oracle_gemm_nvfp4).
  */
 #include <math.h>
 #include <stddef.h>
@@ -583,6 +588,37 @@ int oracle_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uin
                 double va = ldexp(oracle_e2m1_value(ca), (int)a_scales[m * (K / 32) + k / 32] - 127);
                 double vb = ldexp(oracle_e2m1_value(cb), (int)b_scales[n * (K / 32) + k / 32] - 127);
                 sum += va * vb;
+            }
+            c[m * N + n] = sum;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * R11: product of two NVFP4 matrices (the FP4 GEMM of [MRGPTQ] Sommario
+ * tecnico section 3 item 4 and section 4, for the NVFP4 format of [DIAG]
+ * section 2).  A (M x K) and B (N x K) are codes and UE4M3 scale bytes per 16
+ * elements along K, as oracle_quantize writes them for block 16, with
+ * per-tensor scales ga and gb; each element is dequantized exactly as
+ * oracle_dequantize does (binary32: d = RN32(s_hat * g), x_hat = RN32(v * d)),
+ * and C = A_hat * B_hat^T is summed in binary64, row major M x N.
+ */
+int oracle_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, float ga,
+                      const uint8_t* b_codes, const uint8_t* b_scales, float gb, int64_t M,
+                      int64_t N, int64_t K, double* c)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return ORACLE_BAD_ARG;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t ea = m * K + k, eb = n * K + k;
+                int ca = (a_codes[ea / 2] >> ((ea % 2) * 4)) & 15;
+                int cb = (b_codes[eb / 2] >> ((eb % 2) * 4)) & 15;
+                block_scale sa = scale_from_byte(FMT_UE4M3, a_scales[m * (K / 16) + k / 16], ga);
+                block_scale sb = scale_from_byte(FMT_UE4M3, b_scales[n * (K / 16) + k / 16], gb);
+                sum += (double)element_value(FMT_UE4M3, ca, sa) * (double)element_value(FMT_UE4M3, cb, sb);
             }
             c[m * N + n] = sum;
         }
