@@ -266,6 +266,45 @@ fp4q_status fp4_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
                            int32_t ct, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * NVFP4 matrix product ("Bridging the Gap...", Sommario tecnico section 3
+ * item 4 and section 4, for the NVFP4 format of "Diagnosing FP4 inference",
+ * section 2).  C = A_hat * B_hat^T, where A (M x K) and B (N x K) are NVFP4
+ * matrices exactly as nvfp4_quantize writes them with block 16 and UE4M3
+ * scales (codes rows x K/2 bytes, scale bytes rows x K/16), each with its
+ * per-tensor scale g.  The matrix cores' block scales are powers of two, so
+ * each element's E2M1 value times its block scale (exact in bf16) goes
+ * through bf16 matrix instructions, and a_g * b_g is applied to the binary32
+ * result.
+ *   a_codes, b_codes    device, 16-byte aligned
+ *   a_scales, b_scales  device, 4-byte aligned
+ *   a_g, b_g            device binary32 per-tensor scales (as nvfp4_quantize
+ *                       writes or reads them); NULL means 1
+ *   M, N, K             K % 64 == 0, K <= 2^23, M < 2^31, N * sizeof(out
+ *                       element) < 2^23; M or N == 0 is a no-op; K == 0
+ *                       writes zeros
+ *   c, ct               as for fp4_gemm_mxfp4
+ *   ws, ws_bytes        device scratch of at least
+ *                       fp4_gemm_nvfp4_workspace_bytes(M, N, K) bytes (0 for
+ *                       most shapes; then ws may be NULL), 16-byte aligned:
+ *                       binary32 partial products of K ranges for products
+ *                       with too few 256 x 256 tiles.  Owned by the caller.
+ * Against the exact product of the dequantized operands (x_hat = RN32(v *
+ * RN32(s_hat * g)), as fp4_dequantize writes them), C differs by rounding of
+ * order (K/16 + 8) * 2^-23 of sum |a_hat| |b_hat|: binary32 accumulation in
+ * 16-element steps, partial products added in binary64, and the roundings of
+ * the dequantized values and of the per-tensor scales.  Results are the same
+ * on every run for a given shape.  Errors as for fp4_gemm_mxfp4.
+ */
+fp4q_status fp4_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g,
+                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_g, int64_t M,
+                           int64_t N, int64_t K, void* c, int32_t ct, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Workspace bytes fp4_gemm_nvfp4 needs for an M x N x K product: 4 * M * N per
+ * K range when K is split (a function of M, N and K only); 0 otherwise. */
+size_t fp4_gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 /* Workspace bytes fp4_gemm_mxfp4 needs for an M x N x K product: 256 *
  * (ceil(M/32) + ceil(N/32)) * ceil(K/256), rounded up to 256, plus
  * 4 * M * N per K range when K is split (the larger of the two kernels'

@@ -35,6 +35,7 @@ STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_WORKSPA
 
 EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "fp4_quantize_search", "fp4_dequantize",
            "fp4_block_mse", "hadamard_block_rotate", "fp4_gemm_mxfp4", "fp4_gemm_workspace_bytes",
+           "fp4_gemm_nvfp4", "fp4_gemm_nvfp4_workspace_bytes",
            "fp4q_workspace_bytes",
            "fp4q_last_error", "fp4q_abi_version")
 
@@ -70,6 +71,9 @@ def _bind(l):
     l.fp4_gemm_mxfp4.argtypes = [P, P, P, P, i64, i64, i64, P, i32, P, sz, P]
     l.fp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     l.fp4_gemm_workspace_bytes.restype = sz
+    l.fp4_gemm_nvfp4.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, i32, P, sz, P]
+    l.fp4_gemm_nvfp4_workspace_bytes.argtypes = [i64, i64, i64]
+    l.fp4_gemm_nvfp4_workspace_bytes.restype = sz
     l.fp4_block_mse.argtypes = [P, i32, P, P, i32, i32, P, i64, i64, i32, P, i32, P, P, sz, P]
     l.hadamard_block_rotate.argtypes = [P, i32, i64, i64, i32, P, P]
     for name in ("mxfp4_quantize", "nvfp4_quantize", "fp4_dequantize", "fp4_block_mse",
@@ -267,6 +271,32 @@ def fp4_gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch
     _check(lib().fp4_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), m, n,
                                 k, _ptr(out), _dtype_code(out), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(a_codes.device)))
+    return out
+
+
+def fp4_gemm_nvfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, a_g: Optional[torch.Tensor],
+                   b_codes: torch.Tensor, b_scales: torch.Tensor, b_g: Optional[torch.Tensor],
+                   out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = A_hat @ B_hat.T for NVFP4 operands as nvfp4_quantize writes them with
+    block 16 and UE4M3 scales: codes (rows x K/2 uint8), scale bytes (rows x
+    K/16 uint8) and the per-tensor scale (a 1-element float32 device tensor, or
+    None for 1)."""
+    a_codes, a_scales = _matrix(a_codes, "a_codes"), _matrix(a_scales, "a_scales")
+    b_codes, b_scales = _matrix(b_codes, "b_codes"), _matrix(b_scales, "b_scales")
+    m, k = a_codes.shape[0], a_codes.shape[1] * 2
+    n = b_codes.shape[0]
+    if b_codes.shape[1] * 2 != k or a_scales.shape != (m, k // 16) or b_scales.shape != (n, k // 16):
+        raise ValueError("operand shapes do not match: codes rows x K/2, scales rows x K/16")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_codes.device)
+    need = int(lib().fp4_gemm_nvfp4_workspace_bytes(m, n, k))
+    if ws is None and need:
+        ws = gemm_workspace(a_codes.device, need)
+    _check(lib().fp4_gemm_nvfp4(_ptr(a_codes), _ptr(a_scales), _ptr(a_g), _ptr(b_codes),
+                                _ptr(b_scales), _ptr(b_g), m, n, k, _ptr(out), _dtype_code(out),
+                                _ptr(ws), 0 if ws is None else ws.numel(),
+                                _stream(a_codes.device)))
     return out
 
 

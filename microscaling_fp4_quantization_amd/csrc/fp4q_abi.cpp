@@ -246,6 +246,49 @@ size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return fp4q::gemm_workspace_bytes(M, N, K);
 }
 
+fp4q_status fp4_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g,
+                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_g, int64_t M,
+                           int64_t N, int64_t K, void* c, int32_t ct, void* ws, size_t ws_bytes,
+                           void* stream) {
+    const char* fn = "fp4_gemm_nvfp4";
+    TRY(check_dtype(fn, ct));
+    if (M < 0 || N < 0 || K < 0) return fail(FP4Q_ERR_SHAPE, "%s: negative size", fn);
+    if (K % 64 != 0) return fail(FP4Q_ERR_SHAPE, "%s: K = %lld is not a multiple of 64", fn, (long long)K);
+    if (K > (int64_t)1 << 23) return fail(FP4Q_ERR_SHAPE, "%s: K = %lld exceeds 2^23", fn, (long long)K);
+    const int64_t eb = ct == FP4Q_F32 ? 4 : 2;
+    if (N * eb >= (int64_t)1 << 23)
+        return fail(FP4Q_ERR_SHAPE, "%s: N = %lld is too large for this output type", fn, (long long)N);
+    if (M >= (int64_t)1 << 31) return fail(FP4Q_ERR_SHAPE, "%s: M = %lld exceeds 2^31", fn, (long long)M);
+    if (M > 0 && N > 0) {
+        if (!c) return fail(FP4Q_ERR_ARG, "%s: c must not be NULL", fn);
+        if (!aligned(c, (size_t)eb)) return fail(FP4Q_ERR_ALIGN, "%s: c is not aligned to its element", fn);
+        if (K > 0) {
+            if (!a_codes || !a_scales || !b_codes || !b_scales)
+                return fail(FP4Q_ERR_ARG, "%s: codes and scales must not be NULL", fn);
+            if (!aligned(a_codes, 16) || !aligned(b_codes, 16))
+                return fail(FP4Q_ERR_ALIGN, "%s: codes must be 16-byte aligned", fn);
+            if (!aligned(a_scales, 4) || !aligned(b_scales, 4))
+                return fail(FP4Q_ERR_ALIGN, "%s: scales must be 4-byte aligned", fn);
+            if ((a_g && !aligned(a_g, 4)) || (b_g && !aligned(b_g, 4)))
+                return fail(FP4Q_ERR_ALIGN, "%s: per-tensor scales must be 4-byte aligned", fn);
+            const size_t need = fp4q::gemm_nvfp4_workspace_bytes(M, N, K);
+            if (need > 0 && (!ws || ws_bytes < need))
+                return fail(FP4Q_ERR_WORKSPACE, "%s: needs a workspace of %zu bytes (got %zu)", fn, need,
+                            ws ? ws_bytes : (size_t)0);
+            if (need > 0 && !aligned(ws, 16))
+                return fail(FP4Q_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+        }
+    }
+    fp4q::GemmNvJob j{a_codes, a_scales, b_codes, b_scales, a_g, b_g, M, N, K, c, ct, ws, stream};
+    char msg[256] = {0};
+    return launched(fp4q::launch_gemm_nvfp4(j, msg, sizeof msg), msg);
+}
+
+size_t fp4_gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return fp4q::gemm_nvfp4_workspace_bytes(M, N, K);
+}
+
 fp4q_status hadamard_block_rotate(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t n_rot,
                                   float* out, void* stream) {
     const char* fn = "hadamard_block_rotate";

@@ -534,6 +534,177 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(GParams p) {
 int64_t frags_of(int64_t rows) { return (rows + kFrag - 1) / kFrag; }
 
 // ---------------------------------------------------------------------------
+// NVFP4 GEMM.  C = gA gB * (A_v * B_v^T), where A_v and B_v hold each element's
+// E2M1 value times its block's UE4M3 scale (blocks of 16 along K) and gA, gB
+// are the per-tensor scales.  The matrix cores' block scales are powers of two
+// only, and an E2M1 value times a UE4M3 scale (up to 6 significant bits) fits
+// neither FP8 nor FP6, but it is exact in bf16: so the operands are decoded
+// into bf16 in LDS and multiplied with v_mfma_f32_32x32x16_bf16, and gA gB is
+// applied to the binary32 result.
+//
+// The tile, the waves' 2 x 4 layout and the epilogue are the MXFP4 kernel's.
+// K advances 64 per stage through two LDS stages of bf16 (256 + 256 rows x
+// 128 bytes).  Each of the 512 threads decodes one row's 64 elements of the
+// next stage: two 16-byte code loads and one scale dword into registers, then
+// v_cvt_scalef32_pk_f32_fp4 (at scale 1), a binary32 multiply by the block
+// scale (v_cvt_f32_fp8 decodes UE4M3 exactly), and the upper halves of the
+// exact binary32 products as bf16.  In LDS a row's eight 16-byte pieces are
+// rotated by row / 2 as in the MXFP4 kernel; at step j lane l reads piece
+// 2 j + l / 32 of row l % 32 of its fragment, for both operands alike.
+constexpr int BKN = 64;                        // K elements per NVFP4 stage
+constexpr int kNvRow = BKN * 2;                // bf16 bytes per row per stage
+constexpr int kNvStage = (BM + BN) * kNvRow;   // 64 KB
+static_assert(2 * kNvStage >= kEpiBytes && BM + BN == kThreads, "NVFP4 stage plan");
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+struct NvParams {
+    const uint8_t* a_codes;
+    const uint8_t* a_scales;
+    const uint8_t* b_codes;
+    const uint8_t* b_scales;
+    const float* ga;  // per-tensor scales (device), NULL for 1
+    const float* gb;
+    int64_t M, N, K;
+    void* c;
+    int ct;           // 0 bf16, 1 f32
+    int splits;       // K ranges per tile (1: C directly)
+    float* partial;   // splits > 1: binary32 partial products, splits x M x N
+};
+
+// Upper halves of two binary32 values with at most 8 significant bits: their
+// bf16 encodings, exactly.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+    return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
+}
+
+__global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(NvParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kNvStage];
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    const int splits = p.splits, split = (int)(blockIdx.x % splits);
+    int64_t tm, tn;
+    tile_of(blockIdx.x / splits, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+    const int64_t rows_a = p.M - m0 < BM ? p.M - m0 : BM;
+    const int64_t rows_b = p.N - n0 < BN ? p.N - n0 : BN;
+    const int rowb = (int)(p.K / 2), kbn = (int)(p.K / 16);
+    const int S = (int)(p.K / BKN);
+    const int per = (S + splits - 1) / splits;
+    const int s_lo = split * per, s_hi = s_lo + per < S ? s_lo + per : S;
+    const float gg = (p.ga ? *p.ga : 1.0f) * (p.gb ? *p.gb : 1.0f);
+
+    // Decoding role: waves 0-3 take rows of A, waves 4-7 rows of B (a
+    // wave-uniform choice, so each wave has one pair of windows).
+    const bool dec_a = wave < BM / kWave;
+    const int drow = threadIdx.x - (dec_a ? 0 : BM);
+    const Rsrc rcode = dec_a ? make_rsrc(p.a_codes + m0 * rowb, rows_a * rowb)
+                             : make_rsrc(p.b_codes + n0 * rowb, rows_b * rowb);
+    const Rsrc rscl = dec_a ? make_rsrc(p.a_scales + m0 * kbn, rows_a * kbn)
+                            : make_rsrc(p.b_scales + n0 * kbn, rows_b * kbn);
+    const int drot = drow / 2;
+    auto load = [&](int s, u32x4_t& c0, u32x4_t& c1, uint32_t& sc) {
+        const int off = s < s_hi ? drow * rowb + 32 * s : kPastWindow;
+        const int soff = s < s_hi ? drow * kbn + 4 * s : kPastWindow;
+        c0 = __builtin_amdgcn_raw_buffer_load_b128(rcode, off, 0, 0);
+        c1 = __builtin_amdgcn_raw_buffer_load_b128(rcode, off + 16, 0, 0);
+        sc = __builtin_amdgcn_raw_buffer_load_b32(rscl, soff, 0, 0);
+    };
+    auto decode = [&](uint8_t* stage, const u32x4_t& c0, const u32x4_t& c1, uint32_t sc) {
+        uint8_t* row = stage + (dec_a ? 0 : BM * kNvRow) + drow * kNvRow;
+        float sv[4];
+        sv[0] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
+        sv[1] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
+        sv[2] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 2);
+        sv[3] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 3);
+#pragma unroll
+        for (int pc = 0; pc < 8; ++pc) {
+            const uint32_t w = pc < 4 ? c0[pc] : c1[pc - 4];
+            const float s = sv[pc / 2];
+            float2v f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+            float2v f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+            float2v f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+            float2v f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+            const u32x4_t o = {pack_bf16_exact(f0[0] * s, f0[1] * s), pack_bf16_exact(f1[0] * s, f1[1] * s),
+                               pack_bf16_exact(f2[0] * s, f2[1] * s), pack_bf16_exact(f3[0] * s, f3[1] * s)};
+            *reinterpret_cast<u32x4_t*>(row + 16 * ((pc + drot) & 7)) = o;
+        }
+    };
+
+    v16f acc[FB][FA];
+#pragma unroll
+    for (int i = 0; i < FB; ++i)
+#pragma unroll
+        for (int j = 0; j < FA; ++j) acc[i][j] = v16f{};
+
+    const int r = lane % kFrag, h = lane / kFrag;
+    {
+        u32x4_t c0, c1;
+        uint32_t sc;
+        load(s_lo, c0, c1, sc);
+        decode(lds, c0, c1, sc);
+    }
+    __syncthreads();
+    for (int s = s_lo; s < s_hi; ++s) {
+        const int cur = (s - s_lo) & 1;
+        const uint8_t* st = lds + cur * kNvStage;
+        u32x4_t c0, c1;
+        uint32_t sc = 0;
+        const bool more = s + 1 < s_hi;
+        if (more) load(s + 1, c0, c1, sc);
+#pragma unroll
+        for (int j = 0; j < BKN / 16; ++j) {
+            bf16x8_t a[FA], b[FB];
+#pragma unroll
+            for (int fa = 0; fa < FA; ++fa) {
+                const int row = wm * WM + fa * kFrag + r;
+                a[fa] = *reinterpret_cast<const bf16x8_t*>(st + row * kNvRow + 16 * ((2 * j + h + row / 2) & 7));
+            }
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb) {
+                const int row = wn * WN + fb * kFrag + r;
+                b[fb] = *reinterpret_cast<const bf16x8_t*>(st + BM * kNvRow + row * kNvRow +
+                                                           16 * ((2 * j + h + row / 2) & 7));
+            }
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                for (int fa = 0; fa < FA; ++fa)
+                    acc[fb][fa] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[fb], a[fa], acc[fb][fa], 0, 0, 0);
+        }
+        if (more) decode(lds + (cur ^ 1) * kNvStage, c0, c1, sc);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < FB; ++i)
+#pragma unroll
+        for (int j = 0; j < FA; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] *= gg;
+
+    if (splits > 1) {
+        float* part = p.partial + (int64_t)split * p.M * p.N;
+        const Rsrc rp = make_rsrc(part + m0 * p.N, rows_a * p.N * 4);
+        if (((p.N * 4) & 15) == 0) store_tile<4>(acc, lds, rp, wave, wm, wn, lane, rows_a, n0, p.N);
+        else store_direct(acc, rp, 1, wm, wn, lane, rows_a, n0, p.N);
+        return;
+    }
+    const int eb = p.ct == 1 ? 4 : 2;
+    const Rsrc rc = make_rsrc(static_cast<char*>(p.c) + m0 * p.N * eb, rows_a * p.N * eb);
+    if (((p.N * eb) & 15) == 0) {
+        if (p.ct == 1) store_tile<4>(acc, lds, rc, wave, wm, wn, lane, rows_a, n0, p.N);
+        else store_tile<2>(acc, lds, rc, wave, wm, wn, lane, rows_a, n0, p.N);
+    } else {
+        store_direct(acc, rc, p.ct, wm, wn, lane, rows_a, n0, p.N);
+    }
+}
+
+
+// ---------------------------------------------------------------------------
 // Decode-sized products: M <= 32 rows of A (a batch of tokens), any N and K.
 // The product is a pass over B, so the work is cut into units of one 32-row
 // fragment of B and one range of K segments (256 elements each), one unit per
@@ -850,6 +1021,37 @@ void launch_decode_ar(const DecParams& p, hipStream_t stream) {
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t packed = (packed_bytes(M, N, K) + 255) / 256 * 256;
     return (size_t)(packed + (int64_t)workspace_splits(M, N, K) * M * N * 4);
+}
+
+int launch_gemm_nvfp4(const GemmNvJob& j, char* msg, size_t msg_len) {
+    if (j.M == 0 || j.N == 0) return 0;
+    const hipStream_t stream = static_cast<hipStream_t>(j.stream);
+    const int64_t tiles = ((j.M + BM - 1) / BM) * ((j.N + BN - 1) / BN);
+    const int sp = splits_for(j.M, j.N, j.K);
+    if (tiles * sp > INT32_MAX) {
+        snprintf(msg, msg_len, "gemm: %lld x %lld x %lld needs more workgroups than one launch holds",
+                 (long long)j.M, (long long)j.N, (long long)j.K);
+        return (int)hipErrorInvalidConfiguration;
+    }
+    float* partial = reinterpret_cast<float*>(j.ws);
+    const NvParams p{j.a_codes, j.a_scales, j.b_codes, j.b_scales, j.ga, j.gb, j.M, j.N, j.K,
+                     j.c, j.ct, sp, partial};
+    hipLaunchKernelGGL(k_gemm_nvfp4, dim3((unsigned)(tiles * sp)), dim3(kThreads), 0, stream, p);
+    if (sp > 1) {
+        const int64_t count = j.M * j.N;
+        const int64_t groups = std::min<int64_t>((count + 1023) / 1024, 8192);
+        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)groups), dim3(256), 0, stream, partial, sp, count,
+                           j.c, j.ct);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) return 0;
+    snprintf(msg, msg_len, "gemm nvfp4 kernel launch: %s", hipGetErrorString(e));
+    return (int)e;
+}
+
+size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const int sp = splits_for(M, N, K);
+    return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * 4 : 0;
 }
 
 int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {

@@ -92,11 +92,28 @@ struct GemmJob {
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+struct GemmNvJob {
+    const uint8_t* a_codes;
+    const uint8_t* a_scales;  // UE4M3 per 16 elements
+    const uint8_t* b_codes;
+    const uint8_t* b_scales;
+    const float* ga;          // per-tensor scales (device), nullable
+    const float* gb;
+    int64_t M, N, K;
+    void* c;
+    int ct;                   // 0 bf16, 1 f32
+    void* ws;                 // gemm_nvfp4_workspace_bytes(M, N, K) bytes: partials
+    void* stream;
+};
+
+size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 // Each returns 0 on success, else a HIP error code; `msg` gets a description.
 int launch_quantize(const QuantJob& j, char* msg, size_t msg_len);
 int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len);
 int launch_block_mse(const MseJob& j, char* msg, size_t msg_len);
 int launch_rotate(const RotateJob& j, char* msg, size_t msg_len);
 int launch_gemm(const GemmJob& j, char* msg, size_t msg_len);
+int launch_gemm_nvfp4(const GemmNvJob& j, char* msg, size_t msg_len);
 
 }  // namespace fp4q

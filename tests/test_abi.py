@@ -137,6 +137,27 @@ def test_gemm_validation(L):
     assert gm(A16, A16b, A16c, A16, 0, 4, 64, A16b, 1, ws=None, wsb=0) == OK
 
 
+def test_gemm_nvfp4_validation(L):
+    gn = lambda a, sa, b, sb, m, n, k, c, ct, ga=None, gb=None, ws=A16, wsb=1 << 20: L.fp4_gemm_nvfp4(
+        a, sa, ga, b, sb, gb, m, n, k, c, ct, ws, wsb, None)
+    assert gn(A16, A16b, A16c, A16, 4, 4, 96, A16b, 1) == SHAPE and "multiple of 64" in err(L)
+    assert gn(A16, A16b, A16c, A16, 4, 4, -64, A16b, 1) == SHAPE
+    assert gn(A16, A16b, A16c, A16, 4, 4, 1 << 24, A16b, 1) == SHAPE and "2^23" in err(L)
+    assert gn(A16, A16b, A16c, A16, 4, 1 << 21, 64, A16b, 1) == SHAPE
+    assert gn(A16, A16b, A16c, A16, 4, 4, 64, None, 1) == ARG
+    assert gn(A16, None, A16c, A16, 4, 4, 64, A16b, 1) == ARG
+    assert gn(A16 + 8, A16b, A16c, A16, 4, 4, 64, A16b, 1) == ALIGN
+    assert gn(A16, A16b + 2, A16c, A16, 4, 4, 64, A16b, 1) == ALIGN and "4-byte" in err(L)
+    assert gn(A16, A16b, A16c, A16, 4, 4, 64, A16b, 1, ga=A16 + 2) == ALIGN
+    assert gn(A16, A16b, A16c, A16, 4, 4, 64, A16b, 7) == ARG
+    assert gn(A16, A16b, A16c, A16, 0, 4, 64, A16b, 1, ws=None, wsb=0) == OK
+    # Products with enough tiles need no workspace; few tiles split K.
+    assert L.fp4_gemm_nvfp4_workspace_bytes(8192, 18944, 3584) == 0
+    wb = L.fp4_gemm_nvfp4_workspace_bytes(16, 3584, 18944)
+    assert wb > 0 and wb % (16 * 3584 * 4) == 0 and 2 <= wb // (16 * 3584 * 4) <= 18944 // 256
+    assert L.fp4_gemm_nvfp4_workspace_bytes(0, 5, 64) == 0
+
+
 def test_gemm_workspace_bytes(L):
     """Packed scales: 256 B per 32-row fragment of A and B per 256-wide K stage,
     padded to 256 B; then, when K is split into ranges, one binary32 M x N
