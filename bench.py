@@ -321,6 +321,7 @@ GEMM_TOKENS = 8192
 GEMM_METRIC = ("TFLOP/s of MXFP4 x MXFP4 products (W4A4 Qwen2.5-7B MLP, 8192 tokens, "
                "activation quantization included); % of dense FP4 matrix-core peak")
 MFMA_FP4_PEAK_TFLOPS = 10100.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 GEMM_SAMPLE_ROWS = 8
 
 
@@ -350,6 +351,7 @@ def gemm_main(args, steps, warmup):
     decode = [(tok, n, a) for tok in (1, 16) for n, a in (("up", "x"), ("down", "h"))]
     need = max([fq.lib().fp4_gemm_workspace_bytes(T, weights[n][0].shape[0], acts[a].shape[1])
                 for n, a in prods] +
+               [fq.lib().fp4_gemm_nvfp4_workspace_bytes(T, weights["up"][0].shape[0], hidden)] +
                [fq.lib().fp4_gemm_workspace_bytes(tok, weights[n][0].shape[0], acts[a].shape[1])
                 for tok, n, a in decode])
     ws = fq.gemm_workspace(dev, need)
@@ -399,6 +401,22 @@ def gemm_main(args, steps, warmup):
             "shape_MxNxK": f"{tok}x{wc.shape[0]}x{acts[a].shape[1]}",
             "us_per_call": round(ms * 1e3, 2),
             "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1)}
+    # The same up projection in NVFP4 (block 16, UE4M3, dynamic g; bf16 matrix
+    # cores, so its peak is the dense bf16 one).
+    nw = fq.nvfp4_quantize(w_host["up"].to(dev), 16, fq.FMT_UE4M3, fq.G_DYNAMIC, block_mse=False,
+                           stats=False)
+    nx = fq.nvfp4_quantize(acts["x"], 16, fq.FMT_UE4M3, fq.G_DYNAMIC, block_mse=False, stats=False)
+    cn = torch.empty_like(outs["up"])
+    nv_fn = lambda: fq.fp4_gemm_nvfp4(nx.codes, nx.scales, nx.g, nw.codes, nw.scales, nw.g,
+                                      torch.bfloat16, out=cn, ws=ws)
+    nv_fn()
+    ms = time_region(torch, stream, nv_fn, reps)
+    breakdown["nvfp4_gemm_up"] = {"shape_MxNxK": breakdown["gemm_up"]["shape_MxNxK"],
+                                  "us_per_call": round(ms * 1e3, 2),
+                                  "TFLOPs": round(flops["up"] / (ms * 1e-3) / 1e12, 1),
+                                  "frac_of_bf16_dense_peak": round(flops["up"] / (ms * 1e-3) / 1e12
+                                                                   / MFMA_BF16_PEAK_TFLOPS, 4)}
+    del nw
     for a in ("x", "h"):
         ms = time_region(torch, stream, lambda a=a: quantize(a), reps)
         breakdown[f"quantize_{a}"] = {"shape": "x".join(map(str, acts[a].shape)),
