@@ -288,7 +288,11 @@ fp4q_status fp4_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, cons
  *                       fp4_gemm_nvfp4_workspace_bytes(M, N, K) bytes (0 for
  *                       most shapes; then ws may be NULL), 16-byte aligned:
  *                       binary32 partial products of K ranges for products
- *                       with too few 256 x 256 tiles.  Owned by the caller.
+ *                       with too few 256 x 256 tiles or few rows of B.
+ *                       Owned by the caller.
+ * Products of at most 32 rows of A run a kernel that streams B once, 32 rows
+ * of B per wave; others run the 256 x 256 tile kernel; the contract below is
+ * the same for both.
  * Against the exact product of the dequantized operands (x_hat = RN32(v *
  * RN32(s_hat * g)), as fp4_dequantize writes them), C differs by rounding of
  * order (K/16 + 8) * 2^-23 of sum |a_hat| |b_hat|: binary32 accumulation in

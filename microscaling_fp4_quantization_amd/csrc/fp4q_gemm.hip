@@ -579,6 +579,17 @@ __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
     return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
 }
 
+// Byte i of w as an FP8 E4M3 value in binary32 (exact; UE4M3 scale bytes are
+// E4M3 codes with the sign bit clear).  i must fold to a constant.
+__device__ __forceinline__ float fp8_byte_f32(uint32_t w, int i) {
+    switch (i) {
+        case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+        case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+        case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+        default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(NvParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kNvStage];
     const int lane = threadIdx.x % kWave;
@@ -893,6 +904,167 @@ __global__ __launch_bounds__(W * kWave) void k_gemm_decode(DecParams p) {
 }
 
 
+// NVFP4 decode kernel (M <= 32): the units, buffers and direct loads of
+// k_gemm_decode, with each operand's 32 rows x 16 UE4M3 scale bytes of a
+// segment brought in by two dword-wide direct loads, and the arithmetic of
+// k_gemm_nvfp4: within a segment lane l (row l % 32, half h = l / 32) reads
+// the 16-byte pieces 4 h + i (i = 0..3) of its row; bytes 4 t .. 4 t + 3 of
+// piece i are the 8 elements it feeds to bf16 step 4 i + t, decoded in
+// registers to v * s_hat with their block's scale (block 8 h + 2 i + t / 2 of
+// the segment: the lane's scale bytes are one 8-byte LDS read).  A and B are
+// read and paired alike, so every element meets its partner once.
+template <int AR>
+struct NvDecLayout {
+    static constexpr int kB = kFrag * kRowStage;       // B codes, 4 KB
+    static constexpr int kA = AR * 8 * kRowStage;      // A codes
+    static constexpr int kS = kFrag * 16;              // scale bytes per operand
+    static constexpr int kBuf = kB + kA + 2 * kS;
+    static constexpr int kZero = kDecBufs * kBuf;
+    static constexpr int kUnit = kZero + 16;
+    static constexpr int kLoads = 4 + AR + 2 + 2;
+    static_assert(kBuf % 16 == 0 && (kDecBufs - 1) * kLoads < 64, "nvfp4 decode layout");
+};
+
+struct NvDecParams {
+    const uint8_t* a_codes;
+    const uint8_t* a_scales;
+    const uint8_t* b_codes;
+    const uint8_t* b_scales;
+    const float* ga;
+    const float* gb;
+    int64_t M, N, K;
+    int S;           // K segments, ceil(K / 256)
+    int splits;
+    int64_t units;
+    void* c;
+    int ct;
+    float* partial;
+};
+
+// 8 elements (one dword of codes) as bf16, times a block scale: exact.
+__device__ __forceinline__ bf16x8_t decode8_bf16(uint32_t w, float s) {
+    const float2v f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const float2v f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const float2v f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const float2v f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    const u32x4_t o = {pack_bf16_exact(f0[0] * s, f0[1] * s), pack_bf16_exact(f1[0] * s, f1[1] * s),
+                       pack_bf16_exact(f2[0] * s, f2[1] * s), pack_bf16_exact(f3[0] * s, f3[1] * s)};
+    return __builtin_bit_cast(bf16x8_t, o);
+}
+
+template <int AR, int W>
+__global__ __launch_bounds__(W * kWave) void k_gemm_decode_nv(NvDecParams p) {
+    typedef NvDecLayout<AR> L;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[W * L::kUnit];
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t unit = (int64_t)blockIdx.x * W + wave;
+    if (unit >= p.units) return;  // the whole wave; no workgroup barrier follows
+    const int splits = p.splits, split = (int)(unit % splits);
+    const int64_t n0 = unit / splits * kFrag;
+    const int64_t rows_b = p.N - n0 < kFrag ? p.N - n0 : kFrag;
+    const int rowb = (int)(p.K / 2), kbn = (int)(p.K / 16), S = p.S;
+    const int per = (S + splits - 1) / splits;
+    const int s_lo = split * per, s_hi = s_lo + per < S ? s_lo + per : S;
+    const float gg = (p.ga ? *p.ga : 1.0f) * (p.gb ? *p.gb : 1.0f);
+    const Rsrc rb = make_rsrc(p.b_codes + n0 * rowb, rows_b * rowb);
+    const Rsrc ra = make_rsrc(p.a_codes, p.M * rowb);
+    const Rsrc rbs = make_rsrc(p.b_scales + n0 * kbn, rows_b * kbn);
+    const Rsrc ras = make_rsrc(p.a_scales, p.M * kbn);
+    uint8_t* base = lds + wave * L::kUnit;
+    *reinterpret_cast<u32x4_t*>(base + L::kZero) = u32x4_t{0u, 0u, 0u, 0u};
+
+    const int crow = lane / 8, cslot = lane % 8;
+    auto issue = [&](int s, uint8_t* buf) {
+        const int klim = s < s_hi ? rowb : 0;
+        const int slim = s < s_hi ? kbn : 0;
+#pragma unroll
+        for (int q = 0; q < 4 + AR; ++q) {
+            const bool is_b = q < 4;
+            const int qq = is_b ? q : q - 4;
+            const int piece = (cslot - 4 * (qq & 1) - lane / 16) & 7;
+            const int pos = 128 * s + 16 * piece;
+            const int off = pos < klim ? (8 * qq + crow) * rowb + pos : kDropped;
+            uint8_t* dst = buf + (is_b ? 0 : L::kB) + qq * 8 * kRowStage;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_b ? rb : ra, (LdsPtr)dst, 16, off, 0, 0, 0);
+        }
+        // Scales: instruction q moves rows 16 q .. 16 q + 15, dword lane % 4 of
+        // row 16 q + lane / 4.
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int spos = 16 * s + 4 * (lane % 4);
+            const int soff = spos < slim ? (16 * q + lane / 4) * kbn + spos : kDropped;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (LdsPtr)(buf + L::kB + L::kA + q * 256), 4, soff, 0,
+                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (LdsPtr)(buf + L::kB + L::kA + L::kS + q * 256), 4,
+                                                     soff, 0, 0, 0);
+        }
+    };
+
+    const int r = lane % kFrag, h = lane / kFrag;
+    const bool a_real = r < 8 * AR;
+    constexpr int kAhead = kDecBufs - 1;
+    v16f acc = {};
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) issue(s_lo + i, base + i * L::kBuf);
+    int cur = 0;
+    for (int s = s_lo; s < s_hi; ++s) {
+        const int nxt = cur == 0 ? kAhead : cur - 1;
+        issue(s + kAhead, base + nxt * L::kBuf);
+        wait_vm<kAhead * L::kLoads>();
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* buf = base + cur * L::kBuf;
+        const u32x2_t sbw = *reinterpret_cast<const u32x2_t*>(buf + L::kB + L::kA + r * 16 + 8 * h);
+        const u32x2_t saw = *reinterpret_cast<const u32x2_t*>(buf + L::kB + L::kA + L::kS + r * 16 + 8 * h);
+        u32x4_t bo[4], ao[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slot = (4 * h + i + r / 2) & 7;
+            bo[i] = *reinterpret_cast<const u32x4_t*>(buf + r * kRowStage + 16 * slot);
+            ao[i] = *reinterpret_cast<const u32x4_t*>(a_real ? buf + L::kB + r * kRowStage + 16 * slot
+                                                             : base + L::kZero);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int blk = 2 * i + t / 2;  // scale byte of the lane's 8
+                const float sb = fp8_byte_f32(sbw[blk / 4], blk % 4);
+                const float sa = fp8_byte_f32(saw[blk / 4], blk % 4);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(decode8_bf16(bo[i][t], sb),
+                                                              decode8_bf16(ao[i][t], sa), acc, 0, 0, 0);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        cur = cur == kAhead ? 0 : cur + 1;
+    }
+    wait_vm<0>();
+
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] *= gg;
+    const int64_t m = lane % kFrag;
+    if (splits == 1) {
+        const int eb = p.ct == 1 ? 4 : 2;
+        const Rsrc rc = make_rsrc(p.c, p.M * p.N * eb);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t n = n0 + 8 * (e / 4) + 4 * h + e % 4;
+            const int off = m < p.M && n < p.N ? (int)((m * p.N + n) * eb) : kDropped;
+            if (p.ct == 1)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[e]), rc, off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)to_bf16(acc[e]), rc, off, 0, 0);
+        }
+    } else {
+        const Rsrc rp = make_rsrc(p.partial + split * p.M * p.N, p.M * p.N * 4);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t n = n0 + 8 * (e / 4) + 4 * h + e % 4;
+            const int off = m < p.M && n < p.N ? (int)((m * p.N + n) * 4) : kDropped;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[e]), rp, off, 0, 0);
+        }
+    }
+}
+
 // C = sum over the K ranges of their binary32 partial products, added in
 // binary64 in range order and rounded once to binary32 (then to bf16 for a
 // bf16 C): one rounding more than the accumulation's own, the same for every
@@ -1010,6 +1182,13 @@ int workspace_splits(int64_t M, int64_t N, int64_t K) {
 }
 
 template <int AR>
+void launch_decode_nv_ar(const NvDecParams& p, hipStream_t stream) {
+    constexpr int W = dec_waves(AR);
+    const int64_t groups = (p.units + W - 1) / W;
+    hipLaunchKernelGGL((k_gemm_decode_nv<AR, W>), dim3((unsigned)groups), dim3(W * kWave), 0, stream, p);
+}
+
+template <int AR>
 void launch_decode_ar(const DecParams& p, hipStream_t stream) {
     constexpr int W = dec_waves(AR);
     const int64_t groups = (p.units + W - 1) / W;
@@ -1026,6 +1205,34 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 int launch_gemm_nvfp4(const GemmNvJob& j, char* msg, size_t msg_len) {
     if (j.M == 0 || j.N == 0) return 0;
     const hipStream_t stream = static_cast<hipStream_t>(j.stream);
+    if (j.M <= kDecMaxM) {
+        const int sp = decode_splits(j.M, j.N, j.K);
+        const int64_t units = frags_of(j.N) * sp;
+        if (units > INT32_MAX) {
+            snprintf(msg, msg_len, "gemm: %lld x %lld x %lld needs more workgroups than one launch holds",
+                     (long long)j.M, (long long)j.N, (long long)j.K);
+            return (int)hipErrorInvalidConfiguration;
+        }
+        float* partial = reinterpret_cast<float*>(j.ws);
+        const NvDecParams p{j.a_codes, j.a_scales, j.b_codes, j.b_scales, j.ga, j.gb, j.M, j.N, j.K,
+                            (int)((j.K + BK - 1) / BK), sp, units, j.c, j.ct, partial};
+        switch ((j.M + 7) / 8) {
+            case 1: launch_decode_nv_ar<1>(p, stream); break;
+            case 2: launch_decode_nv_ar<2>(p, stream); break;
+            case 3: launch_decode_nv_ar<3>(p, stream); break;
+            default: launch_decode_nv_ar<4>(p, stream); break;
+        }
+        if (sp > 1) {
+            const int64_t count = j.M * j.N;
+            const int64_t rg = std::min<int64_t>((count + 1023) / 1024, 8192);
+            hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)rg), dim3(256), 0, stream, partial, sp, count,
+                               j.c, j.ct);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e == hipSuccess) return 0;
+        snprintf(msg, msg_len, "gemm nvfp4 decode kernel launch: %s", hipGetErrorString(e));
+        return (int)e;
+    }
     const int64_t tiles = ((j.M + BM - 1) / BM) * ((j.N + BN - 1) / BN);
     const int sp = splits_for(j.M, j.N, j.K);
     if (tiles * sp > INT32_MAX) {
@@ -1050,7 +1257,7 @@ int launch_gemm_nvfp4(const GemmNvJob& j, char* msg, size_t msg_len) {
 }
 
 size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    const int sp = splits_for(M, N, K);
+    const int sp = M <= kDecMaxM ? decode_splits(M, N, K) : splits_for(M, N, K);
     return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * 4 : 0;
 }
 

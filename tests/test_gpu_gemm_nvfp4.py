@@ -13,7 +13,9 @@ accumulation in 16-element steps with a factor 2 of headroom, plus the
 roundings of the dequantized values (x_hat = RN32(v * RN32(s * g))) that the
 kernel does not take (it multiplies by gA gB at the end).  bf16 output adds
 half a bf16 ulp.  Shapes cover both epilogues, ragged M and N, K in whole
-64-element stages, and products split along K.
+64-element stages, products split along K, and both kernels: products of at
+most 32 rows of A take the decode kernel (one K range per fragment of B, or
+several added by the reduction), the others the tile kernel.
 """
 import numpy as np
 import pytest
@@ -66,7 +68,8 @@ def test_nv_gemm_exact_when_sums_are_exact(m, n, k, given_g):
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 64), (64, 512, 1024), (200, 333, 192), (128, 256, 3584),
                                    (33, 1000, 4096), (300, 517, 384), (520, 300, 512), (777, 1031, 1152),
-                                   (1, 300, 2048), (16, 1000, 4096), (5, 520, 1088), (3, 257, 2048)])
+                                   (1, 300, 2048), (16, 1000, 4096), (5, 520, 1088), (3, 257, 2048),
+                                   (20, 300, 512), (32, 520, 1024), (17, 15000, 256), (25, 33, 64)])
 def test_nv_gemm_within_bound(m, n, k):
     ac, asc, ga = operand(m, k, [72, m, k])
     bc, bsc, gb = operand(n, k, [73, n, k])
@@ -128,4 +131,21 @@ def test_nv_gemm_qwen7_up_projection_sampled_columns():
     bc, bsc = wq["codes"][cols], wq["scales"][cols]
     want = oracle.gemm_nvfp4(ac, asc, ga, bc, bsc, wq["g"], m, len(cols), k)
     tol = bound(ac, asc, ga, bc, bsc, wq["g"], m, len(cols), k) + np.abs(want) * 2.0 ** -8
+    assert np.all(np.abs(got[:, cols] - want) <= tol)
+
+
+def test_nv_gemm_decode_down_projection_sampled():
+    """16 tokens x 18944 times the NVFP4 3584 x 18944 down projection: the
+    decode kernel with K split into ranges."""
+    import fp4_workloads as wl
+    print("  case 16x3584x18944 nvfp4", flush=True)
+    m, n, k = 16, 3584, 18944
+    w = wl.qwen7_mlp(1, 1).float().numpy()
+    wq = oracle.quantize(w, oracle.FMT_UE4M3, 16, oracle.GMODE_DYNAMIC)
+    ac, asc, ga = operand(m, k, 79, spread=2)
+    got = run(ac, asc, ga, wq["codes"], wq["scales"], wq["g"])
+    cols = np.sort(np.random.default_rng(80).choice(n, 48, replace=False))
+    bc, bsc = wq["codes"][cols], wq["scales"][cols]
+    want = oracle.gemm_nvfp4(ac, asc, ga, bc, bsc, wq["g"], m, len(cols), k)
+    tol = bound(ac, asc, ga, bc, bsc, wq["g"], m, len(cols), k)
     assert np.all(np.abs(got[:, cols] - want) <= tol)
