@@ -252,8 +252,11 @@ __device__ __forceinline__ uint4 buf_load16(Rsrc r, int off) {
 //            one-round grid, so that all waves sweep the tensor together and
 //            the accesses in flight stay within a compact region; cpw = -2
 //            sweeps from the end of the tensor to its start.
-// Waves are numbered so that each XCD owns one contiguous eighth of the
-// tensor (cpw >= 0) or of every sweep (cpw < 0).
+// With cpw > 0, waves are numbered in dispatch order (consecutive
+// workgroups run on different XCDs; measured on 67.9 M elements: NVFP4
+// quantize 34.7 -> 33.0 us, rotation 84.6 -> 76.6 us, fp32 dequantization
+// 80.5 -> 77.3 us against XCD-contiguous numbering); otherwise each XCD owns
+// one contiguous eighth of the tensor (cpw = 0) or of every sweep (cpw < 0).
 struct WaveRange {
     int64_t c0, step, n, c1;
 };
@@ -262,7 +265,11 @@ template <int WAVES = kWaves, int U = kUnroll>
 __device__ __forceinline__ WaveRange wave_range(int64_t n_chunks, int64_t cpw) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t W = (int64_t)gridDim.x * WAVES;
-    const int64_t wid = (int64_t)xcd_slice(blockIdx.x, gridDim.x) * WAVES + wave;
+    // Short-lived workgroups (cpw > 0) keep the dispatch order, so that the
+    // workgroups in flight on all eight XCDs cover one compact window of the
+    // tensor; one-round grids give each XCD a contiguous part.
+    const int64_t slot = cpw > 0 ? (int64_t)blockIdx.x : (int64_t)xcd_slice(blockIdx.x, gridDim.x);
+    const int64_t wid = slot * WAVES + wave;
     if (cpw < 0) {
         const int64_t groups = (n_chunks + U - 1) / U;
         const int64_t n = wid < groups ? (groups - wid + W - 1) / W : 0;
@@ -1218,7 +1225,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows_wg(RowParams rp) {
     const int nk = (int)((rp.cols + kChunk - 1) / kChunk);  // <= kRowChunks * kWaves
     const QParams& p = rp.q;
     const int64_t G = gridDim.x;
-    const int64_t first_row = xcd_slice(blockIdx.x, gridDim.x);
+    // One row per workgroup: dispatch order; a sweep: XCD-contiguous rows.
+    const int64_t first_row = G >= rp.rows ? (int64_t)blockIdx.x : xcd_slice(blockIdx.x, gridDim.x);
     Acc acc;
     Raw<XT> cur[kRowChunks];
     if (first_row < rp.rows)
