@@ -8,8 +8,8 @@
 // error sums are reduced across the L lanes with DPP quad permutes and row
 // mirrors; nothing goes through LDS on the hot path.  Waves take groups of
 // chunks with every load of a group issued before any use (the split between
-// waves is chosen per kernel, see wave_range), numbered so that each XCD
-// streams one contiguous part of the tensor.  Memory is reached through
+// waves and their numbering across the XCDs are chosen per kernel, see
+// wave_range).  Memory is reached through
 // range-checked buffer resources, so ragged ends need no branches.
 //
 // Arithmetic (the rules the pages leave open are stated in include/fp4q.h):
@@ -252,11 +252,12 @@ __device__ __forceinline__ uint4 buf_load16(Rsrc r, int off) {
 //            one-round grid, so that all waves sweep the tensor together and
 //            the accesses in flight stay within a compact region; cpw = -2
 //            sweeps from the end of the tensor to its start.
-// With cpw > 0, waves are numbered in dispatch order (consecutive
-// workgroups run on different XCDs; measured on 67.9 M elements: NVFP4
-// quantize 34.7 -> 33.0 us, rotation 84.6 -> 76.6 us, fp32 dequantization
-// 80.5 -> 77.3 us against XCD-contiguous numbering); otherwise each XCD owns
-// one contiguous eighth of the tensor (cpw = 0) or of every sweep (cpw < 0).
+// With cpw != 0, waves are numbered in dispatch order (consecutive
+// workgroups run on different XCDs; measured on 67.9 M elements against
+// XCD-contiguous numbering: short-lived NVFP4 quantize 34.7 -> 33.0 us,
+// rotation 84.6 -> 76.6 us, fp32 dequantization 80.5 -> 77.3 us; the sweeps
+// 1-2.5 % faster); with cpw = 0 each XCD owns one contiguous eighth of the
+// tensor.
 struct WaveRange {
     int64_t c0, step, n, c1;
 };
@@ -265,10 +266,11 @@ template <int WAVES = kWaves, int U = kUnroll>
 __device__ __forceinline__ WaveRange wave_range(int64_t n_chunks, int64_t cpw) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t W = (int64_t)gridDim.x * WAVES;
-    // Short-lived workgroups (cpw > 0) keep the dispatch order, so that the
-    // workgroups in flight on all eight XCDs cover one compact window of the
-    // tensor; one-round grids give each XCD a contiguous part.
-    const int64_t slot = cpw > 0 ? (int64_t)blockIdx.x : (int64_t)xcd_slice(blockIdx.x, gridDim.x);
+    // Short-lived workgroups (cpw > 0) and the sweep (cpw < 0) keep the
+    // dispatch order, so that the waves working at one time on all eight XCDs
+    // cover one compact window of the tensor; the balanced split gives each
+    // XCD a contiguous part.
+    const int64_t slot = cpw != 0 ? (int64_t)blockIdx.x : (int64_t)xcd_slice(blockIdx.x, gridDim.x);
     const int64_t wid = slot * WAVES + wave;
     if (cpw < 0) {
         const int64_t groups = (n_chunks + U - 1) / U;
