@@ -106,7 +106,7 @@ def _traffic_plan(workload):
     raise SystemExit(f"no traffic plan for workload {workload}")
 
 
-def write_traffic(workload, fetch_dir, write_dir):
+def write_traffic(workload, fetch_dir, write_dir, out_json=None):
     """Turn two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; csv output, -o
     run) into the workload's traffic record and summary under profiles/.
     The counters read KiB per dispatch; each is scaled by what it reads for
@@ -143,7 +143,8 @@ def write_traffic(workload, fetch_dir, write_dir):
     f_kib = sum(p[3] for p in f_parts)
     w_kib = sum(p[3] for p in w_parts)
     hbm = int(round(f_kib * 1024 * f_scale + w_kib * 1024 * w_scale))
-    src, out_json = TRAFFIC[workload]
+    src, default_json = TRAFFIC[workload]
+    out_json = out_json or default_json
     cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/traffic_{workload}/{c} -o run -- "
             + plan["run"] for c in ("FETCH_SIZE", "WRITE_SIZE")]
     rec = {"kernel": plan["label"], "kernel_source_sha256_16": kernel_source_hash(workload),
