@@ -178,3 +178,48 @@ def test_gemm_decode_unaligned_scales():
         got = fq.fp4_gemm_mxfp4(t(ac), sa[shift:].view(m, k // 32), t(bc), sb[shift:].view(n, k // 32))
         outs.append(got.cpu().numpy())
         assert np.all(np.abs(outs[-1] - want) <= tol), shift
+
+
+def bf16_round(x):
+    """Binary32 values rounded to bf16 (nearest even), as binary32."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).bfloat16().float().numpy()
+
+
+# Many tiles, one K range each: with scale bytes in [125, 127] and K <= 768
+# every partial sum is a multiple of 2^-6 below 2^15, exact in binary32, so
+# bf16 C must be the oracle's product rounded once to bf16.  Shapes: just
+# over one and two workgroups per CU (272 and 306 tiles, the second with a
+# ragged M and N whose rows of C are not whole 16-byte units, so the
+# element-wise epilogue, and a K tail inside the last stage), and four per CU
+# (1024 tiles).  Sampled columns (first and last included), every row.
+@pytest.mark.parametrize("m,n,k", [(4352, 4096, 512), (4100, 4500, 544), (8192, 8192, 768)])
+def test_gemm_many_tiles_exact_bf16(m, n, k):
+    print(f"  case many tiles {m}x{n}x{k}", flush=True)
+    rng = np.random.default_rng([57, m, n, k])
+    ac = rng.integers(0, 256, (m, k // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    asc = rng.integers(125, 128, (m, k // 32), dtype=np.uint8)
+    bsc = rng.integers(125, 128, (n, k // 32), dtype=np.uint8)
+    got = run(ac, asc, bc, bsc, torch.bfloat16)
+    sel = np.sort(rng.choice(n, 64, replace=False))
+    sel = np.unique(np.concatenate([sel, [0, n - 1]]))
+    want = oracle.gemm_mxfp4(ac, asc, bc[sel], bsc[sel], m, len(sel), k)
+    np.testing.assert_array_equal(got[:, sel], bf16_round(want))
+
+
+def test_gemm_full_up_projection_sampled():
+    """8192 tokens x 3584 times the 18944 x 3584 up-projection in bf16: the
+    launch the MLP step times."""
+    import fp4_workloads as wl
+    print("  case 8192x18944x3584 bf16", flush=True)
+    w = wl.qwen7_mlp(0, 1).float().numpy()
+    sampled(8192, 18944, 3584, (58, None, 59), 40, torch.bfloat16, w=w)
+
+
+def test_gemm_full_down_projection_sampled():
+    """8192 tokens x 18944 times the 3584 x 18944 down-projection in bf16 (74
+    K stages per tile, one K range)."""
+    import fp4_workloads as wl
+    print("  case 8192x3584x18944 bf16", flush=True)
+    w = wl.qwen7_mlp(1, 1).float().numpy()
+    sampled(8192, 3584, 18944, (60, None, 61), 16, torch.bfloat16, w=w)
