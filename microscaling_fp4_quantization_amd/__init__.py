@@ -241,8 +241,10 @@ _gemm_workspaces = {}
 
 
 def gemm_workspace(device, nbytes: int) -> torch.Tensor:
-    """A device workspace of at least `nbytes` for fp4_gemm_mxfp4, kept per
-    device and grown on demand (shared by calls made on one stream)."""
+    """A device workspace of at least `nbytes` for the GEMMs, kept per device
+    and grown on demand.  Calls that use it must be ordered (one stream): two
+    products running at once on different streams need workspaces of their own
+    (pass ``ws=``)."""
     key = torch.device(device).index
     ws = _gemm_workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
@@ -303,6 +305,11 @@ def fp4_gemm_nvfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, a_g: Optional[
 def fp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, fmt: int, block: int,
                    g: Optional[torch.Tensor] = None, rotate: int = 0,
                    out_dtype=torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x_hat from codes and scale bytes (fmt FMT_MXFP4, FMT_UE4M3 or FMT_UE5M3;
+    ``g`` the one-element per-tensor scale of UE4M3 codes, None for 1, ignored
+    for the other formats), back in the original domain when ``rotate`` is the
+    block size the codes were rotated with; float32 or bf16 (round to nearest
+    even)."""
     codes = _matrix(codes, "codes")
     rows, cols = codes.shape[0], codes.shape[1] * 2
     if out is None:
@@ -328,6 +335,8 @@ def fp4_block_mse(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, fm
 
 
 def hadamard_block_rotate(x: torch.Tensor, n: int, out: Optional[torch.Tensor] = None):
+    """Each run of ``n`` (16 or 32) consecutive elements of a row times the
+    normalized Sylvester Hadamard matrix, in float32 (its own inverse)."""
     x = _matrix(x)
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
