@@ -262,7 +262,8 @@ WORKLOADS = {
          "format": "NVFP4: block 16, UE4M3 scales, dynamic FP32 per-tensor scale",
          "outputs": "codes + scales + per-block MSE + three-term error split"},
         _qwen7_tensors, [Spec("nv16_dyn", "nv", 16, 1, 1)], 50, 5,
-        ("2 of the 6 tensors (18944x3584, sigma 0.01 and 0.02), whole", 2, 1, 0)),
+        ("4 of the 6 tensors (the three 18944x3584 ones and 3584x18944 with sigma 0.01), whole",
+         4, 1, 0)),
     "qwen05": Workload(
         "qwen2.5-0.5b-up-mxfp4-fp32",
         {"tensors": "1 fp32 4864x896, N(0, 0.02), seed 0",
@@ -323,7 +324,7 @@ GEMM_METRIC = ("TFLOP/s of MXFP4 x MXFP4 products (W4A4 Qwen2.5-7B MLP, 8192 tok
                "activation quantization included); % of dense FP4 matrix-core peak")
 MFMA_FP4_PEAK_TFLOPS = 10100.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-GEMM_SAMPLE_ROWS = 8
+GEMM_SAMPLE_ROWS = 12
 
 
 def gemm_main(args, steps, warmup):
