@@ -1,4 +1,5 @@
-// fp4q_gemm.hip -- MXFP4 GEMM on the gfx950 scaled matrix cores.
+// fp4q_gemm.hip -- FP4 GEMMs on gfx950: MXFP4 on the scaled matrix cores,
+// NVFP4 on the bf16 matrix cores from operands decoded in LDS or registers.
 //
 // C (M x N) = A_hat (M x K) * B_hat^T, where A and B are MXFP4 matrices in the
 // layout the quantize kernels write: row-major E2M1 codes two per byte (element
@@ -24,6 +25,11 @@
 //                 advances 256 at a time through two LDS stages;
 //  k_gemm_decode  products of at most 32 rows of A: one pass over B, 32 rows of
 //                 B and a range of K per wave (no scale packing);
+//  k_gemm_nvfp4   the NVFP4 product (UE4M3 scales per 16, a per-tensor scale
+//                 per operand) in the 256 x 256 tiling, each stage decoded to
+//                 bf16 in LDS for the bf16 matrix cores;
+//  k_gemm_decode_nv  its decode-sized form (k_gemm_decode's units, operands
+//                 decoded to bf16 in registers);
 //  k_splitk_reduce  adds the binary32 partial products of K ranges when a
 //                 product is split along K.
 //
