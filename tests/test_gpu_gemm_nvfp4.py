@@ -149,3 +149,43 @@ def test_nv_gemm_decode_down_projection_sampled():
     want = oracle.gemm_nvfp4(ac, asc, ga, bc, bsc, wq["g"], m, len(cols), k)
     tol = bound(ac, asc, ga, bc, bsc, wq["g"], m, len(cols), k)
     assert np.all(np.abs(got[:, cols] - want) <= tol)
+
+
+# Many tiles, one K range each, bf16 C: with g = 1, scale bytes in [0x38,
+# 0x3F] and K = 128 every partial sum is exact in binary32 (as above), so C
+# must be the oracle's product rounded once to bf16.  Just over one
+# workgroup per CU (289 tiles, ragged M and N with rows of C that are not
+# whole 16-byte units) and four per CU (1024 tiles).  Sampled columns (first
+# and last included), every row.
+@pytest.mark.parametrize("m,n,k", [(4100, 4300, 128), (8192, 8192, 128)])
+def test_nv_gemm_many_tiles_exact_bf16(m, n, k):
+    print(f"  case many tiles {m}x{n}x{k} nvfp4", flush=True)
+    rng = np.random.default_rng([81, m, n, k])
+    ac = rng.integers(0, 256, (m, k // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    asc = rng.integers(0x38, 0x40, (m, k // 16), dtype=np.uint8)
+    bsc = rng.integers(0x38, 0x40, (n, k // 16), dtype=np.uint8)
+    got = run(ac, asc, None, bc, bsc, None, torch.bfloat16)
+    sel = np.unique(np.concatenate([rng.choice(n, 64, replace=False), [0, n - 1]]))
+    want = oracle.gemm_nvfp4(ac, asc, 1.0, bc[sel], bsc[sel], 1.0, m, len(sel), k)
+    want_bf16 = torch.from_numpy(want.astype(np.float32)).bfloat16().float().numpy()
+    np.testing.assert_array_equal(got[:, sel], want_bf16)
+
+
+def test_nv_gemm_full_up_projection_sampled():
+    """8192 tokens x 3584 times the NVFP4 18944 x 3584 up-projection in bf16:
+    the NVFP4 launch the MLP benchmark times."""
+    import fp4_workloads as wl
+    print("  case 8192x18944x3584 nvfp4 bf16", flush=True)
+    m, n, k = 8192, 18944, 3584
+    w = wl.qwen7_mlp(0, 1).float().numpy()
+    wq = oracle.quantize(w, oracle.FMT_UE4M3, 16, oracle.GMODE_DYNAMIC)
+    ac, asc, ga = operand(m, k, 82, spread=2)
+    got = run(ac, asc, ga, wq["codes"], wq["scales"], wq["g"], torch.bfloat16)
+    cols = np.sort(np.random.default_rng(83).choice(n, 32, replace=False))
+    bc, bsc = wq["codes"][cols], wq["scales"][cols]
+    want = oracle.gemm_nvfp4(ac, asc, ga, bc, bsc, wq["g"], m, len(cols), k)
+    tol = bound(ac, asc, ga, bc, bsc, wq["g"], m, len(cols), k) + np.abs(want) * 2.0 ** -8
+    err = np.abs(got[:, cols] - want)
+    i = np.unravel_index(np.argmax(err - tol), err.shape)
+    assert np.all(err <= tol), f"at {i}: got {got[:, cols][i]!r} want {want[i]!r} tol {tol[i]!r}"
