@@ -145,8 +145,9 @@ def write_traffic(workload, fetch_dir, write_dir, out_json=None):
     hbm = int(round(f_kib * 1024 * f_scale + w_kib * 1024 * w_scale))
     src, default_json = TRAFFIC[workload]
     out_json = out_json or default_json
-    cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/traffic_{workload}/{c} -o run -- "
-            + plan["run"] for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    rel = lambda d: os.path.relpath(os.path.abspath(d), ROOT)
+    cmds = [f"rocprofv3 --pmc {c} --output-format csv -d {rel(d)} -o run -- " + plan["run"]
+            for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir))]
     rec = {"kernel": plan["label"], "kernel_source_sha256_16": kernel_source_hash(workload),
            "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
@@ -155,8 +156,8 @@ def write_traffic(workload, fetch_dir, write_dir, out_json=None):
     json.dump(rec, open(out_json, "w"), indent=1)
     lines = [f"# HBM traffic per launch: bench.py workload `{workload}`", "",
              "Commands (from the repository root on the MI355X box), one counter per run, then",
-             f"`python bench.py --workload {workload} --write-traffic gpurun_out/traffic_{workload}"
-             f"/FETCH_SIZE gpurun_out/traffic_{workload}/WRITE_SIZE` to write this file:", "", "```",
+             f"`python bench.py --workload {workload} --write-traffic {rel(fetch_dir)} {rel(write_dir)}`"
+             " to write this file:", "", "```",
              *cmds, "```", "",
              f"The calibration copy moves {plan['calib_bytes']:,} bytes each way; the counters read "
              f"{f_cal:,.1f} KiB (fetch) and {w_cal:,.1f} KiB (write) for it, so the scales are "
@@ -660,8 +661,8 @@ def main():
         write_traffic(args.workload, *args.write_traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by rows with one max- and one sum-all-reduce; see DESIGN.md)",
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path would shard by rows, with one max- and one sum-all-reduce)",
               file=sys.stderr)
         sys.exit(2)
     if args.workload == "gemm":
