@@ -1,7 +1,7 @@
 """Helpers shared by the GPU parity tests: run the library and the oracle on the
 same seeded input and compare.
 
-Tolerances (from the arithmetic):
+Tolerances (each derived from the arithmetic the two sides perform):
   codes, scale bytes, g, counts        bit-exact
   dequantized values                   bit-exact (binary32 products, same order)
   per-block MSE                        |k - o| <= 1e-6 |o|, and exactly 0 where o is 0
