@@ -175,6 +175,22 @@ def test_error_split_matches_numpy(orc, name, fmt, b, rot, kind):
     np.testing.assert_array_equal(cnt2, r["counts"])
 
 
+def test_blocks_run_along_rows(orc):
+    """Blocks are 32 consecutive elements of one row: every E8M0 byte equals
+    frexp's exponent of that row segment's absmax (floor(log2 m) - 2 + 127),
+    computed in numpy, and quantizing the transpose gives other bytes."""
+    rng = np.random.default_rng(90)
+    x = (rng.standard_normal((64, 96)) * 2.0 ** rng.integers(-6, 7, (64, 96))).astype(np.float32)
+    got = orc.quantize(x, orc.FMT_MXFP4, 32)["scales"]
+    m = np.abs(x).reshape(64, 3, 32).max(axis=2)
+    e = np.frexp(m)[1]
+    want = np.where(m > 0, np.clip(e - 1 - 2 + 127, 0, 254), 0).astype(np.uint8)
+    np.testing.assert_array_equal(got, want)
+    xt = np.ascontiguousarray(x[:, :64].T)  # 64 x 64: same block count, other direction
+    assert not np.array_equal(orc.quantize(xt, orc.FMT_MXFP4, 32)["scales"].T.reshape(-1),
+                              got[:, :2].reshape(-1))
+
+
 def test_mx_dequant_is_exact_power_of_two_product(orc):
     rng = np.random.default_rng(4)
     x = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-20, 20, (64, 1)))).astype(np.float32)
