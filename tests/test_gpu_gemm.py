@@ -207,6 +207,23 @@ def test_gemm_many_tiles_exact_bf16(m, n, k):
     np.testing.assert_array_equal(got[:, sel], bf16_round(want))
 
 
+def test_gemm_many_tiles_exact_f32():
+    """512 tiles of binary32 C, one K range each (the two-pass epilogue
+    through LDS straight into C): bit-exact against the oracle, sampled
+    columns, every row (sums exact as above)."""
+    m, n, k = 8192, 4096, 512
+    print(f"  case many tiles {m}x{n}x{k} f32", flush=True)
+    rng = np.random.default_rng([62, m, n, k])
+    ac = rng.integers(0, 256, (m, k // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    asc = rng.integers(125, 128, (m, k // 32), dtype=np.uint8)
+    bsc = rng.integers(125, 128, (n, k // 32), dtype=np.uint8)
+    got = run(ac, asc, bc, bsc)
+    sel = np.unique(np.concatenate([rng.choice(n, 64, replace=False), [0, n - 1]]))
+    want = oracle.gemm_mxfp4(ac, asc, bc[sel], bsc[sel], m, len(sel), k)
+    np.testing.assert_array_equal(got[:, sel], want.astype(np.float32))
+
+
 def test_gemm_full_up_projection_sampled():
     """8192 tokens x 3584 times the 18944 x 3584 up-projection in bf16: the
     launch the MLP step times."""
