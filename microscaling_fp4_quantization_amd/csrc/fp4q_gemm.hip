@@ -115,18 +115,29 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
 // One workgroup per (fragment, run of 16 stages): it copies the fragment's
 // 32 rows x 128 scale bytes of those stages into LDS (each row's bytes are
 // contiguous in memory), then writes the 16 x 256 packed bytes, which are
-// contiguous too.
+// contiguous too.  One launch packs both operands: the first workgroups take
+// A's fragments, the rest B's.
 constexpr int kPackStages = 16;
 constexpr int kPackThreads = 256;
 
-__global__ __launch_bounds__(kPackThreads) void k_pack_scales(const uint8_t* __restrict__ sc,
-                                                              int64_t rows, int64_t kblocks,
-                                                              int64_t stages, int64_t frags,
-                                                              uint32_t* __restrict__ out) {
+struct PackOperand {
+    const uint8_t* sc;  // rows x kblocks scale bytes
+    int64_t rows;
+    int64_t groups;     // workgroups: fragments x runs of stages
+    uint32_t* out;      // packed scales
+};
+
+__global__ __launch_bounds__(kPackThreads) void k_pack_scales(PackOperand pa, PackOperand pb,
+                                                              int64_t kblocks, int64_t stages) {
     __shared__ uint8_t tile[kFrag][kPackStages * 8 + 4];  // padded rows
+    const bool second = blockIdx.x >= pa.groups;
+    const uint8_t* __restrict__ sc = second ? pb.sc : pa.sc;
+    const int64_t rows = second ? pb.rows : pa.rows;
+    uint32_t* __restrict__ out = second ? pb.out : pa.out;
+    const int64_t g = second ? blockIdx.x - pa.groups : blockIdx.x;
     const int64_t runs = (stages + kPackStages - 1) / kPackStages;
-    const int64_t f = blockIdx.x / runs;
-    const int64_t s0 = (blockIdx.x % runs) * kPackStages;
+    const int64_t f = g / runs;
+    const int64_t s0 = (g % runs) * kPackStages;
     const int t = threadIdx.x;
     // Load: thread t moves row t / 8, bytes 16 (t % 8) .. + 15 of the run.
     {
@@ -1310,17 +1321,12 @@ int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
                  (long long)j.M, (long long)j.N, (long long)j.K);
         return (int)hipErrorInvalidConfiguration;
     }
-    const struct {
-        const uint8_t* sc;
-        int64_t rows;
-        uint8_t* out;
-    } packs[2] = {{j.a_scales, j.M, a_pack}, {j.b_scales, j.N, b_pack}};
-    for (const auto& pk : packs) {
-        const int64_t groups = frags_of(pk.rows) * ((S + kPackStages - 1) / kPackStages);
-        if (groups == 0) continue;
-        hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)groups), dim3(kPackThreads), 0, stream, pk.sc,
-                           pk.rows, kb, S, frags_of(pk.rows), reinterpret_cast<uint32_t*>(pk.out));
-    }
+    const int64_t runs = (S + kPackStages - 1) / kPackStages;
+    const PackOperand pa{j.a_scales, j.M, frags_of(j.M) * runs, reinterpret_cast<uint32_t*>(a_pack)};
+    const PackOperand pb{j.b_scales, j.N, frags_of(j.N) * runs, reinterpret_cast<uint32_t*>(b_pack)};
+    if (pa.groups + pb.groups > 0)  // none when K = 0
+        hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)(pa.groups + pb.groups)), dim3(kPackThreads), 0,
+                           stream, pa, pb, kb, S);
     const int sp = splits_for(j.M, j.N, j.K);
     float* partial = partial_area;
     GParams p{j.a_codes, j.b_codes, a_pack, b_pack, j.M, j.N, j.K, S, j.c, j.ct, sp, partial};

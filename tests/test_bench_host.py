@@ -19,13 +19,14 @@ def write_csv(d, counter, rows):
 
 def test_traffic_record_scales_counters_by_the_calibration_copy(tmp_path, monkeypatch):
     plan = bench._traffic_plan("gemm")
-    (gemm_name, gemm_grid), (_, pa), (_, pb) = plan["parts"]
+    (gemm_name, gemm_grid), (_, pgrid) = plan["parts"]
     calib = plan["calib_bytes"]
     # Fetch counters read half the bytes (a 2x scale), write counters all of them.
-    fetch = [(1, pa, "k_pack_scales(x)", 100.0), (2, pb, "k_pack_scales(y)", 300.0),
+    # A pack dispatch of another grid (another product's) is not counted.
+    fetch = [(1, pgrid, "k_pack_scales(x)", 400.0), (2, pgrid + 256, "k_pack_scales(y)", 7.0),
              (3, gemm_grid, "k_gemm_mxfp4(GParams)", 1000.0), (4, gemm_grid, "k_gemm_mxfp4(GParams)", 3000.0),
              (5, 64, "__amd_rocclr_copyBuffer", 1.0), (9, 64, "__amd_rocclr_copyBuffer", calib / 2048)]
-    write = [(1, pa, "k_pack_scales(x)", 10.0), (2, pb, "k_pack_scales(y)", 30.0),
+    write = [(1, pgrid, "k_pack_scales(x)", 40.0), (2, pgrid + 256, "k_pack_scales(y)", 7.0),
              (3, gemm_grid, "k_gemm_mxfp4(GParams)", 500.0), (4, gemm_grid, "k_gemm_mxfp4(GParams)", 500.0),
              (9, 64, "__amd_rocclr_copyBuffer", calib / 1024)]
     write_csv(tmp_path / "F", "FETCH_SIZE", fetch)
@@ -33,7 +34,7 @@ def test_traffic_record_scales_counters_by_the_calibration_copy(tmp_path, monkey
     out = tmp_path / "rec.json"
     bench.write_traffic("gemm", str(tmp_path / "F"), str(tmp_path / "W"), str(out))
     rec = json.load(open(out))
-    # per launch: fetch (100 + 300 + mean(1000, 3000)) KiB x 2, write (10 + 30 + 500) KiB x 1
+    # per launch: fetch (400 + mean(1000, 3000)) KiB x 2, write (40 + 500) KiB x 1
     assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
     assert rec["hbm_bytes_per_launch"] == (2400 * 2 + 540) * 1024
     assert rec["kernel_source_sha256_16"] == bench.kernel_source_hash("gemm")
