@@ -28,7 +28,11 @@
 //   Errors: e = x - x_hat in binary32 (exact for MXFP4 and for unsaturated
 //   UE4M3 blocks), squared and summed in binary64.  The max-element term is
 //   computed from the block maximum m itself (every element attaining m has
-//   the same error), the non-max term as block SSE minus it.
+//   the same error).  The non-max term is block SSE minus it when that
+//   difference keeps at least 2^-12 of the SSE (then it is within b 2^-41 of
+//   the separate sum, relatively); otherwise it is summed separately, element
+//   by element, leaving out the lowest-index element attaining m (see
+//   needs_separate_sum).
 //   Tensor terms: per-workgroup binary64 partials, summed in a fixed order by a
 //   one-workgroup finalize kernel, so results are bit-reproducible.
 #include <hip/hip_runtime.h>
@@ -125,6 +129,14 @@ constexpr int kAmaxWaves = FP4Q_AMAX_WAVES;
 constexpr int kAmaxThreads = kWave * kAmaxWaves;
 constexpr int kGridRounds = FP4Q_GRID_ROUNDS;
 
+// The quantize and block-MSE kernels are held to 80 scalar registers.  At 96
+// (the next allocation granule) fewer of their waves fit per SIMD on gfx950
+// (measured on 70.8 M-element launches: mean occupancy 19.9 -> 14.0 waves per
+// CU and 36 -> 45 us for MXFP4 with per-block MSE), while the occupancy query
+// that sizes the one-round grids does not see that limit.  The few scalars
+// over the cap go to VGPR lanes.
+#define FP4Q_SGPR_CAP __attribute__((amdgpu_num_sgpr(80)))
+
 constexpr int kFmtMx = 0;
 constexpr int kFmtUe4m3 = 1;
 constexpr int kFmtUe5m3 = 2;
@@ -164,6 +176,16 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
     if constexpr (L >= 8) v = max(v, dpp_u32<kRowHalfMirror>(v));
     if constexpr (L >= 16) v = max(v, dpp_u32<kRowMirror>(v));
     if constexpr (L >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+    return v;
+}
+
+template <int L>
+__device__ __forceinline__ uint32_t group_min(uint32_t v) {
+    if constexpr (L >= 2) v = min(v, dpp_u32<kQuadXor1>(v));
+    if constexpr (L >= 4) v = min(v, dpp_u32<kQuadXor2>(v));
+    if constexpr (L >= 8) v = min(v, dpp_u32<kRowHalfMirror>(v));
+    if constexpr (L >= 16) v = min(v, dpp_u32<kRowMirror>(v));
+    if constexpr (L >= 32) v = min(v, (uint32_t)__shfl_xor((int)v, 16));
     return v;
 }
 
@@ -291,14 +313,22 @@ __device__ __forceinline__ WaveRange wave_range(int64_t n_chunks, int64_t cpw) {
 
 // Loads the kUnroll chunks starting at chunk c; chunks at or past c1 (another
 // wave's) and elements past n read as zeros.
+// Input window of the U-chunk group starting at chunk c, clipped at chunk c1
+// and at element n.
 template <int XT, int U = kUnroll>
-__device__ __forceinline__ void load_group(Raw<XT> (&raw)[U], const void* x, int64_t n,
-                                           int64_t c, int64_t c1, int lane) {
+__device__ __forceinline__ Rsrc group_input(const void* x, int64_t n, int64_t c, int64_t c1) {
     constexpr int E = XT == 0 ? 2 : 4;
     const int64_t first = c * kChunk;
     int64_t avail = (c1 - c < U ? c1 - c : U) * kChunk;
     if (avail > n - first) avail = n - first;
-    const Rsrc r = make_rsrc(static_cast<const char*>(x) + first * E, avail * E);
+    return make_rsrc(static_cast<const char*>(x) + first * E, avail * E);
+}
+
+template <int XT, int U = kUnroll>
+__device__ __forceinline__ void load_group(Raw<XT> (&raw)[U], const void* x, int64_t n,
+                                           int64_t c, int64_t c1, int lane) {
+    constexpr int E = XT == 0 ? 2 : 4;
+    const Rsrc r = group_input<XT, U>(x, n, c, c1);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if constexpr (XT == 0) {
@@ -498,27 +528,93 @@ __device__ __forceinline__ float requant_ue(float m, const UeScale& s) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0)[0] * s.d;
 }
 
+// Relative block MSE, sse / ss rounded to binary32 (0 when ss = 0).  The
+// reciprocal of ss comes from the hardware estimate and two Newton steps (each
+// squares the relative error), so sse * r is within about 2^-51 of the exact
+// quotient before the final rounding: the result is the correctly rounded
+// quotient or, within 2^-51 of a rounding boundary, its neighbour (one binary32
+// ulp).  ss is a sum of squares of binary32 values, so it lies in [2^-298,
+// 2^264] when positive and neither it nor its reciprocal leaves the normal
+// binary64 range.  This takes about half the instructions of the IEEE division.
+__device__ __forceinline__ float rel_mse(double sse, double ss) {
+    double r = __builtin_amdgcn_rcp(ss);
+    r = fma(r, fma(-ss, r, 1.0), r);
+    r = fma(r, fma(-ss, r, 1.0), r);
+    return ss > 0.0 ? (float)(sse * r) : 0.0f;
+}
+
 // ------------------------------------------------------------ tensor terms
 struct Acc {
     double nonmax = 0.0, max = 0.0, zero = 0.0, sumsq = 0.0;
     uint32_t nzero = 0;  // per lane: at most one per chunk the wave processes
+    uint32_t fixup = 0;  // wave-uniform: a block's separate non-max sum was deferred
 };
 
+// How a chunk's blocks whose non-max term needs the separate sum
+// (needs_separate_sum) are handled.  kSepInline sums them on the spot.
+// kSepDefer adds 0 for them and raises acc.fixup; the wave then runs its range
+// again in kSepFixup, which stores nothing and adds only those blocks'
+// separate sums.  Deferring keeps that rarely run code out of the streaming
+// loop (inline, its mere presence cost 5-9 us per 70.8 M-element launch).
+constexpr int kSepInline = 0, kSepDefer = 1, kSepFixup = 2;
+
+// Index within this lane (0..7) of the block's lowest-index element attaining
+// the block maximum m, or 8 when another lane holds it.  Indices are kept
+// lane-local so that no per-lane index constants stay live in registers.
+template <int L>
+__device__ __forceinline__ int lowest_max_in_lane(const float (&v)[8], float m, int gl) {
+    uint32_t first = 8u;
+#pragma unroll
+    for (int i = 7; i >= 0; --i)
+        if (fabsf(v[i]) == m) first = (uint32_t)i;
+    const uint32_t key = group_min<L>(first == 8u ? 0xFFu : (uint32_t)gl * kLaneElems + first);
+    return (key >> 3) == (uint32_t)gl ? (int)(key & 7u) : 8;
+}
+
+// The separate non-max sum from a lane's values v and dequantized values xh:
+// the squared errors of every element but the lowest-index one attaining the
+// block maximum m, summed in binary64 (each e^2 is exact there).  Every lane of
+// the block gets the same total.
+template <int L>
+__device__ __forceinline__ double nonmax_sum(const float (&v)[8], const float (&xh)[8], float m,
+                                             int gl) {
+    const int skip = lowest_max_in_lane<L>(v, m, gl);
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const double e = (double)(v[i] - xh[i]);
+        if (i != skip) s = fma(e, e, s);
+    }
+    return group_sum<L>(s);
+}
+
+// The non-max term of a block that is not zero-rounded is formed as nm =
+// sse - M from its SSE and its max-element term M (one of the SSE's summands,
+// so sse >= M).  sse is a binary64 sum of b exact squares, within b 2^-53 of
+// the exact SSE, so when nm keeps at least 2^-12 of sse it is within b 2^-41
+// (< 2^-33 for b <= 256) of the exact non-max sum, relatively.  Blocks whose
+// maximum carries more of the error than that (rare: the other elements sit on
+// or next to the grid) take the separate sum instead (nonmax_sum), in a
+// wave-uniform branch or a fix-up pass (kSepDefer).  The decision is the same on every lane of a block.
+__device__ __forceinline__ bool needs_separate_sum(bool zero, double sse, double nm) {
+    return !zero && nm < sse * 0x1p-12;
+}
+
 // Adds one block's terms.  A zero-rounded block (m > 0, every x_hat = 0)
-// contributes its SSE to the zero-rounding term; any other block splits its
-// SSE into the max-element term and the rest.  Zero-rounded blocks are rare, so
-// the selects run only in waves that hold one; the plain adds give the same
-// sums for every other block.
+// contributes its SSE to the zero-rounding term; any other block contributes
+// its max-element term and its non-max term.  Zero-rounded
+// blocks are rare, so the selects run only in waves that hold one; the plain
+// adds give the same sums for every other block.
 __device__ __forceinline__ void add_block(Acc& acc, bool zero, double sse, double mterm,
-                                          double ss) {
+                                          double nonmax, double ss) {
     if (__builtin_amdgcn_ballot_w64(zero)) {
         acc.zero += zero ? sse : 0.0;
         acc.nzero += zero ? 1u : 0u;
         acc.max += zero ? 0.0 : mterm;
-        acc.nonmax += zero ? 0.0 : sse - mterm;
+        acc.nonmax += zero ? 0.0 : nonmax;
     } else {
         acc.max += mterm;
-        acc.nonmax += sse - mterm;
+        acc.nonmax += nonmax;
     }
     acc.sumsq += ss;
 }
@@ -676,14 +772,80 @@ __device__ __forceinline__ QOut group_outputs(const QParams& p, int64_t c, int64
     return o;
 }
 
+// One lane's raw values of the chunk that starts xoff bytes into window r.
+template <int XT>
+__device__ __forceinline__ Raw<XT> load_chunk(Rsrc r, int xoff, int lane) {
+    Raw<XT> raw;
+    if constexpr (XT == 0) {
+        raw.w = buf_load16(r, xoff + lane * 16);
+    } else {
+        raw.a = buf_load16(r, xoff + lane * 32);
+        raw.b = buf_load16(r, xoff + lane * 32 + 16);
+    }
+    return raw;
+}
+
+// The separate non-max sum of a chunk's blocks (see needs_separate_sum) for
+// kSepInline, with the values read again from memory and their codes and
+// dequantized values formed again, two elements at a time, as quantize_chunk
+// forms them under the block's scale: its power of two (MXFP4) or its decode
+// scale d (UE formats; the IEEE quotient x / d is the value the corrected
+// quotient gives where that is used).  Only waves holding a block that needs
+// it run this, and it keeps little live, since the kernels that sum inline
+// hold a whole prefetched row group in registers.
+template <int XT, int FMT, int B, int ROT>
+__device__ __forceinline__ double nonmax_reread(Rsrc xin, int xoff, int lane, int gl, float m,
+                                                float scale) {
+    constexpr int L = B / kLaneElems;
+    const Raw<XT> raw = load_chunk<XT>(xin, xoff, lane);
+    float v[8];
+    unpack<XT>(raw, v);
+    if constexpr (ROT != 0) rotate8<ROT>(v, gl);
+    const int skip = lowest_max_in_lane<L>(v, m, gl);
+    const float sc = FMT == kFmtMx ? scale : 1.0f;
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+        // One pair at a time: the barrier keeps the scheduler from forming
+        // all pairs at once (which would raise the kernel's register count).
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ROT == 0) {
+            float w[8];
+            unpack<XT>(raw, w);
+            v[j] = w[j];
+            v[j + 1] = w[j + 1];
+        }
+        uint32_t c;
+        if constexpr (FMT == kFmtMx) {
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[j], v[j + 1], sc, 0);
+        } else {
+            const float y0 = v[j] / scale, y1 = v[j + 1] / scale;
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, 1.0f, 0);
+        }
+        const float2_t h = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, sc, 0);
+        float x0 = h[0], x1 = h[1];
+        if constexpr (FMT != kFmtMx) {
+            x0 = x0 * scale;
+            x1 = x1 * scale;
+        }
+        const double e0 = (double)(v[j] - x0), e1 = (double)(v[j + 1] - x1);
+        if (skip != j) s = fma(e0, e0, s);
+        if (skip != j + 1) s = fma(e1, e1, s);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    return group_sum<L>(s);
+}
+
 // One 512-element chunk: lane `lane` holds elements 8 lane .. 8 lane + 7 of it
 // and block lane / L of it (gl = lane % L).  Every lane of a block ends with the
 // block's results; the block's first lane stores its scale and MSE, and every
 // lane adds the block's terms to acc (the caller keeps only the first lanes').
-template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ>
+// The chunk's input starts xoff bytes into the window xin (read again only for
+// the separate non-max sum in kSepInline).  SEP: see kSepInline.
+template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ, int SEP = kSepInline>
 __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const QOut& o,
                                                const QParams& p, const UeCtx& ue, int lane,
-                                               int gl, Acc& acc) {
+                                               int gl, Acc& acc, Rsrc xin, int xoff) {
     constexpr int L = B / kLaneElems;
     constexpr int kBlocks = kChunk / B;
     constexpr int kSt = quant_store_policy<FMT>();
@@ -748,8 +910,12 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
         }
     }
     const int blk = u * kBlocks + lane / L;  // block index within the group
-    __builtin_amdgcn_raw_buffer_store_b32(cw, o.codes, (u * kChunk + lane * kLaneElems) / 2, 0, kSt);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, o.scales, gl == 0 ? blk : kDropped, 0, kSt);
+    if constexpr (SEP != kSepFixup) {
+        __builtin_amdgcn_raw_buffer_store_b32(cw, o.codes, (u * kChunk + lane * kLaneElems) / 2, 0,
+                                              kSt);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, o.scales, gl == 0 ? blk : kDropped, 0,
+                                             kSt);
+    }
     if constexpr (ERR) {
         double sse = 0.0, ss = 0.0;
 #pragma unroll
@@ -763,10 +929,10 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
         }
         sse = group_sum<L>(sse);
         if constexpr (SUMSQ) ss = group_sum<L>(ss);
-        if (p.block_mse) {
+        if (SEP != kSepFixup && p.block_mse) {
             float mse;
             // Relative MSE always comes with the sum of squares (SUMSQ).
-            if (SUMSQ && p.mse_kind == kMseRel) mse = ss > 0.0 ? (float)(sse / ss) : 0.0f;
+            if (SUMSQ && p.mse_kind == kMseRel) mse = rel_mse(sse, ss);
             else mse = (float)(sse * (1.0 / B));
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mse), o.mse,
                                                   gl == 0 ? blk * 4 : kDropped, 0, kSt);
@@ -776,12 +942,34 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
         // the terms are not formed at all (a wave-uniform branch).
         if (p.so.stats) {
             const double em = (double)(m - xh_m);
-            add_block(acc, (m > 0.0f) && (xh_m == 0.0f), sse, em * em, ss);
+            const double mterm = em * em;
+            const bool zero = (m > 0.0f) && (xh_m == 0.0f);
+            double nm = sse - mterm;
+            const bool sep = needs_separate_sum(zero, sse, nm);
+            if constexpr (SEP == kSepInline) {
+                if (__builtin_amdgcn_ballot_w64(sep)) {
+                    const float scale = FMT == kFmtMx ? __uint_as_float(sbyte << 23)
+                                                      : ue.tab[sbyte].x;
+                    const double s2 = nonmax_reread<XT, FMT, B, ROT>(xin, xoff, lane, gl, m, scale);
+                    if (sep) nm = s2;
+                }
+            } else if constexpr (SEP == kSepDefer) {
+                if (sep) nm = 0.0;
+                if (__builtin_amdgcn_ballot_w64(sep)) acc.fixup = 1u;
+            } else {
+                if (__builtin_amdgcn_ballot_w64(sep)) {
+                    const double s2 = nonmax_sum<L>(v, xh, m, gl);
+                    if (sep) acc.nonmax += s2;
+                }
+                return;
+            }
+            add_block(acc, zero, sse, mterm, nm, ss);
         }
     }
 }
 
-// Scale search on one chunk.  Candidates are the max-based scale code c0 (the
+// Scale search on one chunk (SEP: kSepDefer or kSepFixup, see kSepInline).
+// Candidates are the max-based scale code c0 (the
 // code quantize_chunk takes) and its neighbours c0 + j, 0 < |j| <= radius,
 // inside [0, max_byte]; consecutive codes are consecutive scale values in all
 // three formats.  Each is scored by the block's SSE in binary64, with every
@@ -792,7 +980,7 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
 // replaces the best so far only when its SSE is below best - best * 2^-40, so
 // near-ties keep the code closest to c0.  Outputs are quantize_chunk's, for
 // the chosen code.
-template <int XT, int FMT, int B, int ROT, bool SUMSQ>
+template <int XT, int FMT, int B, int ROT, bool SUMSQ, int SEP>
 __device__ __forceinline__ void search_chunk(const Raw<XT>& raw, int u, const QOut& o,
                                              const QParams& p, const UeCtx& ue, int lane,
                                              int gl, Acc& acc) {
@@ -871,18 +1059,45 @@ __device__ __forceinline__ void search_chunk(const Raw<XT>& raw, int u, const QO
         ss = group_sum<L>(ss);
     }
     const int blk = u * kBlocks + lane / L;
-    __builtin_amdgcn_raw_buffer_store_b32(best_cw, o.codes, (u * kChunk + lane * kLaneElems) / 2, 0, kSt);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)best_byte, o.scales, gl == 0 ? blk : kDropped, 0, kSt);
-    if (p.block_mse) {
+    if constexpr (SEP != kSepFixup) {
+        __builtin_amdgcn_raw_buffer_store_b32(best_cw, o.codes, (u * kChunk + lane * kLaneElems) / 2,
+                                              0, kSt);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)best_byte, o.scales, gl == 0 ? blk : kDropped,
+                                             0, kSt);
+    }
+    if (SEP != kSepFixup && p.block_mse) {
         float mse;
-        if (SUMSQ && p.mse_kind == kMseRel) mse = ss > 0.0 ? (float)(best / ss) : 0.0f;
+        if (SUMSQ && p.mse_kind == kMseRel) mse = rel_mse(best, ss);
         else mse = (float)(best * (1.0 / B));
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mse), o.mse,
                                               gl == 0 ? blk * 4 : kDropped, 0, kSt);
     }
     if (p.so.stats) {
         const double em = (double)(m - best_xm);
-        add_block(acc, (m > 0.0f) && (best_xm == 0.0f), best, em * em, ss);
+        const double mterm = em * em;
+        const bool zero = (m > 0.0f) && (best_xm == 0.0f);
+        double nm = best - mterm;
+        const bool sep = needs_separate_sum(zero, best, nm);
+        if constexpr (SEP == kSepDefer) {
+            if (sep) nm = 0.0;
+            if (__builtin_amdgcn_ballot_w64(sep)) acc.fixup = 1u;
+        } else if constexpr (SEP == kSepFixup) {
+            if (__builtin_amdgcn_ballot_w64(sep)) {
+                float xh[8];  // the chosen code's dequantized values
+                if constexpr (FMT == kFmtMx) {
+                    decode_word(best_cw, __uint_as_float((uint32_t)best_byte << 23), xh);
+                } else {
+                    decode_word(best_cw, 1.0f, xh);
+                    const float d = ue.tab[best_byte].x;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xh[i] = xh[i] * d;
+                }
+                const double s2 = nonmax_sum<L>(v, xh, m, gl);
+                if (sep) acc.nonmax += s2;
+            }
+            return;
+        }
+        add_block(acc, zero, best, mterm, nm, ss);
     }
 }
 
@@ -910,7 +1125,7 @@ __global__ __launch_bounds__(kThreads)
 #if FP4Q_QUANT_WPE
 __attribute__((amdgpu_waves_per_eu(FP4Q_QUANT_WPE)))
 #endif
-void k_quantize(QParams p) {
+FP4Q_SGPR_CAP void k_quantize(QParams p) {
     constexpr int L = B / kLaneElems;
     const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
@@ -937,8 +1152,10 @@ void k_quantize(QParams p) {
         ue.tab = s_tab;
     }
     Acc acc;
+    constexpr int E = XT == 0 ? 2 : 4;
     for (int64_t i = 0, c = wr.c0; i < wr.n; ++i, c += wr.step) {
         const QOut o = group_outputs<B, kQuantUnroll>(p, c, wr.c1);
+        const Rsrc xin = group_input<XT, kQuantUnroll>(p.x, p.n, c, wr.c1);
         const int64_t left = wr.c1 - c;  // wave-uniform
 #if FP4Q_PREFETCH
         Raw<XT> nxt[kQuantUnroll];
@@ -948,9 +1165,10 @@ void k_quantize(QParams p) {
         for (int u = 0; u < kQuantUnroll; ++u)
             if (u < left) {
                 if constexpr (SEARCH)
-                    search_chunk<XT, FMT, B, ROT, SUMSQ>(cur[u], u, o, p, ue, lane, gl, acc);
+                    search_chunk<XT, FMT, B, ROT, SUMSQ, kSepDefer>(cur[u], u, o, p, ue, lane, gl, acc);
                 else
-                    quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ>(cur[u], u, o, p, ue, lane, gl, acc);
+                    quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer>(
+                        cur[u], u, o, p, ue, lane, gl, acc, xin, u * kChunk * E);
             }
 #if FP4Q_PREFETCH
 #pragma unroll
@@ -958,6 +1176,29 @@ void k_quantize(QParams p) {
 #else
         if (i + 1 < wr.n) load_group<XT, kQuantUnroll>(cur, p.x, p.n, c + wr.step, wr.c1, lane);
 #endif
+    }
+    if constexpr (ERR) {
+        // Fix-up pass: only waves that deferred a block's separate non-max sum
+        // (rare) read their range again.
+        if (p.so.stats && __builtin_amdgcn_readfirstlane(acc.fixup)) {
+            for (int64_t i = 0, c = wr.c0; i < wr.n; ++i, c += wr.step) {
+                Raw<XT> raw[kQuantUnroll];
+                load_group<XT, kQuantUnroll>(raw, p.x, p.n, c, wr.c1, lane);
+                const QOut o = group_outputs<B, kQuantUnroll>(p, c, wr.c1);
+                const Rsrc xin = group_input<XT, kQuantUnroll>(p.x, p.n, c, wr.c1);
+                const int64_t left = wr.c1 - c;
+#pragma unroll
+                for (int u = 0; u < kQuantUnroll; ++u)
+                    if (u < left) {
+                        if constexpr (SEARCH)
+                            search_chunk<XT, FMT, B, ROT, SUMSQ, kSepFixup>(raw[u], u, o, p, ue, lane,
+                                                                            gl, acc);
+                        else
+                            quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepFixup>(
+                                raw[u], u, o, p, ue, lane, gl, acc, xin, u * kChunk * E);
+                    }
+            }
+        }
     }
     if (p.so.stats) {
         if (gl != 0) acc = Acc{};  // every lane of a block holds its terms: keep one copy
@@ -1074,13 +1315,19 @@ struct RowParams {
 // The kUnroll-chunk group starting at chunk k of a row of `cols` elements;
 // elements past the row's end read as zeros.
 template <int XT>
-__device__ __forceinline__ void load_row_group(Raw<XT> (&raw)[kUnroll], const void* xrow,
-                                               int64_t cols, int64_t k, int lane) {
+__device__ __forceinline__ Rsrc row_group_input(const void* xrow, int64_t cols, int64_t k) {
     constexpr int E = XT == 0 ? 2 : 4;
     const int64_t first = k * kChunk;
     int64_t avail = (int64_t)kUnroll * kChunk;
     if (avail > cols - first) avail = cols - first;
-    const Rsrc r = make_rsrc(static_cast<const char*>(xrow) + first * E, avail * E);
+    return make_rsrc(static_cast<const char*>(xrow) + first * E, avail * E);
+}
+
+template <int XT>
+__device__ __forceinline__ void load_row_group(Raw<XT> (&raw)[kUnroll], const void* xrow,
+                                               int64_t cols, int64_t k, int lane) {
+    constexpr int E = XT == 0 ? 2 : 4;
+    const Rsrc r = row_group_input<XT>(xrow, cols, k);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         if constexpr (XT == 0) {
@@ -1175,10 +1422,12 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows(RowParams rp) {
             Raw<XT> nxt[kUnroll];
             if (k + kUnroll < nk) load_row_group<XT>(nxt, xrow, rp.cols, k + kUnroll, lane);
             const QOut o = row_outputs<B>(p, row, rp.cols, k);
+            const Rsrc xin = row_group_input<XT>(xrow, rp.cols, k);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
                 if (k + u < nk)
-                    quantize_chunk<XT, kFmtUe4m3, B, ROT, ERR, SUMSQ>(cur[u], u, o, p, ue, lane, gl, acc);
+                    quantize_chunk<XT, kFmtUe4m3, B, ROT, ERR, SUMSQ>(cur[u], u, o, p, ue, lane, gl, acc,
+                                                                      xin, u * kChunk * E);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
         }
@@ -1273,7 +1522,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize_rows_wg(RowParams rp) {
                 o.codes = make_rsrc(p.codes + first / 2, avail / 2);
                 o.scales = make_rsrc(p.scales + first / B, avail / B);
                 o.mse = make_rsrc(p.block_mse + first / B, p.block_mse ? avail / B * 4 : 0);
-                quantize_chunk<XT, kFmtUe4m3, B, ROT, ERR, SUMSQ>(cur[u], 0, o, p, ue, lane, gl, acc);
+                quantize_chunk<XT, kFmtUe4m3, B, ROT, ERR, SUMSQ>(
+                    cur[u], 0, o, p, ue, lane, gl, acc,
+                    make_rsrc(static_cast<const char*>(p.x) + row * rp.cols * E, rp.cols * E),
+                    k * kChunk * E);
             }
         }
 #pragma unroll
@@ -1392,18 +1644,91 @@ struct MParams {
     StatsOut so;
 };
 
-// Same work split, per-element arithmetic and accumulation order as
-// k_quantize, so the per-block MSE of codes that k_quantize wrote is
-// bit-identical to the value it reported.
-template <int XT, int FMT, int B, int ROT, bool SUMSQ>
-__global__ __launch_bounds__(kThreads) void k_block_mse(MParams p) {
+// Error terms of one chunk of stored codes (cw) and scale bytes (sb) against
+// its values (raw): the same per-element arithmetic and accumulation order as
+// quantize_chunk, so the per-block MSE of codes that k_quantize wrote is
+// bit-identical to the value it reported.  The max-element term follows the
+// lowest index attaining the block maximum, which matters for arbitrary codes.
+// SEP: kSepDefer or kSepFixup (see kSepInline).
+template <int XT, int FMT, int B, int ROT, bool SUMSQ, int SEP>
+__device__ __forceinline__ void mse_chunk(const Raw<XT>& raw, uint32_t cw, uint32_t sb, int u,
+                                          Rsrc rm, const MParams& p, float g, int lane, int gl,
+                                          Acc& acc) {
+    static_assert(SEP != kSepInline, "block MSE defers the separate sums");
     constexpr int L = B / kLaneElems;
     constexpr int kBlocks = kChunk / B;
-    const int lane = threadIdx.x % kWave;
-    const int gl = lane & (L - 1);
-    const float g = (FMT != kFmtMx && p.g) ? *p.g : 1.0f;
-    const WaveRange wr = wave_range(p.n_chunks, p.cpw);
-    Acc acc;
+    float v[8], xh[8];
+    unpack<XT>(raw, v);
+    if constexpr (ROT != 0) rotate8<ROT>(v, gl);
+    dequant_word<FMT>(cw, sb, p.fmt, g, xh);
+    float mf = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mf = fmaxf(mf, fabsf(v[i]));
+    const float m = __uint_as_float(group_max<L>(__float_as_uint(mf)));
+    double sse = 0.0, ss = 0.0;
+    uint32_t key = 0xFFu;  // lowest in-block index attaining m
+    float e_key = 0.0f;
+    uint32_t any_nz = 0;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+        const float e = v[i] - xh[i];
+        if (fabsf(v[i]) == m) {
+            key = (uint32_t)(gl * 8 + i);
+            e_key = e;
+        }
+        any_nz |= (xh[i] != 0.0f) ? 1u : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const double e = (double)(v[i] - xh[i]);
+        sse = fma(e, e, sse);
+        if constexpr (SUMSQ) {
+            const double xv = (double)v[i];
+            ss = fma(xv, xv, ss);
+        }
+    }
+    sse = group_sum<L>(sse);
+    if constexpr (SUMSQ) ss = group_sum<L>(ss);
+    any_nz = group_max<L>(any_nz);
+#pragma unroll
+    for (int s = 1; s < L; s <<= 1) {
+        const uint32_t ok = (uint32_t)__shfl_xor((int)key, s);
+        const float oe = __shfl_xor(e_key, s);
+        if (ok < key) {
+            key = ok;
+            e_key = oe;
+        }
+    }
+    if (SEP != kSepFixup && p.block_mse) {
+        float mse;
+        if (p.mse_kind == kMseRel) mse = rel_mse(sse, ss);
+        else mse = (float)(sse * (1.0 / B));
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mse), rm,
+                                              gl == 0 ? (u * kBlocks + lane / L) * 4 : kDropped, 0, 0);
+    }
+    if (p.so.stats) {
+        const double mterm = (double)e_key * (double)e_key;
+        const bool zero = (m > 0.0f) && !any_nz;
+        double nm = sse - mterm;
+        const bool sep = needs_separate_sum(zero, sse, nm);
+        if constexpr (SEP == kSepDefer) {
+            if (sep) nm = 0.0;
+            if (__builtin_amdgcn_ballot_w64(sep)) acc.fixup = 1u;
+        } else {
+            if (__builtin_amdgcn_ballot_w64(sep)) {
+                const double s2 = nonmax_sum<L>(v, xh, m, gl);
+                if (sep) acc.nonmax += s2;
+            }
+            return;
+        }
+        add_block(acc, zero, sse, mterm, nm, ss);
+    }
+}
+
+// mse_chunk over a wave's range, in mode SEP.
+template <int XT, int FMT, int B, int ROT, bool SUMSQ, int SEP>
+__device__ __forceinline__ void block_mse_range(const MParams& p, const WaveRange& wr, float g,
+                                                int lane, int gl, Acc& acc) {
     for (int64_t i = 0, c = wr.c0; i < wr.n; ++i, c += wr.step) {
         Raw<XT> raw[kUnroll];
         uint32_t cw[kUnroll], sb[kUnroll];
@@ -1415,61 +1740,26 @@ __global__ __launch_bounds__(kThreads) void k_block_mse(MParams p) {
         const Rsrc rm = make_rsrc(p.block_mse + first / B, p.block_mse ? avail / B * 4 : 0);
         const int64_t left = wr.c1 - c;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            if (u >= left) continue;
-            float v[8], xh[8];
-            unpack<XT>(raw[u], v);
-            if constexpr (ROT != 0) rotate8<ROT>(v, gl);
-            dequant_word<FMT>(cw[u], sb[u], p.fmt, g, xh);
-            float mf = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) mf = fmaxf(mf, fabsf(v[i]));
-            const float m = __uint_as_float(group_max<L>(__float_as_uint(mf)));
-            double sse = 0.0, ss = 0.0;
-            uint32_t key = 0xFFu;  // lowest in-block index attaining m
-            float e_key = 0.0f;
-            uint32_t any_nz = 0;
-#pragma unroll
-            for (int i = 7; i >= 0; --i) {
-                const float e = v[i] - xh[i];
-                if (fabsf(v[i]) == m) {
-                    key = (uint32_t)(gl * 8 + i);
-                    e_key = e;
-                }
-                any_nz |= (xh[i] != 0.0f) ? 1u : 0u;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const double e = (double)(v[i] - xh[i]);
-                sse = fma(e, e, sse);
-                if constexpr (SUMSQ) {
-                    const double xv = (double)v[i];
-                    ss = fma(xv, xv, ss);
-                }
-            }
-            sse = group_sum<L>(sse);
-            if constexpr (SUMSQ) ss = group_sum<L>(ss);
-            any_nz = group_max<L>(any_nz);
-#pragma unroll
-            for (int s = 1; s < L; s <<= 1) {
-                const uint32_t ok = (uint32_t)__shfl_xor((int)key, s);
-                const float oe = __shfl_xor(e_key, s);
-                if (ok < key) {
-                    key = ok;
-                    e_key = oe;
-                }
-            }
-            if (p.block_mse) {
-                float mse;
-                if (p.mse_kind == kMseRel) mse = ss > 0.0 ? (float)(sse / ss) : 0.0f;
-                else mse = (float)(sse * (1.0 / B));
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mse), rm,
-                                                      gl == 0 ? (u * kBlocks + lane / L) * 4 : kDropped,
-                                                      0, 0);
-            }
-            add_block(acc, (m > 0.0f) && !any_nz, sse, (double)e_key * (double)e_key, ss);
-        }
+        for (int u = 0; u < kUnroll; ++u)
+            if (u < left)
+                mse_chunk<XT, FMT, B, ROT, SUMSQ, SEP>(raw[u], cw[u], sb[u], u, rm, p, g, lane, gl, acc);
     }
+}
+
+// Block MSE (and tensor terms) of stored codes: the work split of k_quantize,
+// chunk by chunk through mse_chunk, with the separate non-max sums deferred
+// to a fix-up pass of the waves that need one.
+template <int XT, int FMT, int B, int ROT, bool SUMSQ>
+__global__ __launch_bounds__(kThreads) FP4Q_SGPR_CAP void k_block_mse(MParams p) {
+    constexpr int L = B / kLaneElems;
+    const int lane = threadIdx.x % kWave;
+    const int gl = lane & (L - 1);
+    const float g = (FMT != kFmtMx && p.g) ? *p.g : 1.0f;
+    const WaveRange wr = wave_range(p.n_chunks, p.cpw);
+    Acc acc;
+    block_mse_range<XT, FMT, B, ROT, SUMSQ, kSepDefer>(p, wr, g, lane, gl, acc);
+    if (p.so.stats && __builtin_amdgcn_readfirstlane(acc.fixup))
+        block_mse_range<XT, FMT, B, ROT, SUMSQ, kSepFixup>(p, wr, g, lane, gl, acc);
     if (p.so.stats) {
         if (gl != 0) acc = Acc{};
         write_partial(acc, p.so);

@@ -255,3 +255,52 @@ def test_workspace_reuse_across_grid_sizes():
         q = fq.mxfp4_quantize(x)
         ref = oracle.quantize(to_oracle_input(x), oracle.FMT_MXFP4, 32)
         assert_stats(fq.stats_dict(q.stats), ref["terms"], ref["counts"])
+
+
+def max_dominated_rows(fmt: int, n_rows: int, cols: int, seed: int) -> np.ndarray:
+    """Blocks whose error sits almost all on the block maximum: the maximum
+    (one element at a random position) is off the grid, every other element is
+    on the E2M1 grid except one tiny value (2^-40 of the scale) that rounds to
+    zero.  The non-max term is then 2^-80 of the max term per block: a
+    difference SSE - M would return 0."""
+    rng = np.random.default_rng(seed)
+    block = 32 if fmt == oracle.FMT_MXFP4 else 16
+    # MXFP4: max 7 at scale 2^0 codes to 6 (error 1); UE4M3 with g = 1: max 6.25
+    # gives s_hat = 1 (byte 0x38), codes to 6 (error 0.25).
+    top = 7.0 if fmt == oracle.FMT_MXFP4 else 6.25
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0], np.float32)
+    x = rng.choice(grid, (n_rows, cols)).astype(np.float32)
+    x *= np.where(rng.random((n_rows, cols)) < .5, -1, 1).astype(np.float32)
+    nb = cols // block
+    for r in range(n_rows):
+        for k in range(nb):
+            pos = rng.permutation(block)
+            b0 = k * block
+            x[r, b0 + pos[0]] = np.float32(top) * (1 if rng.random() < .5 else -1)
+            x[r, b0 + pos[1]] = np.float32(2.0 ** -40)
+    return x
+
+
+@pytest.mark.parametrize("fmt", [oracle.FMT_MXFP4, oracle.FMT_UE4M3])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_nonmax_term_when_the_maximum_carries_the_error(fmt, dtype):
+    """The tensor non-max term is 2^-80 of the max term and must still hold the
+    relative bar (fused quantize, the block-MSE kernel and the scale search)."""
+    xa = max_dominated_rows(fmt, 37, 1024, 113)
+    x = torch.from_numpy(xa).to(dtype).to(DEV)
+    xo = to_oracle_input(x)
+    block = 32 if fmt == oracle.FMT_MXFP4 else 16
+    if fmt == oracle.FMT_MXFP4:
+        q = fq.mxfp4_quantize(x)
+    else:
+        q = fq.nvfp4_quantize(x, 16, fq.FMT_UE4M3, fq.G_NONE)
+    ref = oracle.quantize(xo, fmt, block)
+    assert 0.0 < ref["terms"][0] < 2.0 ** -60 * ref["terms"][1]
+    compare_quant(q, ref, xin=xo)
+    bm, st = fq.fp4_block_mse(x, q.codes, q.scales, fmt, block, None, 0)
+    rbm, acc, cnt = oracle.block_mse(xo, ref["codes"], ref["scales"], fmt, block, 1.0, 0)
+    assert_block_mse(bm.cpu().numpy(), rbm)
+    assert_stats(fq.stats_dict(st), acc, cnt)
+    qs = fq.fp4_quantize_search(x, fmt, block, fq.G_NONE, None, 0, 1)
+    rs = oracle.quantize_search(xo, fmt, block, oracle.GMODE_NONE, None, 0, 1)
+    compare_quant(qs, rs, xin=xo)
