@@ -1,41 +1,50 @@
 """Benchmark of the FP4 quantization path on one MI355X.
 
-Default workload (one step = the whole path over one batch):
-  six bf16 Qwen2.5-7B MLP tensors, 18944 x 3584 and 3584 x 18944 with
-  N(0, sigma), sigma in {0.01, 0.02, 0.04} (seeded), each quantized to NVFP4:
-  the per-tensor amax pass, then block-16 UE4M3 scales under the dynamic FP32
-  per-tensor scale, E2M1 codes packed two per byte, dequantization, per-block
-  MSE and the three-term error split.  Inputs are resident in HBM before timing.
-  The step spreads its independent per-tensor calls over two HIP streams (one
-  workspace each; --streams 1 runs them back to back on one stream).
+Default workload (one step = the whole path over one batch): a random-init
+Qwen2.5-14B-shaped stack, 48 layers x {q 5120x5120, k and v 1024x5120, o
+5120x5120, gate and up 13824x5120, down 5120x13824}, bf16 N(0, 0.02) seeded
+per tensor (13.2e9 parameters, 26.4 GB resident in HBM before timing).  Every
+tensor is quantized twice per step: MXFP4 (block 32, E8M0) and NVFP4 (block 16,
+UE4M3 under the dynamic FP32 per-tensor scale, whose amax pass reads the tensor
+once more), each with packed codes, scale bytes, the relative per-block MSE and
+the three-term error split.  The step spreads its independent calls over two
+HIP streams (one workspace each; --streams 1 runs them back to back).
 
-Prints one JSON line.  `value` is GB/s of input quantized+packed+MSE'd over
-the whole step (all kernels of all tensors).  For the default workload
-`roofline` is the quantize kernel alone (the step's own k_quantize
-instantiation, launched once per tensor with the step's per-tensor scale
-given), timed with HIP events on the stream it runs on; algorithmic bytes per
-element = 2 (read) + 0.5 (codes) + 1/16 (scales) + 4/16 (per-block MSE).  For
-the other workloads it is the whole step's algorithmic bytes (every kernel,
-the amax pre-pass read included) over the step time.  `cpu_baseline` times the
-oracle (single thread) on a bounded sample of the same workload.
+Prints one JSON line:
+  value         GB/s of input quantized+packed+MSE'd over the whole step (every
+                kernel of every call; K steps between HIP events), with the
+                per-step median and minimum beside the mean.
+  roofline      the step's own quantize launches: one step's calls replayed back
+                to back on one stream, each kernel launch bracketed by HIP
+                events on that stream (fp4q_profile_events); achieved = their
+                algorithmic bytes (read 2 B/element, codes 0.5, scale bytes 1/b,
+                per-block MSE 4/b) over their summed durations, against 8 TB/s.
+                The per-tensor amax pass (read 2 B/element) is reported beside it
+                as s0_amax_pass.  `traffic` is the counter-measured HBM bytes per
+                launch from profiles/ when taken on the current kernel source.
+  copy_ceiling  a plain device copy of the largest tensor (read + write), the
+                bandwidth this access pattern reaches on the box.
+  cpu_baseline  the oracle on a bounded sample of the same workload, on all host
+                threads (row slices) and on one, with the CPU model.
 
 Workloads (--workload):
-  qwen7        the default above
+  qwen14model  the default above (--layers L runs only the first L layers)
+  qwen7        six bf16 Qwen2.5-7B MLP tensors, 18944x3584 and 3584x18944 with
+               N(0, sigma), sigma in {0.01, 0.02, 0.04}: NVFP4 under the dynamic
+               per-tensor scale, per-block MSE and the three-term split
   qwen05       fp32 4864 x 896 (Qwen2.5-0.5B up-projection), MXFP4 with per-block
                MSE: launch-bound, reported in GB/s only
   llama8       four bf16 14336 x 4096 tensors (Llama-3.1-8B MLP), narrow Normal
-               sigma in {0.002, 0.005, 0.01, 0.05}, UE4M3 without a per-tensor
-               scale at block sizes 256, 128, 64, 32, 16 and 8, MSE and split
+               sigma in {0.002, 0.005, 0.01, 0.05}, UE4M3 and UE5M3 scales without
+               a per-tensor scale at block sizes 256 ... 8, MSE and split, with the
+               three-term model's prediction beside the measured terms
   qwen14rot    bf16 13824 x 5120 Student-t(4) with 1 % outlier columns x20:
                MXFP4 and dynamic NVFP4, each without and with block rotation
   act5120      activation matrices of 1, 16, 128, 2048 and 8192 tokens x 5120:
                NVFP4 + rotation with per-token scales, NVFP4 with the per-tensor
                dynamic scale, MXFP4 + rotation; time per call for each
-  qwen7search  the six default tensors, MXFP4 and dynamic NVFP4 with the per-block
+  qwen7search  the six qwen7 tensors, MXFP4 and dynamic NVFP4 with the per-block
                scale search (radius 1)
-  qwen14model  a random-init Qwen2.5-14B-shaped stack (48 layers x 7 projections,
-               13.2e9 bf16 parameters, 26.4 GB) quantized whole to MXFP4 and to
-               dynamic NVFP4, relative per-block MSE and per-tensor split
   gemm         a W4A4 Qwen2.5-7B MLP forward over 8192 tokens on MXFP4 operands:
                quantize the activations X (8192 x 3584) and H (8192 x 18944) to
                MXFP4, then the gate and up products (8192 x 18944 x 3584) and the
@@ -60,6 +69,8 @@ HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "microscaling_fp4_quantization_amd", "csrc")
 # Per workload: the roofline kernel's source file and its committed traffic record.
 TRAFFIC = {
+    "qwen14model": (os.path.join(CSRC, "fp4q_kernels.hip"),
+                    os.path.join(ROOT, "profiles", "quantize_qwen14_model_traffic.json")),
     "qwen7": (os.path.join(CSRC, "fp4q_kernels.hip"),
               os.path.join(ROOT, "profiles", "quantize_nvfp4_qwen7_traffic.json")),
     "gemm": (os.path.join(CSRC, "fp4q_gemm.hip"),
@@ -87,6 +98,18 @@ def read_traffic(workload="qwen7"):
 # of one call (name fragment, grid size in work items or None for any), the
 # bytes of the calibration copy, and the call's algorithmic bytes.
 def _traffic_plan(workload):
+    if workload == "qwen14model":
+        import fp4_workloads as wl
+        ns = [r * c for _, (r, c) in wl.QWEN14_PROJ]
+        # mean algorithmic bytes of one layer's 14 quantize launches (MXFP4 b32
+        # and NVFP4 b16 of each projection, relative per-block MSE)
+        alg = sum(n * (2 + 0.5 + 1 / 32 + 4 / 32) + n * (2 + 0.5 + 1 / 16 + 4 / 16) for n in ns) / (2 * len(ns))
+        return {"parts": [("k_quantize<0, ", None)],
+                "label": "k_quantize, the step's launches (MXFP4 b32 and dynamic NVFP4 b16 with relative "
+                         "per-block MSE and the three-term split): mean per launch over one layer's 14",
+                "calib_bytes": 5120 * 5120 * 2, "alg_bytes": int(alg),
+                "run": "python -u bench.py --layers 1 --steps 1 --warmup 0 --no-cpu-baseline "
+                       "--calibration-copy"}
     if workload == "qwen7":
         n = 18944 * 3584
         return {"parts": [("k_quantize<0, 1, 16, 0, true, false, false>", None)],
@@ -194,6 +217,19 @@ class Spec:
             b += n * in_bytes
         return b
 
+    def launches(self):
+        """The kernels one call launches, in order."""
+        seq = ["amax"] if (self.fmt == "nv" and self.gmode == 1) else []
+        seq.append("quantize")
+        if self.stats:
+            seq.append("finalize")
+        return seq
+
+    def quantize_bytes(self, n, in_bytes):
+        """Algorithmic bytes of the quantize kernel alone: its read, the codes,
+        scale bytes and per-block MSE."""
+        return n * (in_bytes + 0.5 + 1.0 / self.block + (4.0 / self.block if self.block_mse else 0))
+
     def describe(self):
         if self.fmt == "mx":
             s = "MXFP4 b32"
@@ -208,7 +244,7 @@ class Spec:
 
 
 class Workload:
-    """`sample` = (description, tensors, repeats, spec index) of the oracle's
+    """`sample` = (description, number of tensors, spec indices) of the oracle's
     bounded CPU sample.  `per_call` asks for a time per (tensor, spec) pair in
     the breakdown (latency-bound workloads)."""
 
@@ -244,11 +280,15 @@ def _act5120_tensors():
     return [wl.activations_5120(m) for m in wl.ACT_TOKENS]
 
 
+QWEN14_LAYERS_RUN = None  # --layers: leading layers of the stack to run (counter runs)
+
+
 def _qwen14model_tensors():
     """Generated on host threads (one PCG64 stream per tensor, as the recipe says)
     and moved to the device one by one; yields host tensors lazily."""
     import fp4_workloads as wl
-    keys = [(layer, p) for layer in range(wl.QWEN14_LAYERS) for p in range(len(wl.QWEN14_PROJ))]
+    layers = QWEN14_LAYERS_RUN or wl.QWEN14_LAYERS
+    keys = [(layer, p) for layer in range(layers) for p in range(len(wl.QWEN14_PROJ))]
     workers = max(1, min(16, os.cpu_count() or 1))
     with ThreadPoolExecutor(workers) as ex:
         for t in ex.map(lambda k: wl.qwen14_layer_tensor(*k), keys):
@@ -263,20 +303,22 @@ WORKLOADS = {
          "outputs": "codes + scales + per-block MSE + three-term error split"},
         _qwen7_tensors, [Spec("nv16_dyn", "nv", 16, 1, 1)], 50, 5,
         ("4 of the 6 tensors (the three 18944x3584 ones and 3584x18944 with sigma 0.01), whole",
-         4, 1, 0)),
+         4, [0])),
     "qwen05": Workload(
         "qwen2.5-0.5b-up-mxfp4-fp32",
         {"tensors": "1 fp32 4864x896, N(0, 0.02), seed 0",
          "format": "MXFP4: block 32, E8M0 scales", "outputs": "codes + scales + per-block MSE"},
         _qwen05_tensors, [Spec("mx32", "mx", 32, stats=False)], 400, 20,
-        ("the tensor, whole, 40 times", 1, 40, 0)),
+        ("the tensor, whole", 1, [0])),
     "llama8": Workload(
         "llama3.1-8b-mlp-ue4m3-block-sweep",
         {"tensors": "4 bf16 14336x4096, sigma 0.002/0.005/0.01/0.05",
-         "format": "UE4M3 scales, no per-tensor scale, blocks 256/128/64/32/16/8",
+         "format": "UE4M3 and UE5M3 scales, no per-tensor scale, blocks 256/128/64/32/16/8",
          "outputs": "codes + scales + per-block MSE + three-term error split"},
-        _llama8_tensors, [Spec(f"ue4m3_b{b}", "nv", b, 1, 0) for b in (256, 128, 64, 32, 16, 8)],
-        20, 2, ("2 of the 4 tensors (sigma 0.002 and 0.005), whole", 2, 1, 4)),
+        _llama8_tensors,
+        [Spec(f"ue4m3_b{b}", "nv", b, 1, 0) for b in (256, 128, 64, 32, 16, 8)] +
+        [Spec(f"ue5m3_b{b}", "nv", b, 2, 0) for b in (256, 128, 64, 32, 16, 8)],
+        20, 2, ("2 of the 4 tensors (sigma 0.002 and 0.005), whole, at block 16", 2, [4, 10])),
     "qwen14rot": Workload(
         "qwen2.5-14b-mlp-outliers-rotation",
         {"tensors": "1 bf16 13824x5120, Student-t(4) sd 0.02, 51 outlier columns x20",
@@ -285,7 +327,7 @@ WORKLOADS = {
         _qwen14rot_tensors,
         [Spec("mx32", "mx", 32), Spec("mx32_rot", "mx", 32, rotate=32),
          Spec("nv16_dyn", "nv", 16, 1, 1), Spec("nv16_dyn_rot", "nv", 16, 1, 1, rotate=16)],
-        50, 5, ("the tensor, whole, 3 times", 1, 3, 2)),
+        50, 5, ("the tensor, whole", 1, [0, 3])),
     "qwen7search": Workload(
         "qwen2.5-7b-mlp-scale-search",
         {"tensors": "6 bf16: 18944x3584 and 3584x18944, sigma 0.01/0.02/0.04",
@@ -294,7 +336,7 @@ WORKLOADS = {
          "outputs": "codes + scales + per-block MSE + three-term error split"},
         _qwen7_tensors,
         [Spec("mx32_search1", "mx", 32, radius=1), Spec("nv16_dyn_search1", "nv", 16, 1, 1, radius=1)],
-        20, 2, ("1 of the 6 tensors (18944x3584, sigma 0.01), whole", 1, 1, 1)),
+        20, 2, ("1 of the 6 tensors (18944x3584, sigma 0.01), whole", 1, [0])),
     "act5120": Workload(
         "activations-5120-token-shapes",
         {"tensors": "5 bf16 activation matrices M x 5120, M = 1, 16, 128, 2048, 8192",
@@ -305,7 +347,7 @@ WORKLOADS = {
         [Spec("nv16_rot_rowg", "nv", 16, 1, 3, rotate=16, block_mse=False, stats=False),
          Spec("nv16_tensor_g", "nv", 16, 1, 1, block_mse=False, stats=False),
          Spec("mx32_rot", "mx", 32, rotate=32, block_mse=False, stats=False)],
-        50, 5, ("all five matrices, whole, 8 times", 5, 8, 0),
+        50, 5, ("all five matrices, whole", 5, [0, 1, 2]),
         per_call=True),
     "qwen14model": Workload(
         "qwen2.5-14b-shaped-model-sweep",
@@ -314,7 +356,7 @@ WORKLOADS = {
          "outputs": "codes + scales + relative per-block MSE + per-tensor split"},
         _qwen14model_tensors,
         [Spec("mx32", "mx", 32, mse_kind=1), Spec("nv16_dyn", "nv", 16, 1, 1, mse_kind=1)],
-        5, 1, ("layer 0's q, k, v, o, gate and up projections, whole", 6, 1, 1)),
+        5, 1, ("layer 0's seven projections (q, k, v, o, gate, up, down), whole", 7, [0, 1])),
 }
 
 
@@ -533,10 +575,11 @@ class Runner:
                               scales=o["scales"], block_mse=bm, mse_kind=s.mse_kind, stats=st,
                               ws=ws)
 
-    def step(self, given=False):
-        """All calls of one step; with given=True each runs alone on the caller's
-        stream (the roofline leg)."""
-        if given or len(self.streams) == 1:
+    def step(self, given=False, one_stream=False):
+        """All calls of one step; with one_stream (or given, which also passes the
+        dynamic per-tensor scale as given) they run back to back on the caller's
+        stream."""
+        if given or one_stream or len(self.streams) == 1:
             for ti in range(len(self.xs)):
                 for si in range(len(self.specs)):
                     self.call(ti, si, given)
@@ -612,32 +655,154 @@ def time_region(torch, stream, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_call(oracle, xf, s, threads, pool):
+    """One call of spec s on float32 array xf through the oracle, on row slices
+    over `threads` threads (the per-tensor dynamic scale from the slices' amax)."""
+    fmt = oracle.FMT_MXFP4 if s.fmt == "mx" else s.scale_fmt
+    rows = xf.shape[0]
+    n = max(1, min(rows, 2 * threads))
+    cuts = [rows * i // n for i in range(n + 1)]
+    slices = [xf[cuts[i]:cuts[i + 1]] for i in range(n)]
+    run = (lambda f, it: list(pool.map(f, it))) if pool else (lambda f, it: [f(v) for v in it])
+    g, gmode = None, oracle.GMODE_NONE
+    if s.fmt == "nv" and s.gmode == 1:
+        g = oracle.dynamic_g(max(run(lambda a: oracle.tensor_amax(a, s.rotate), slices)))
+        gmode = oracle.GMODE_GIVEN
+    elif s.fmt == "nv" and s.gmode == 3:
+        gmode = oracle.GMODE_ROW
+    if s.radius is not None:
+        run(lambda a: oracle.quantize_search(a, fmt, s.block, gmode, g, s.rotate, s.radius,
+                                             s.mse_kind), slices)
+    else:
+        run(lambda a: oracle.quantize(a, fmt, s.block, gmode, g, s.rotate, s.mse_kind), slices)
+
+
 def cpu_baseline(w, xs_host_sample):
-    """The oracle as it stands (one thread) on a bounded sample of the workload."""
+    """The oracle as it stands, on a bounded sample of the workload: every spec
+    of the step (or the sample's subset) on the sample tensors, on all host
+    threads (row slices), and on one thread for the first sample tensor."""
     import numpy as np
     import oracle
-    desc, n_tensors, repeat, spec_idx = w.sample
-    s = w.specs[spec_idx]
-    fmt = oracle.FMT_MXFP4 if s.fmt == "mx" else s.scale_fmt
-    gmode = {0: oracle.GMODE_NONE, 1: oracle.GMODE_DYNAMIC, 2: oracle.GMODE_GIVEN,
-             3: oracle.GMODE_ROW}[s.gmode]
-    n, el, in_bytes = 0, 0.0, 2
+    desc, n_tensors, spec_idx = w.sample
+    specs = [w.specs[i] for i in spec_idx]
+    threads = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                         else (os.cpu_count() or 1)))
+    host = []
     for x in xs_host_sample[:n_tensors]:
-        xf = x.float().numpy() if hasattr(x, "float") else np.asarray(x, np.float32)
         in_bytes = 4 if (hasattr(x, "dtype") and str(x.dtype) == "torch.float32") else 2
-        for _ in range(repeat):
-            t = time.perf_counter()
-            if s.radius is not None:
-                oracle.quantize_search(xf, fmt, s.block, gmode, None, s.rotate, s.radius,
-                                       s.mse_kind)
-            else:
-                oracle.quantize(xf, fmt, s.block, gmode, None, s.rotate, s.mse_kind)
-            el += time.perf_counter() - t
-            n += xf.size
-    return {"value": round(n * in_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{desc}, {s.describe()}, single-threaded C oracle",
-            "seconds": round(el, 2)}
+        host.append((x.float().numpy() if hasattr(x, "float") else np.asarray(x, np.float32), in_bytes))
+
+    def timed(tensors, pool, nthreads):
+        t = time.perf_counter()
+        nbytes = 0
+        for xf, in_bytes in tensors:
+            for s in specs:
+                _oracle_call(oracle, xf, s, nthreads, pool)
+                nbytes += xf.size * in_bytes
+        return nbytes, time.perf_counter() - t
+
+    with ThreadPoolExecutor(threads) as pool:
+        nb, el = timed(host, pool, threads)
+    nb1, el1 = timed(host[:1], None, 1)
+    what = ", ".join(s.describe() for s in specs)
+    return {"value": round(nb / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{desc}; {what}; C oracle on {threads} host threads (row slices)",
+            "seconds": round(el, 2), "cpu_model": _cpu_model(),
+            "single_thread": {"value": round(nb1 / el1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"the first of those tensors; {what}",
+                              "seconds": round(el1, 2)}}
+
+
+def three_term_table(fq, run, sigmas):
+    """Per-element non-max, max-element and zero-rounding terms the GPU measured
+    (each call's tensor stats) beside the three-term model's prediction for
+    N(0, sigma) (stored by tests/golden/make_mse_model.py), and the small-block
+    inversion (total MSE at block 8 above that at block 16)."""
+    try:
+        model = json.load(open(os.path.join(ROOT, "tests", "golden", "mse_model_llama8.json")))["terms"]
+    except (OSError, ValueError):
+        model = {}
+    fmt_name = {1: "ue4m3", 2: "ue5m3"}
+    table, totals = {}, {}
+    for ti, x in enumerate(run.xs):
+        sigma = sigmas[ti]
+        n = x.numel()
+        for si, s in enumerate(run.specs):
+            st = fq.stats_dict(run.out[(ti, si)]["stats"])
+            meas = [st["sse_nonmax"] / n, st["sse_max"] / n, st["sse_zero"] / n]
+            name = fmt_name[s.scale_fmt]
+            key = f"{name}/{sigma}/{s.block}"
+            m = model.get(key)
+            entry = {"measured_N_M_Z": [float(f"{v:.5g}") for v in meas],
+                     "measured_total": float(f"{sum(meas):.5g}")}
+            if m:
+                entry["model_N_M_Z"] = [float(f"{m[k]:.5g}") for k in ("nonmax", "max", "zero")]
+                entry["model_total"] = float(f"{m['total']:.5g}")
+                entry["measured_over_model"] = round(sum(meas) / m["total"], 4)
+            table.setdefault(name, {}).setdefault(str(sigma), {})[str(s.block)] = entry
+            totals[(name, sigma, s.block)] = sum(meas)
+    inversion = {}
+    for name in ("ue4m3", "ue5m3"):
+        for sigma in sigmas:
+            if (name, sigma, 8) in totals and (name, sigma, 16) in totals:
+                inversion[f"{name}/{sigma}"] = totals[(name, sigma, 8)] > totals[(name, sigma, 16)]
+    return {"per_element_terms": table, "mse_b8_above_b16": inversion}
+
+
+def launch_times(fq, torch, run):
+    """Every call of one step replayed back to back on one stream, each kernel
+    launch timed with HIP events on that stream (fp4q_profile_events).  Returns
+    {kind: [(us, algorithmic bytes)]} for kinds amax, quantize and finalize."""
+    seq = []
+    for ti, x in enumerate(run.xs):
+        for si, s in enumerate(run.specs):
+            in_bytes = x.element_size()
+            for kind in s.launches():
+                nb = {"amax": x.numel() * in_bytes, "quantize": s.quantize_bytes(x.numel(), in_bytes),
+                      "finalize": 0}[kind]
+                seq.append((ti, si, kind, nb))
+    run.step(given=False, one_stream=True)  # warm
+    torch.cuda.synchronize()
+    with fq.LaunchTimer(len(seq)) as t:
+        run.step(given=False, one_stream=True)
+    us = t.durations_us()
+    if len(us) != len(seq):
+        raise RuntimeError(f"recorded {len(us)} launches, expected {len(seq)}")
+    out = {}
+    for (ti, si, kind, nb), u in zip(seq, us):
+        out.setdefault(kind, []).append((u, nb, si))
+    return out
+
+
+def copy_ceiling(torch, xs):
+    """A plain device copy of the largest tensor (cycling over up to three of
+    that size, so the 256 MB last-level cache does not hold them): read + write
+    bytes over time, the bandwidth this access pattern reaches."""
+    big = max(x.numel() for x in xs)
+    shape = next(x.shape for x in xs if x.numel() == big)
+    src = [x.view(-1) for x in xs if x.numel() == big][:3]
+    dst = torch.empty_like(src[0])
+    stream = torch.cuda.current_stream()
+    for i in range(3):
+        dst.copy_(src[i % len(src)])
+    reps = 30
+    ms = time_region(torch, stream, lambda: [dst.copy_(src[i % len(src)]) for i in range(len(src))], reps)
+    per = ms / len(src)
+    gbs = 2 * src[0].numel() * src[0].element_size() / (per * 1e-3) / 1e9
+    return {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "us_per_copy": round(per * 1e3, 2),
+            "what": f"device copy of a {'x'.join(map(str, shape))} {str(src[0].dtype)[6:]} tensor "
+                    f"(read + write), {len(src)} distinct tensors cycled"}
 
 
 def main():
@@ -646,7 +811,9 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="qwen7", choices=sorted(WORKLOADS) + ["gemm"])
+    ap.add_argument("--workload", default="qwen14model", choices=sorted(WORKLOADS) + ["gemm"])
+    ap.add_argument("--layers", type=int, default=None,
+                    help="qwen14model: run only the first LAYERS layers (short counter runs)")
     ap.add_argument("--streams", type=int, default=2,
                     help="HIP streams the step's independent calls are spread over")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -668,6 +835,8 @@ def main():
         gemm_main(args, args.steps if args.steps is not None else 20,
                   args.warmup if args.warmup is not None else 3)
         return
+    global QWEN14_LAYERS_RUN
+    QWEN14_LAYERS_RUN = args.layers
     w = WORKLOADS[args.workload]
     steps = args.steps if args.steps is not None else w.steps
     warmup = args.warmup if args.warmup is not None else w.warmup
@@ -691,36 +860,51 @@ def main():
     for _ in range(warmup):
         run.step()
     stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    ms_step = time_region(torch, stream, run.step, steps)
+    ev[0].record(stream)
+    for i in range(steps):
+        run.step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    ms_step = ev[0].elapsed_time(ev[steps]) / steps
     value = n_elem_calls * in_bytes / (ms_step * 1e-3) / 1e9
 
-    if args.workload == "qwen7":
-        # Dominant kernel alone.  With the per-tensor scale given (the g each step
-        # computed), per-block MSE and no stats, a call launches exactly one
-        # kernel: the same k_quantize instantiation the step runs (in the dynamic
-        # mode the amax pass supplies sum x^2, so the step's quantize kernel omits
-        # it too).  The step's launches also form the tensor terms and reduce the
-        # amax partials, so they run on the one-round grid; these run on
-        # short-lived workgroups, and skip the tensor-term arithmetic.
-        reps = max(10, steps)
-        run.step(given=True)
-        us_launch = time_region(torch, stream, lambda: run.step(given=True), reps) * 1e3 / len(xs)
-        bytes_launch = xs[0].numel() * (2 + 0.5 + 1 / 16 + 4 / 16)
-        achieved = bytes_launch / (us_launch * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": read_traffic(),
-                    "kernel": "k_quantize<bf16, UE, 16, no rotation, err, no sumsq>",
-                    "us_per_launch": round(us_launch, 3),
-                    "algorithmic_bytes_per_launch": int(bytes_launch)}
-    else:
-        achieved = alg_bytes / (ms_step * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "whole step (every kernel of every call)",
-                    "algorithmic_bytes_per_step": int(alg_bytes)}
+    # Dominant kernel: the step's own quantize launches (every call of a step,
+    # replayed on one stream, each launch timed with events on that stream).
+    lt = launch_times(fq, torch, run)
+    q = lt["quantize"]
+    q_us, q_bytes = sum(u for u, _, _ in q), sum(nb for _, nb, _ in q)
+    achieved = q_bytes / (q_us * 1e-6) / 1e9
+    per_spec = {}
+    for si, s in enumerate(w.specs):
+        sel = [(u, nb) for u, nb, sj in q if sj == si]
+        su, sb = sum(u for u, _ in sel), sum(nb for _, nb in sel)
+        per_spec[s.tag] = {"launches": len(sel), "us_per_launch": round(su / len(sel), 3),
+                           "GBps": round(sb / (su * 1e-6) / 1e9, 1),
+                           "frac": round(sb / (su * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic(args.workload) if args.workload in TRAFFIC else None,
+                "kernel": "k_quantize: every quantize launch of one step (the step's calls replayed "
+                          "on one stream, HIP events around each launch)",
+                "us_per_launch": round(q_us / len(q), 3),
+                "algorithmic_bytes_per_launch": int(q_bytes / len(q)),
+                "launches": len(q), "per_spec": per_spec}
+    if "amax" in lt:
+        a = lt["amax"]
+        a_us, a_bytes = sum(u for u, _, _ in a), sum(nb for _, nb, _ in a)
+        roofline["s0_amax_pass"] = {
+            "kernel": "k_amax (per-tensor amax for the dynamic scale: reads the input once)",
+            "launches": len(a), "us_per_launch": round(a_us / len(a), 3),
+            "GBps": round(a_bytes / (a_us * 1e-6) / 1e9, 1),
+            "frac": round(a_bytes / (a_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    if "finalize" in lt:
+        f = lt["finalize"]
+        roofline["stats_reduction_us_per_launch"] = round(sum(u for u, _, _ in f) / len(f), 3)
 
     # Per-spec breakdown: one timed pass of each call type over all tensors.
     breakdown = {}
@@ -748,13 +932,17 @@ def main():
                                                     / (ms * 1e-3) / 1e9, 1),
                                 "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
 
+    ceiling = copy_ceiling(torch, xs) if not w.per_call else None
     if args.calibration_copy:
         dst = torch.empty_like(xs[0])
         dst.copy_(xs[0])
         torch.cuda.synchronize()
 
     config = {"workload": w.name, **w.config, "elements_per_step": n_elem_calls,
-              "streams": max(1, args.streams)}
+              "streams": max(1, args.streams),
+              "arithmetic": "binary32 scales and codes, binary64 error sums"}
+    if args.workload == "qwen14model":
+        config["layers"] = QWEN14_LAYERS_RUN or 48
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -763,18 +951,26 @@ def main():
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
+        "ms_per_step_min": round(per_step[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if in_bytes == 4 else "bf16",
         "data": "synthetic (seeded numpy PCG64, " +
                 ("fp32" if in_bytes == 4 else "rounded to bf16") + ")",
         "config": config,
         "roofline": roofline,
         "step_breakdown": {"algorithmic_GBps_all_kernels":
                            round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
+                           "frac_all_kernels": round(alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "wall_s_timed_region": round(t_wall, 3), **breakdown},
     }
+    if ceiling:
+        line["copy_ceiling"] = ceiling
+    if args.workload == "llama8":
+        import fp4_workloads as wl
+        line["three_term_model"] = three_term_table(fq, run, wl.LLAMA8_SIGMAS)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, sample_host)
     print(json.dumps(line), flush=True)

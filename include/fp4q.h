@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 1
+#define FP4Q_ABI_VERSION 2
 
 typedef enum {
     FP4Q_OK = 0,
@@ -325,6 +325,23 @@ const char* fp4q_last_error(void);
 
 /* FP4Q_ABI_VERSION of the loaded library. */
 int32_t fp4q_abi_version(void);
+
+/* Launch timing, for benchmarks and profiling (no counterpart on the pages).
+ * events: 2 * n_pairs HIP events (hipEvent_t passed as void*), created and
+ * owned by the caller (with timing enabled to read durations).  From this call
+ * on, every kernel the library launches from the calling thread records
+ * events[2i] on its stream just before itself and events[2i + 1] just after,
+ * for i = 0, 1, ... in launch order, until n_pairs launches have been
+ * recorded.  A quantize call launches, in order: the amax pass (dynamic
+ * per-tensor scale only), the quantize kernel, and the reduction of the tensor
+ * terms (stats only).  n_pairs = 0 or events = NULL stops recording.  The
+ * array and the events must stay valid while recording is on; nothing is
+ * allocated.  Errors: FP4Q_ERR_ARG for n_pairs < 0. */
+fp4q_status fp4q_profile_events(void* const* events, int32_t n_pairs);
+
+/* Kernel launches recorded on the calling thread since the last
+ * fp4q_profile_events call. */
+int32_t fp4q_profile_count(void);
 
 #ifdef __cplusplus
 }

@@ -33,11 +33,12 @@ G_NONE, G_DYNAMIC, G_GIVEN, G_ROW = 0, 1, 2, 3
 MSE_ABS, MSE_REL = 0, 1
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
 
-EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "fp4_quantize_search", "fp4_dequantize",
+EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "fp4_quantize_search",
+           "fp4_dequantize",
            "fp4_block_mse", "hadamard_block_rotate", "fp4_gemm_mxfp4", "fp4_gemm_workspace_bytes",
            "fp4_gemm_nvfp4", "fp4_gemm_nvfp4_workspace_bytes",
            "fp4q_workspace_bytes",
-           "fp4q_last_error", "fp4q_abi_version")
+           "fp4q_last_error", "fp4q_abi_version", "fp4q_profile_events", "fp4q_profile_count")
 
 
 class Fp4qError(RuntimeError):
@@ -85,6 +86,10 @@ def _bind(l):
     l.fp4q_last_error.restype = c.c_char_p
     l.fp4q_abi_version.argtypes = []
     l.fp4q_abi_version.restype = c.c_int32
+    l.fp4q_profile_events.argtypes = [P, i32]
+    l.fp4q_profile_events.restype = c.c_int
+    l.fp4q_profile_count.argtypes = []
+    l.fp4q_profile_count.restype = c.c_int32
     return l
 
 
@@ -127,8 +132,11 @@ def workspace_bytes(rows: int = 0, cols: int = 0, block: int = 32) -> int:
 
 
 def workspace(device) -> torch.Tensor:
-    """A zero-filled workspace for `device`, shared by calls made on one stream."""
-    key = torch.device(device).index
+    """A zero-filled workspace for `device` and torch's current stream on it.
+    Calls made on one stream share it (stream order keeps them apart); calls
+    made on another stream get a workspace of their own."""
+    dev = torch.device(device)
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None:
         ws = torch.zeros(workspace_bytes(), dtype=torch.uint8, device=device)
@@ -242,10 +250,10 @@ _gemm_workspaces = {}
 
 def gemm_workspace(device, nbytes: int) -> torch.Tensor:
     """A device workspace of at least `nbytes` for the GEMMs, kept per device
-    and grown on demand.  Calls that use it must be ordered (one stream): two
-    products running at once on different streams need workspaces of their own
-    (pass ``ws=``)."""
-    key = torch.device(device).index
+    and current stream and grown on demand (calls on one stream are ordered, so
+    they can share it)."""
+    dev = torch.device(device)
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
     ws = _gemm_workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
@@ -343,3 +351,37 @@ def hadamard_block_rotate(x: torch.Tensor, n: int, out: Optional[torch.Tensor] =
     _check(lib().hadamard_block_rotate(_ptr(x), _dtype_code(x), x.shape[0], x.shape[1], n,
                                        _ptr(out), _stream(x.device)))
     return out
+
+
+class LaunchTimer:
+    """Times the library's kernel launches with HIP events (fp4q_profile_events).
+
+    Inside ``with LaunchTimer(n) as t:``, each kernel the library launches from
+    this thread (up to ``n``) is bracketed by a pair of events on its stream;
+    afterwards ``t.durations_us()`` (which synchronises) gives their durations
+    in launch order.  A quantize call launches the amax pass (dynamic scale
+    only), the quantize kernel and the stats reduction (stats only)."""
+
+    def __init__(self, n: int, device=None):
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        stream = torch.cuda.current_stream(dev)
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for e in self.events:  # torch creates the HIP event at its first record
+            e.record(stream)
+        self._handles = (ctypes.c_void_p * (2 * n))(*[e.cuda_event for e in self.events])
+        self.n = n
+        self.count = 0
+
+    def __enter__(self):
+        _check(lib().fp4q_profile_events(self._handles, self.n))
+        return self
+
+    def __exit__(self, *exc):
+        self.count = int(lib().fp4q_profile_count())
+        lib().fp4q_profile_events(None, 0)
+        return False
+
+    def durations_us(self):
+        torch.cuda.synchronize()
+        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) * 1e3
+                for i in range(self.count)]

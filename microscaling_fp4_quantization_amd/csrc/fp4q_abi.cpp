@@ -316,4 +316,12 @@ const char* fp4q_last_error(void) { return g_err; }
 
 int32_t fp4q_abi_version(void) { return FP4Q_ABI_VERSION; }
 
+fp4q_status fp4q_profile_events(void* const* events, int32_t n_pairs) {
+    if (n_pairs < 0) return fail(FP4Q_ERR_ARG, "fp4q_profile_events: n_pairs %d is negative", n_pairs);
+    fp4q::profile_set(events, events ? n_pairs : 0);
+    return ok();
+}
+
+int32_t fp4q_profile_count(void) { return fp4q::profile_count(); }
+
 }  // extern "C"

@@ -1202,14 +1202,14 @@ template <int AR>
 void launch_decode_nv_ar(const NvDecParams& p, hipStream_t stream) {
     constexpr int W = dec_waves(AR);
     const int64_t groups = (p.units + W - 1) / W;
-    hipLaunchKernelGGL((k_gemm_decode_nv<AR, W>), dim3((unsigned)groups), dim3(W * kWave), 0, stream, p);
+    FP4Q_LAUNCH((k_gemm_decode_nv<AR, W>), dim3((unsigned)groups), dim3(W * kWave), 0, stream, p);
 }
 
 template <int AR>
 void launch_decode_ar(const DecParams& p, hipStream_t stream) {
     constexpr int W = dec_waves(AR);
     const int64_t groups = (p.units + W - 1) / W;
-    hipLaunchKernelGGL((k_gemm_decode<AR, W>), dim3((unsigned)groups), dim3(W * kWave), 0, stream, p);
+    FP4Q_LAUNCH((k_gemm_decode<AR, W>), dim3((unsigned)groups), dim3(W * kWave), 0, stream, p);
 }
 
 }  // namespace
@@ -1242,7 +1242,7 @@ int launch_gemm_nvfp4(const GemmNvJob& j, char* msg, size_t msg_len) {
         if (sp > 1) {
             const int64_t count = j.M * j.N;
             const int64_t rg = std::min<int64_t>((count + 1023) / 1024, 8192);
-            hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)rg), dim3(256), 0, stream, partial, sp, count,
+            FP4Q_LAUNCH(k_splitk_reduce, dim3((unsigned)rg), dim3(256), 0, stream, partial, sp, count,
                                j.c, j.ct);
         }
         const hipError_t e = hipGetLastError();
@@ -1260,11 +1260,11 @@ int launch_gemm_nvfp4(const GemmNvJob& j, char* msg, size_t msg_len) {
     float* partial = reinterpret_cast<float*>(j.ws);
     const NvParams p{j.a_codes, j.a_scales, j.b_codes, j.b_scales, j.ga, j.gb, j.M, j.N, j.K,
                      j.c, j.ct, sp, partial};
-    hipLaunchKernelGGL(k_gemm_nvfp4, dim3((unsigned)(tiles * sp)), dim3(kThreads), 0, stream, p);
+    FP4Q_LAUNCH(k_gemm_nvfp4, dim3((unsigned)(tiles * sp)), dim3(kThreads), 0, stream, p);
     if (sp > 1) {
         const int64_t count = j.M * j.N;
         const int64_t groups = std::min<int64_t>((count + 1023) / 1024, 8192);
-        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)groups), dim3(256), 0, stream, partial, sp, count,
+        FP4Q_LAUNCH(k_splitk_reduce, dim3((unsigned)groups), dim3(256), 0, stream, partial, sp, count,
                            j.c, j.ct);
     }
     const hipError_t e = hipGetLastError();
@@ -1304,7 +1304,7 @@ int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
         if (sp > 1) {
             const int64_t count = j.M * j.N;
             const int64_t rg = std::min<int64_t>((count + 1023) / 1024, 8192);
-            hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)rg), dim3(256), 0, stream, partial_area, sp,
+            FP4Q_LAUNCH(k_splitk_reduce, dim3((unsigned)rg), dim3(256), 0, stream, partial_area, sp,
                                count, j.c, j.ct);
         }
         const hipError_t e = hipGetLastError();
@@ -1325,16 +1325,16 @@ int launch_gemm(const GemmJob& j, char* msg, size_t msg_len) {
     const PackOperand pa{j.a_scales, j.M, frags_of(j.M) * runs, reinterpret_cast<uint32_t*>(a_pack)};
     const PackOperand pb{j.b_scales, j.N, frags_of(j.N) * runs, reinterpret_cast<uint32_t*>(b_pack)};
     if (pa.groups + pb.groups > 0)  // none when K = 0
-        hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)(pa.groups + pb.groups)), dim3(kPackThreads), 0,
+        FP4Q_LAUNCH(k_pack_scales, dim3((unsigned)(pa.groups + pb.groups)), dim3(kPackThreads), 0,
                            stream, pa, pb, kb, S);
     const int sp = splits_for(j.M, j.N, j.K);
     float* partial = partial_area;
     GParams p{j.a_codes, j.b_codes, a_pack, b_pack, j.M, j.N, j.K, S, j.c, j.ct, sp, partial};
-    hipLaunchKernelGGL(k_gemm_mxfp4, dim3((unsigned)(tiles * sp)), dim3(kThreads), 0, stream, p);
+    FP4Q_LAUNCH(k_gemm_mxfp4, dim3((unsigned)(tiles * sp)), dim3(kThreads), 0, stream, p);
     if (sp > 1) {
         const int64_t count = j.M * j.N;
         const int64_t groups = std::min<int64_t>((count + 1023) / 1024, 8192);
-        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)groups), dim3(256), 0, stream, partial, sp,
+        FP4Q_LAUNCH(k_splitk_reduce, dim3((unsigned)groups), dim3(256), 0, stream, partial, sp,
                            count, j.c, j.ct);
     }
     const hipError_t e = hipGetLastError();

@@ -1890,7 +1890,7 @@ int report(hipError_t e, const char* what, char* msg, size_t len) {
 
 // Sums the partials of a G-workgroup stats kernel.
 int launch_finalize(const StatsOut& so, int G, hipStream_t st, char* msg, size_t len) {
-    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kThreads), 0, st, so, G);
+    FP4Q_LAUNCH(k_finalize, dim3(1), dim3(kThreads), 0, st, so, G);
     return report(hipGetLastError(), "finalize kernel launch", msg, len);
 }
 
@@ -1956,12 +1956,12 @@ int launch_quantize_rows(const QuantJob& j, char* msg, size_t msg_len) {
     hipStream_t st = static_cast<hipStream_t>(j.stream);
     if (j.n == 0) {
         if (j.rows > 0) {
-            hipLaunchKernelGGL(k_fill_ones, dim3(16), dim3(256), 0, st, j.g, j.rows);
+            FP4Q_LAUNCH(k_fill_ones, dim3(16), dim3(256), 0, st, j.g, j.rows);
             int rc = report(hipGetLastError(), "fill kernel launch", msg, msg_len);
             if (rc) return rc;
         }
         if (j.stats) {
-            hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, st, j.stats, nullptr);
+            FP4Q_LAUNCH(k_empty, dim3(1), dim3(64), 0, st, j.stats, nullptr);
             return report(hipGetLastError(), "empty-tensor kernel", msg, msg_len);
         }
         return 0;
@@ -1997,7 +1997,7 @@ int launch_quantize_rows(const QuantJob& j, char* msg, size_t msg_len) {
     rp.rows = j.rows;
     rp.cols = j.cols;
     rp.g_rows = j.g;
-    hipLaunchKernelGGL(k, dim3((int)G), dim3(kThreads), 0, st, rp);
+    FP4Q_LAUNCH(k, dim3((int)G), dim3(kThreads), 0, st, rp);
     int rc = report(hipGetLastError(), "per-row quantize kernel launch", msg, msg_len);
     if (rc || !j.stats) return rc;
     return launch_finalize(p.so, (int)G, st, msg, msg_len);
@@ -2064,6 +2064,34 @@ MseKernel pick_mse_block(int block, int rotate, bool sumsq) {
 
 }  // namespace
 
+namespace {
+thread_local void* const* t_events = nullptr;
+thread_local int t_pairs = 0;
+thread_local int t_used = 0;
+}  // namespace
+
+void profile_set(void* const* events, int n_pairs) {
+    t_events = n_pairs > 0 ? events : nullptr;
+    t_pairs = t_events ? n_pairs : 0;
+    t_used = 0;
+}
+
+int profile_count() { return t_used; }
+
+void profile_before(void* stream) {
+    if (t_used < t_pairs)
+        (void)hipEventRecord(static_cast<hipEvent_t>(t_events[2 * t_used]),
+                             static_cast<hipStream_t>(stream));
+}
+
+void profile_after(void* stream) {
+    if (t_used < t_pairs) {
+        (void)hipEventRecord(static_cast<hipEvent_t>(t_events[2 * t_used + 1]),
+                             static_cast<hipStream_t>(stream));
+        ++t_used;
+    }
+}
+
 int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     if (j.gmode == 3) return launch_quantize_rows(j, msg, msg_len);
     hipStream_t st = static_cast<hipStream_t>(j.stream);
@@ -2071,7 +2099,7 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     const bool dynamic = (j.fmt != kFmtMx) && (j.gmode == 1);
     if (j.n == 0) {
         if (j.stats || dynamic) {
-            hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, st, j.stats, dynamic ? j.g : nullptr);
+            FP4Q_LAUNCH(k_empty, dim3(1), dim3(64), 0, st, j.stats, dynamic ? j.g : nullptr);
             return report(hipGetLastError(), "empty-tensor kernel", msg, msg_len);
         }
         return 0;
@@ -2127,7 +2155,7 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
             p.so.sumsq_part = a.sumsq;
             p.so.G_sumsq = sa.G;
             G_amax = sa.G;
-            hipLaunchKernelGGL(ka, dim3(G_amax), dim3(kAmaxThreads), 0, st, a);
+            FP4Q_LAUNCH(ka, dim3(G_amax), dim3(kAmaxThreads), 0, st, a);
             int rc = report(hipGetLastError(), "amax kernel launch", msg, msg_len);
             if (rc) return rc;
             p.amax_part = a.part;
@@ -2137,7 +2165,7 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
             p.g_in = j.g;
         }
     }
-    hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
+    FP4Q_LAUNCH(k, dim3(G), dim3(kThreads), 0, st, p);
     int rc = report(hipGetLastError(), "quantize kernel launch", msg, msg_len);
     if (rc || !j.stats) return rc;
     return launch_finalize(p.so, G, st, msg, msg_len);
@@ -2157,7 +2185,7 @@ int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len) {
                       : pick_dequant_block<kFmtUe4m3, 0>(j.block, j.rotate);
     const Split sp = split_for(chunks, reinterpret_cast<const void*>(k), kStreamCpwLight);
     p.cpw = sp.cpw;
-    hipLaunchKernelGGL(k, dim3(sp.G), dim3(kThreads), 0, st, p);
+    FP4Q_LAUNCH(k, dim3(sp.G), dim3(kThreads), 0, st, p);
     return report(hipGetLastError(), "dequantize kernel launch", msg, msg_len);
 }
 
@@ -2165,7 +2193,7 @@ int launch_block_mse(const MseJob& j, char* msg, size_t msg_len) {
     hipStream_t st = static_cast<hipStream_t>(j.stream);
     if (j.n == 0) {
         if (j.stats) {
-            hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, st, j.stats, nullptr);
+            FP4Q_LAUNCH(k_empty, dim3(1), dim3(64), 0, st, j.stats, nullptr);
             return report(hipGetLastError(), "empty-tensor kernel", msg, msg_len);
         }
         return 0;
@@ -2200,7 +2228,7 @@ int launch_block_mse(const MseJob& j, char* msg, size_t msg_len) {
                                j.stats == nullptr ? kStreamCpwLight : kStreamCpw);
     const int G = sp.G;
     p.cpw = sp.cpw;
-    hipLaunchKernelGGL(k, dim3(G), dim3(kThreads), 0, st, p);
+    FP4Q_LAUNCH(k, dim3(G), dim3(kThreads), 0, st, p);
     int rc = report(hipGetLastError(), "block-mse kernel launch", msg, msg_len);
     if (rc || !j.stats) return rc;
     return launch_finalize(p.so, G, st, msg, msg_len);
@@ -2216,7 +2244,7 @@ int launch_rotate(const RotateJob& j, char* msg, size_t msg_len) {
     else k = j.rotate == 16 ? k_rotate<1, 16> : k_rotate<1, 32>;
     const Split sp = split_for(chunks, reinterpret_cast<const void*>(k), kStreamCpwLight);
     p.cpw = sp.cpw;
-    hipLaunchKernelGGL(k, dim3(sp.G), dim3(kThreads), 0, st, p);
+    FP4Q_LAUNCH(k, dim3(sp.G), dim3(kThreads), 0, st, p);
     return report(hipGetLastError(), "rotate kernel launch", msg, msg_len);
 }
 

@@ -108,6 +108,22 @@ struct GemmNvJob {
 
 size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+// Launch timing (fp4q_profile_events): while the calling thread has event
+// pairs left, every kernel launch records the next pair on its stream around
+// itself.  Streams and events are passed as void*.
+void profile_set(void* const* events, int n_pairs);
+int profile_count();
+void profile_before(void* stream);
+void profile_after(void* stream);
+
+// A kernel launch bracketed by the timing hooks (used for every launch).
+#define FP4Q_LAUNCH(kernel, grid, block, shmem, stream, ...)                       \
+    do {                                                                           \
+        ::fp4q::profile_before(stream);                                            \
+        hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);       \
+        ::fp4q::profile_after(stream);                                             \
+    } while (0)
+
 // Each returns 0 on success, else a HIP error code; `msg` gets a description.
 int launch_quantize(const QuantJob& j, char* msg, size_t msg_len);
 int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len);

@@ -43,7 +43,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.fp4q_abi_version() == 1
+    assert L.fp4q_abi_version() == 2
     assert L.fp4q_workspace_bytes(1, 32, 32) > 0
 
 
@@ -232,3 +232,17 @@ def test_missing_library_raises(tmp_path, monkeypatch):
     monkeypatch.setattr(fq, "_lib", None)
     with pytest.raises(fq.Fp4qError):
         fq.lib()
+
+
+def test_profile_events_validation(L):
+    assert L.fp4q_profile_events(None, -1) == ARG and "negative" in err(L)
+    assert L.fp4q_profile_events(None, 0) == OK
+    assert L.fp4q_profile_count() == 0
+    # Recording on, but an argument error launches nothing, so nothing is recorded.
+    handles = (ctypes.c_void_p * 2)(A16, A16b)
+    assert L.fp4q_profile_events(handles, 1) == OK
+    assert mx(L, x=None) == ARG
+    assert L.fp4q_profile_count() == 0
+    assert L.fp4q_profile_events(None, 0) == OK
+
+

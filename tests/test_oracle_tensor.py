@@ -334,3 +334,19 @@ def test_small_block_inversion_under_ue4m3(orc):
     t16 = orc.quantize(x, orc.FMT_UE4M3, 16)["terms"][:3].sum()
     assert t8 > t16
     assert mse_model.predict(0.002, 8)["total"] > mse_model.predict(0.002, 16)["total"]
+
+
+def test_model_fixture_is_current():
+    """The stored three-term model table the benchmark prints equals the model."""
+    import json
+    import os
+    import sys
+    golden = os.path.join(os.path.dirname(__file__), "golden")
+    sys.path.insert(0, golden)
+    import make_mse_model
+    stored = json.load(open(os.path.join(golden, "mse_model_llama8.json")))["terms"]
+    fresh = make_mse_model.table()
+    assert stored.keys() == fresh.keys()
+    for k in fresh:
+        for t in fresh[k]:
+            assert stored[k][t] == pytest.approx(fresh[k][t], rel=1e-12, abs=1e-300), (k, t)
