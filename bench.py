@@ -198,6 +198,78 @@ def write_traffic(workload, fetch_dir, write_dir, out_json=None):
     print(json.dumps(rec))
 
 
+COUNTER_CLOCK_GHZ = 2.4  # MI355X peak engine clock; the clock under load is lower
+
+
+def write_counters(workload, out_md, bench_line, dirs):
+    """Summarise rocprofv3 counter runs (csv output, -o run, of the workload's
+    counter command) per kernel instantiation: instructions per 512-element
+    chunk, and the derived busy figures rocprofv3 computes.  `bench_line` is
+    an untraced bench.py JSON line of the same workload; its per-format
+    launch times give the VALU issue share (VALU wave-instructions over
+    256 CUs x the launch time x the peak clock, one wave-instruction per CU
+    per cycle; a lower bound, since the clock under load is lower)."""
+    import csv
+    import fp4_workloads as wl
+    if workload != "qwen14model":
+        raise SystemExit("--write-counters covers the qwen14model workload")
+    plan = _traffic_plan(workload)
+    line = json.loads(open(bench_line).read().strip().splitlines()[-1])
+    spec_us = {k: v["us_per_launch"] for k, v in line["roofline"]["per_spec"].items()}
+    amax_us = line["roofline"].get("s0_amax_pass", {}).get("us_per_launch")
+    mean_elems = sum(r * c for _, (r, c) in wl.QWEN14_PROJ) / len(wl.QWEN14_PROJ)
+    chunks = mean_elems / 512
+    kinds = {"k_quantize<0, 0, 32": ("MXFP4 b32 quantize (relative MSE, three-term split)", spec_us.get("mx32")),
+             "k_quantize<0, 1, 16": ("NVFP4 b16 quantize (dynamic g, relative MSE, three-term split)",
+                                     spec_us.get("nv16_dyn")),
+             "k_amax": ("amax pre-pass of dynamic NVFP4 (also sums x^2)", amax_us)}
+    acc = {}
+    for d in dirs:
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            kn = r["Kernel_Name"]
+            key = next((k for k in kinds if k in kn), None)
+            if key is None:
+                continue
+            a = acc.setdefault(key, {})
+            a.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            a.setdefault("_vgpr", set()).add(int(r["VGPR_Count"]) + int(r["Accum_VGPR_Count"]))
+            a.setdefault("_sgpr", set()).add(int(r["SGPR_Count"]))
+    rel = lambda d: os.path.relpath(os.path.abspath(d), ROOT)
+    lines = [f"# Instruction and busy counters per launch: bench.py workload `{workload}`", "",
+             "Counter runs (from the repository root on the MI355X box), one counter set per run, "
+             "csv output under the directories named:", "", "```"]
+    lines += [f"rocprofv3 --pmc <set> --output-format csv -d {rel(d)} -o run -- {plan['run']}" for d in dirs]
+    lines += ["```", "", f"then `python bench.py --workload {workload} --write-counters {out_md} "
+              f"{rel(bench_line)} {' '.join(rel(d) for d in dirs)}`.  Launch times come from the untraced "
+              f"bench line ({rel(bench_line)}: per-format mean over the step's launches).", "",
+              f"A chunk is 512 elements; one layer's seven projections average {mean_elems / 1e6:.2f} M "
+              f"elements ({chunks:,.0f} chunks) per launch.  VALU issue share = VALU wave-instructions / "
+              f"(256 CUs x launch time x {COUNTER_CLOCK_GHZ} GHz), one wave-instruction per CU per cycle; "
+              "the clock under load is lower than the peak, so the true share is higher.  VALUBusy, "
+              "SALUBusy and MemUnitStalled are rocprofv3's derived metrics (percent of the counter "
+              "window, which also covers the dispatch's start and drain).", ""]
+    hdr = None
+    for key, (label, us) in kinds.items():
+        if key not in acc:
+            continue
+        a = acc[key]
+        mean = {c: sum(v) / len(v) for c, v in a.items() if not c.startswith("_")}
+        n_disp = max(len(v) for c, v in a.items() if not c.startswith("_"))
+        lines += [f"## `{key}...>`: {label}", "",
+                  f"{n_disp} dispatches per counter; VGPRs {sorted(a['_vgpr'])}, SGPRs {sorted(a['_sgpr'])}; "
+                  f"launch time {us} us (untraced).", "", "| counter | mean per launch | per chunk |",
+                  "|---|---|---|"]
+        for c in sorted(mean):
+            per = f"{mean[c] / chunks:.2f}" if c.startswith("SQ_INSTS") else ""
+            lines.append(f"| {c} | {mean[c]:,.2f} | {per} |")
+        if "SQ_INSTS_VALU" in mean and us:
+            share = mean["SQ_INSTS_VALU"] / (256 * us * 1e-6 * COUNTER_CLOCK_GHZ * 1e9)
+            lines += ["", f"VALU issue share (lower bound): {share:.3f}"]
+        lines.append("")
+    open(out_md, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
 # ------------------------------------------------------------------ workloads
 class Spec:
     """One quantization call applied to every tensor of a workload."""
@@ -762,7 +834,8 @@ def three_term_table(fq, run, sigmas):
 def launch_times(fq, torch, run):
     """Every call of one step replayed back to back on one stream, each kernel
     launch timed with HIP events on that stream (fp4q_profile_events).  Returns
-    {kind: [(us, algorithmic bytes)]} for kinds amax, quantize and finalize."""
+    {kind: [(us, algorithmic bytes, spec index, tensor shape)]} for kinds amax,
+    quantize and finalize."""
     seq = []
     for ti, x in enumerate(run.xs):
         for si, s in enumerate(run.specs):
@@ -780,7 +853,7 @@ def launch_times(fq, torch, run):
         raise RuntimeError(f"recorded {len(us)} launches, expected {len(seq)}")
     out = {}
     for (ti, si, kind, nb), u in zip(seq, us):
-        out.setdefault(kind, []).append((u, nb, si))
+        out.setdefault(kind, []).append((u, nb, si, "x".join(map(str, run.xs[ti].shape))))
     return out
 
 
@@ -822,9 +895,18 @@ def main():
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the workload's traffic record under profiles/ from two "
                          "rocprofv3 counter runs, then exit (no GPU needed)")
+    ap.add_argument("--write-counters", nargs="+", metavar="ARG",
+                    help="OUT_MD BENCH_LINE DIR...: summarise rocprofv3 instruction/busy counter "
+                         "runs of the workload into OUT_MD, then exit (no GPU needed)")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(args.workload, *args.write_traffic)
+        return
+    if args.write_counters:
+        if len(args.write_counters) < 3:
+            ap.error("--write-counters needs OUT_MD BENCH_LINE and at least one DIR")
+        write_counters(args.workload, args.write_counters[0], args.write_counters[1],
+                       args.write_counters[2:])
         return
     if args.gpus != 1:
         print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -877,15 +959,24 @@ def main():
     # replayed on one stream, each launch timed with events on that stream).
     lt = launch_times(fq, torch, run)
     q = lt["quantize"]
-    q_us, q_bytes = sum(u for u, _, _ in q), sum(nb for _, nb, _ in q)
+    q_us, q_bytes = sum(e[0] for e in q), sum(e[1] for e in q)
     achieved = q_bytes / (q_us * 1e-6) / 1e9
     per_spec = {}
     for si, s in enumerate(w.specs):
-        sel = [(u, nb) for u, nb, sj in q if sj == si]
-        su, sb = sum(u for u, _ in sel), sum(nb for _, nb in sel)
+        sel = [e for e in q if e[2] == si]
+        su, sb = sum(e[0] for e in sel), sum(e[1] for e in sel)
+        by_shape = {}
+        for e in sel:
+            by_shape.setdefault(e[3], []).append(e)
         per_spec[s.tag] = {"launches": len(sel), "us_per_launch": round(su / len(sel), 3),
                            "GBps": round(sb / (su * 1e-6) / 1e9, 1),
                            "frac": round(sb / (su * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        if len(by_shape) > 1:
+            per_spec[s.tag]["by_shape"] = {
+                shp: {"launches": len(v), "us_per_launch": round(sum(e[0] for e in v) / len(v), 3),
+                      "frac": round(sum(e[1] for e in v) / (sum(e[0] for e in v) * 1e-6) / 1e9
+                                    / HBM_PEAK_GBS, 4)}
+                for shp, v in by_shape.items()}
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": read_traffic(args.workload) if args.workload in TRAFFIC else None,
@@ -896,7 +987,7 @@ def main():
                 "launches": len(q), "per_spec": per_spec}
     if "amax" in lt:
         a = lt["amax"]
-        a_us, a_bytes = sum(u for u, _, _ in a), sum(nb for _, nb, _ in a)
+        a_us, a_bytes = sum(e[0] for e in a), sum(e[1] for e in a)
         roofline["s0_amax_pass"] = {
             "kernel": "k_amax (per-tensor amax for the dynamic scale: reads the input once)",
             "launches": len(a), "us_per_launch": round(a_us / len(a), 3),
@@ -904,7 +995,7 @@ def main():
             "frac": round(a_bytes / (a_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     if "finalize" in lt:
         f = lt["finalize"]
-        roofline["stats_reduction_us_per_launch"] = round(sum(u for u, _, _ in f) / len(f), 3)
+        roofline["stats_reduction_us_per_launch"] = round(sum(e[0] for e in f) / len(f), 3)
 
     # Per-spec breakdown: one timed pass of each call type over all tensors.
     breakdown = {}
