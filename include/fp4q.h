@@ -326,6 +326,21 @@ const char* fp4q_last_error(void);
 /* FP4Q_ABI_VERSION of the loaded library. */
 int32_t fp4q_abi_version(void);
 
+/* nvfp4_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, outputs and errors without `ws`/`ws_bytes`.  The
+ * workspace is instead a static device array inside the library
+ * (fp4q_workspace_bytes() bytes, about 0.8 MB, a fixed maximum that every
+ * tensor size fits), one per device, kept until the process ends; its device
+ * address is looked up once per device (FP4Q_ERR_HIP if that fails).  Nothing
+ * is allocated.  All calls on one device share that array, so calls that
+ * overlap on one device (e.g. on two streams) race; calls in stream order do
+ * not. */
+fp4q_status nvfp4_quantize_noalloc(const void* x, int32_t xt, int64_t rows, int64_t cols,
+                                   int32_t block, int32_t scale_fmt, int32_t gmode, float* g,
+                                   int32_t rotate, uint8_t* codes, uint8_t* scales, float* block_mse,
+                                   int32_t mse_kind, fp4q_stats* stats, void* stream);
+
 /* Launch timing, for benchmarks and profiling (no counterpart on the pages).
  * events: 2 * n_pairs HIP events (hipEvent_t passed as void*), created and
  * owned by the caller (with timing enabled to read durations).  From this call

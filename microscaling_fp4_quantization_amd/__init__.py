@@ -33,7 +33,7 @@ G_NONE, G_DYNAMIC, G_GIVEN, G_ROW = 0, 1, 2, 3
 MSE_ABS, MSE_REL = 0, 1
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
 
-EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "fp4_quantize_search",
+EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "nvfp4_quantize_noalloc", "fp4_quantize_search",
            "fp4_dequantize",
            "fp4_block_mse", "hadamard_block_rotate", "fp4_gemm_mxfp4", "fp4_gemm_workspace_bytes",
            "fp4_gemm_nvfp4", "fp4_gemm_nvfp4_workspace_bytes",
@@ -66,6 +66,8 @@ def _bind(l):
     P, i32, i64, sz = c.c_void_p, c.c_int32, c.c_int64, c.c_size_t
     l.mxfp4_quantize.argtypes = [P, i32, i64, i64, i32, P, P, P, i32, P, P, sz, P]
     l.nvfp4_quantize.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, P, P, P, i32, P, P, sz, P]
+    l.nvfp4_quantize_noalloc.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, P, P, P, i32, P, P]
+    l.nvfp4_quantize_noalloc.restype = c.c_int
     l.fp4_dequantize.argtypes = [P, P, i32, i32, P, i64, i64, i32, P, i32, P]
     l.fp4_quantize_search.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, i32, P, P, P, i32,
                                       P, P, sz, P]
@@ -221,6 +223,23 @@ def nvfp4_quantize(x: torch.Tensor, block: int = 16, scale_fmt: int = FMT_UE4M3,
                                 scale_fmt, gmode, _ptr(g), rotate, _ptr(codes), _ptr(scales),
                                 _ptr(block_mse), mse_kind, _ptr(stats), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(x.device)))
+    return Quantized(codes, scales, block_mse, stats, g)
+
+
+def nvfp4_quantize_noalloc(x: torch.Tensor, block: int = 16, scale_fmt: int = FMT_UE4M3,
+                           gmode: int = G_DYNAMIC, g: Optional[torch.Tensor] = None,
+                           rotate: int = 0, *, codes=None, scales=None, block_mse=True,
+                           mse_kind: int = MSE_ABS, stats=True) -> Quantized:
+    """nvfp4_quantize on the library's static device scratch (no workspace).
+    The library allocates nothing; pass preallocated outputs (``codes``,
+    ``scales``, ``block_mse``, ``stats``, ``g``) to allocate nothing here either."""
+    x = _matrix(x)
+    codes, scales, block_mse, stats = _outputs(x, block, codes, scales, block_mse, stats)
+    if gmode != G_NONE and g is None:
+        g = torch.empty(x.shape[0] if gmode == G_ROW else 1, dtype=torch.float32, device=x.device)
+    _check(lib().nvfp4_quantize_noalloc(_ptr(x), _dtype_code(x), x.shape[0], x.shape[1], block,
+                                        scale_fmt, gmode, _ptr(g), rotate, _ptr(codes), _ptr(scales),
+                                        _ptr(block_mse), mse_kind, _ptr(stats), _stream(x.device)))
     return Quantized(codes, scales, block_mse, stats, g)
 
 

@@ -78,7 +78,7 @@ fp4q_status quantize_common(const char* fn, const void* x, int32_t xt, int64_t r
                             int32_t block, int32_t fmt, int32_t gmode, float* g, int32_t rotate,
                             uint8_t* codes, uint8_t* scales, float* block_mse, int32_t mse_kind,
                             fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream,
-                            int32_t radius = -1) {
+                            int32_t radius = -1, bool scratch = false) {
     TRY(check_dtype(fn, xt));
     TRY(check_shape(fn, rows, cols, block, rotate));
     TRY(check_mse(fn, block_mse, mse_kind));
@@ -98,7 +98,13 @@ fp4q_status quantize_common(const char* fn, const void* x, int32_t xt, int64_t r
         if (!aligned(codes, 16)) return fail(FP4Q_ERR_ALIGN, "%s: codes is not 16-byte aligned", fn);
     }
     if (stats && !aligned(stats, 8)) return fail(FP4Q_ERR_ALIGN, "%s: stats is not 8-byte aligned", fn);
-    TRY(check_ws(fn, stats != nullptr || gmode == FP4Q_G_DYNAMIC, ws, ws_bytes));
+    const bool need_ws = stats != nullptr || gmode == FP4Q_G_DYNAMIC;
+    if (scratch && need_ws) {  // the library's static scratch instead of a caller's workspace
+        char msg[256] = {0};
+        if (fp4q::scratch_workspace(&ws, &ws_bytes, msg, sizeof msg))
+            return fail(FP4Q_ERR_HIP, "%s: %s", fn, msg);
+    }
+    TRY(check_ws(fn, need_ws, ws, ws_bytes));
     fp4q::QuantJob j{};
     j.x = x;
     j.xt = xt;
@@ -149,6 +155,18 @@ fp4q_status nvfp4_quantize(const void* x, int32_t xt, int64_t rows, int64_t cols
         return fail(FP4Q_ERR_ARG, "nvfp4_quantize: scale_fmt %d is not UE4M3 (1) or UE5M3 (2)", scale_fmt);
     return quantize_common("nvfp4_quantize", x, xt, rows, cols, block, scale_fmt, gmode, g, rotate,
                            codes, scales, block_mse, mse_kind, stats, ws, ws_bytes, stream);
+}
+
+fp4q_status nvfp4_quantize_noalloc(const void* x, int32_t xt, int64_t rows, int64_t cols,
+                                   int32_t block, int32_t scale_fmt, int32_t gmode, float* g,
+                                   int32_t rotate, uint8_t* codes, uint8_t* scales, float* block_mse,
+                                   int32_t mse_kind, fp4q_stats* stats, void* stream) {
+    if (scale_fmt != FP4Q_FMT_UE4M3 && scale_fmt != FP4Q_FMT_UE5M3)
+        return fail(FP4Q_ERR_ARG, "nvfp4_quantize_noalloc: scale_fmt %d is not UE4M3 (1) or UE5M3 (2)",
+                    scale_fmt);
+    return quantize_common("nvfp4_quantize_noalloc", x, xt, rows, cols, block, scale_fmt, gmode, g,
+                           rotate, codes, scales, block_mse, mse_kind, stats, nullptr, 0, stream, -1,
+                           true);
 }
 
 fp4q_status fp4_quantize_search(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t fmt,

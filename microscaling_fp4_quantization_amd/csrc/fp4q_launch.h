@@ -124,6 +124,11 @@ void profile_after(void* stream);
         ::fp4q::profile_after(stream);                                             \
     } while (0)
 
+// The library's static device scratch for the allocation-free entry point:
+// its device address on the current device (looked up once per device) and
+// its size (kWsBytes).  Returns 0, else a HIP error code with `msg` set.
+int scratch_workspace(void** ptr, size_t* bytes, char* msg, size_t msg_len);
+
 // Each returns 0 on success, else a HIP error code; `msg` gets a description.
 int launch_quantize(const QuantJob& j, char* msg, size_t msg_len);
 int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len);

@@ -246,3 +246,14 @@ def test_profile_events_validation(L):
     assert L.fp4q_profile_events(None, 0) == OK
 
 
+def test_noalloc_validation(L):
+    """Argument errors come back before the scratch is looked up (no GPU touched)."""
+    def nva(x=A16, fmt=1, gmode=0, g=None, block=16, cols=64, kind=0, stats=None):
+        return L.nvfp4_quantize_noalloc(x, 0, 4, cols, block, fmt, gmode, g, 0, A16b, A16c, None,
+                                        kind, stats, None)
+    assert nva(x=None) == ARG
+    assert nva(fmt=0) == ARG and "scale_fmt" in err(L)
+    assert nva(cols=40) == SHAPE
+    assert nva(gmode=2) == ARG and "g pointer" in err(L)
+    assert nva(kind=3) == ARG
+    assert nva(stats=A16 + 4) == ALIGN
