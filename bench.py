@@ -4,11 +4,13 @@ Default workload (one step = the whole path over one batch): a random-init
 Qwen2.5-14B-shaped stack, 48 layers x {q 5120x5120, k and v 1024x5120, o
 5120x5120, gate and up 13824x5120, down 5120x13824}, bf16 N(0, 0.02) seeded
 per tensor (13.2e9 parameters, 26.4 GB resident in HBM before timing).  Every
-tensor is quantized twice per step: MXFP4 (block 32, E8M0) and NVFP4 (block 16,
-UE4M3 under the dynamic FP32 per-tensor scale, whose amax pass reads the tensor
-once more), each with packed codes, scale bytes, the relative per-block MSE and
-the three-term error split.  The step spreads its independent calls over two
-HIP streams (one workspace each; --streams 1 runs them back to back).
+tensor is quantized twice per step, in one fp4_quantize_mx_nv call: MXFP4
+(block 32, E8M0) and NVFP4 (block 16, UE4M3 under the dynamic FP32 per-tensor
+scale, whose tensor maximum the MXFP4 pass takes on the way), each with packed
+codes, scale bytes, the relative per-block MSE and the three-term error split
+(--separate issues the two calls instead, NVFP4 with its own amax pass).  The
+step spreads its calls over two HIP streams (one workspace each; --streams 1
+runs them back to back).
 
 Prints one JSON line:
   value         GB/s of input quantized+packed+MSE'd over the whole step (every
@@ -104,9 +106,10 @@ def _traffic_plan(workload):
         # mean algorithmic bytes of one layer's 14 quantize launches (MXFP4 b32
         # and NVFP4 b16 of each projection, relative per-block MSE)
         alg = sum(n * (2 + 0.5 + 1 / 32 + 4 / 32) + n * (2 + 0.5 + 1 / 16 + 4 / 16) for n in ns) / (2 * len(ns))
-        return {"parts": [("k_quantize<0, ", None)],
-                "label": "k_quantize, the step's launches (MXFP4 b32 and dynamic NVFP4 b16 with relative "
-                         "per-block MSE and the three-term split): mean per launch over one layer's 14",
+        return {"parts": [("k_quantize", None)],
+                "label": "k_quantize_amax (MXFP4 b32) and k_quantize (NVFP4 b16 under the dynamic g), "
+                         "the step's launches, with relative per-block MSE and the three-term split: "
+                         "mean per launch over one layer's 14",
                 "calib_bytes": 5120 * 5120 * 2, "alg_bytes": int(alg),
                 "run": "python -u bench.py --layers 1 --steps 1 --warmup 0 --no-cpu-baseline "
                        "--calibration-copy"}
@@ -219,7 +222,9 @@ def write_counters(workload, out_md, bench_line, dirs):
     amax_us = line["roofline"].get("s0_amax_pass", {}).get("us_per_launch")
     mean_elems = sum(r * c for _, (r, c) in wl.QWEN14_PROJ) / len(wl.QWEN14_PROJ)
     chunks = mean_elems / 512
-    kinds = {"k_quantize<0, 0, 32": ("MXFP4 b32 quantize (relative MSE, three-term split)", spec_us.get("mx32")),
+    kinds = {"k_quantize_amax<0": ("MXFP4 b32 quantize (relative MSE, three-term split, tensor maximum)",
+                                   spec_us.get("mx32")),
+             "k_quantize<0, 0, 32": ("MXFP4 b32 quantize (relative MSE, three-term split)", spec_us.get("mx32")),
              "k_quantize<0, 1, 16": ("NVFP4 b16 quantize (dynamic g, relative MSE, three-term split)",
                                      spec_us.get("nv16_dyn")),
              "k_amax": ("amax pre-pass of dynamic NVFP4 (also sums x^2)", amax_us)}
@@ -270,9 +275,67 @@ def write_counters(workload, out_md, bench_line, dirs):
     print("\n".join(lines))
 
 
+def _short_kernel(name):
+    name = name.replace("fp4q::(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0] if "<" in name.split("(")[0] else name
+
+
+def write_trace(workload, out_md, bench_line, trace_dir, command):
+    """Summarise a `rocprofv3 --kernel-trace --stats` run of bench.py (csv
+    output, -o bench) into OUT_MD: every kernel's statistics, and the launches
+    of the roofline leg (the step replayed on one stream after the warm-up
+    and timed steps and one warm replay) set against the leg's own HIP-event
+    timing in the bench line the same run printed."""
+    import csv
+    line = json.loads(open(bench_line).read().strip().splitlines()[-1])
+    r = line["roofline"]
+    per_step_q = r["launches"]
+    specs = list(r["per_spec"])
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "bench_kernel_stats.csv"))))
+    trace = sorted(csv.DictReader(open(os.path.join(trace_dir, "bench_kernel_trace.csv"))),
+                   key=lambda t: int(t["Dispatch_Id"]))
+    quant = [t for t in trace if "k_quantize<" in t["Kernel_Name"] or "k_quantize_amax<" in t["Kernel_Name"]]
+    start = (line["warmup"] + line["steps"] + 1) * per_step_q
+    leg = quant[start:start + per_step_q]
+    if len(leg) != per_step_q:
+        raise SystemExit(f"trace holds {len(quant)} quantize launches; the leg needs {start + per_step_q}")
+    dur = lambda t: (int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) / 1e3
+    rel = lambda d: os.path.relpath(os.path.abspath(d), ROOT)
+    lines = [f"# Kernel trace: bench.py workload `{workload}`", "",
+             "Command (from the repository root on the MI355X box), then "
+             f"`python bench.py --workload {workload} --write-trace {out_md} {rel(bench_line)} "
+             f"{rel(trace_dir)} \"<command>\"` to write this file:", "", "```", command, "```", "",
+             "| kernel | calls | total us | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for s in stats:
+        lines.append(f"| `{_short_kernel(s['Name'])[:100]}` | {s['Calls']} | "
+                     f"{int(s['TotalDurationNs']) / 1e3:.1f} | {float(s['AverageNs']) / 1e3:.3f} | "
+                     f"{int(s['MinNs']) / 1e3:.3f} | {int(s['MaxNs']) / 1e3:.3f} |")
+    lines += ["", f"The timed steps run their calls on {line['config'].get('streams', 1)} streams, so "
+              "their launches overlap and the statistics above mix overlapped and lone launches.  "
+              f"The roofline leg is quantize launches {start} to {start + per_step_q - 1} in launch "
+              f"order ({line['warmup']} warm-up and {line['steps']} timed steps, then one warm replay "
+              "come before it): one step's calls replayed on one stream.", "",
+              "| roofline leg, per format | launches | trace avg us | bench events avg us | difference |",
+              "|---|---|---|---|---|"]
+    for si, tag in enumerate(specs):
+        sel = [dur(t) for i, t in enumerate(leg) if i % len(specs) == si]
+        tr = sum(sel) / len(sel)
+        ev = r["per_spec"][tag]["us_per_launch"]
+        lines.append(f"| {tag} | {len(sel)} | {tr:.3f} | {ev:.3f} | {100 * (ev - tr) / tr:+.2f} % |")
+    tr_all = sum(dur(t) for t in leg) / len(leg)
+    lines.append(f"| all | {len(leg)} | {tr_all:.3f} | {r['us_per_launch']:.3f} | "
+                 f"{100 * (r['us_per_launch'] - tr_all) / tr_all:+.2f} % |")
+    lines += ["", f"Bench line of this run (under the tracer): value {line['value']} GB/s, "
+              f"{line['ms_per_step']} ms per step, roofline frac {r['frac']}.", ""]
+    open(out_md, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
 # ------------------------------------------------------------------ workloads
 class Spec:
-    """One quantization call applied to every tensor of a workload."""
+    """One quantization call applied to every tensor of a workload.  fmt "pair"
+    is one fp4_quantize_mx_nv call: MXFP4 and dynamic NVFP4 (block `block`)
+    of the tensor, the NVFP4 per-tensor scale taken from the MXFP4 pass."""
 
     def __init__(self, tag, fmt, block, scale_fmt=1, gmode=0, rotate=0, mse_kind=0,
                  block_mse=True, stats=True, radius=None):
@@ -280,22 +343,39 @@ class Spec:
         self.gmode, self.rotate, self.mse_kind = gmode, rotate, mse_kind
         self.block_mse, self.stats = block_mse, stats
         self.radius = radius  # per-block scale search radius, None for the plain call
+        self.parts = []
+        if fmt == "pair":
+            self.parts = [Spec("mx32", "mx", 32, mse_kind=mse_kind, block_mse=block_mse, stats=stats),
+                          Spec(f"nv{block}_dyn", "nv", block, 1, 1, mse_kind=mse_kind,
+                               block_mse=block_mse, stats=stats)]
+
+    @property
+    def formats(self):
+        """Quantizations of each tensor one call performs."""
+        return len(self.parts) if self.parts else 1
 
     def algorithmic_bytes(self, n, in_bytes):
         """Bytes every kernel of the call must move: the amax pre-pass read (dynamic
-        NVFP4), the quantize read, codes, scale bytes and per-block MSE."""
-        b = n * (in_bytes + 0.5 + 1.0 / self.block + (4.0 / self.block if self.block_mse else 0))
+        NVFP4 alone), the quantize read, codes, scale bytes and per-block MSE."""
+        if self.parts:
+            return sum(p.quantize_bytes(n, in_bytes) for p in self.parts)
+        b = self.quantize_bytes(n, in_bytes)
         if self.fmt == "nv" and self.gmode == 1:
             b += n * in_bytes
         return b
 
     def launches(self):
-        """The kernels one call launches, in order."""
+        """The kernels one call launches, in order, each with the format it serves."""
+        if self.parts:  # the MXFP4 pass's reduction also forms g
+            return [(k, p.tag) for p in self.parts for k in ("quantize", "finalize")]
         seq = ["amax"] if (self.fmt == "nv" and self.gmode == 1) else []
         seq.append("quantize")
         if self.stats:
             seq.append("finalize")
-        return seq
+        return [(k, self.tag) for k in seq]
+
+    def part(self, tag):
+        return next(p for p in self.parts if p.tag == tag) if self.parts else self
 
     def quantize_bytes(self, n, in_bytes):
         """Algorithmic bytes of the quantize kernel alone: its read, the codes,
@@ -303,6 +383,8 @@ class Spec:
         return n * (in_bytes + 0.5 + 1.0 / self.block + (4.0 / self.block if self.block_mse else 0))
 
     def describe(self):
+        if self.parts:
+            return " + ".join(p.describe() for p in self.parts) + " (one call, g from the MXFP4 pass)"
         if self.fmt == "mx":
             s = "MXFP4 b32"
         else:
@@ -427,8 +509,8 @@ WORKLOADS = {
          "format": "MXFP4 b32 and NVFP4 b16 dynamic g",
          "outputs": "codes + scales + relative per-block MSE + per-tensor split"},
         _qwen14model_tensors,
-        [Spec("mx32", "mx", 32, mse_kind=1), Spec("nv16_dyn", "nv", 16, 1, 1, mse_kind=1)],
-        5, 1, ("layer 0's seven projections (q, k, v, o, gate, up, down), whole", 7, [0, 1])),
+        [Spec("mx32+nv16_dyn", "pair", 16, mse_kind=1)],
+        20, 3, ("layer 0's seven projections (q, k, v, o, gate, up, down), whole", 7, [0])),
 }
 
 
@@ -609,25 +691,40 @@ class Runner:
         # replay can reuse the step's g.
         shared = {}
         k = 0
+        def outputs(r, c, block, stream):
+            key = (r, c, block, stream)
+            if key not in shared:
+                shared[key] = dict(
+                    codes=torch.empty((r, c // 2), dtype=torch.uint8, device=dev),
+                    scales=torch.empty((r, c // block), dtype=torch.uint8, device=dev),
+                    block_mse=torch.empty((r, c // block), dtype=torch.float32, device=dev))
+            o = dict(shared[key])
+            o["stats"] = fq.new_stats(dev)
+            return o
+
         for ti, x in enumerate(xs):
             r, c = x.shape
             for si, s in enumerate(specs):
-                key = (r, c, s.block, k % n_streams)
+                stream = k % n_streams
                 k += 1
-                if key not in shared:
-                    shared[key] = dict(
-                        codes=torch.empty((r, c // 2), dtype=torch.uint8, device=dev),
-                        scales=torch.empty((r, c // s.block), dtype=torch.uint8, device=dev),
-                        block_mse=torch.empty((r, c // s.block), dtype=torch.float32, device=dev))
-                o = dict(shared[key])
-                o["stats"] = fq.new_stats(dev)
+                if s.parts:
+                    o = {p.tag: outputs(r, c, p.block, stream) for p in s.parts}
+                else:
+                    o = outputs(r, c, s.block, stream)
                 o["g"] = torch.ones(r if s.gmode == 3 else 1, dtype=torch.float32, device=dev)
-                o["stream"] = key[3]
+                o["stream"] = stream
                 self.out[(ti, si)] = o
 
     def call(self, ti, si, given=False, ws=None):
         fq, x, s, o = self.fq, self.xs[ti], self.specs[si], self.out[(ti, si)]
         ws = self.ws if ws is None else ws
+        if s.parts:
+            mx, nv = ({"codes": o[p.tag]["codes"], "scales": o[p.tag]["scales"],
+                       "block_mse": o[p.tag]["block_mse"] if s.block_mse else False,
+                       "stats": o[p.tag]["stats"] if (s.stats and not given) else False}
+                      for p in s.parts)
+            fq.fp4_quantize_mx_nv(x, s.block, mse_kind=s.mse_kind, mx=mx, nv=nv, g=o["g"], ws=ws)
+            return
         bm = o["block_mse"] if s.block_mse else False
         if s.radius is not None:
             fmt = fq.FMT_MXFP4 if s.fmt == "mx" else s.scale_fmt
@@ -740,6 +837,10 @@ def _cpu_model() -> str:
 def _oracle_call(oracle, xf, s, threads, pool):
     """One call of spec s on float32 array xf through the oracle, on row slices
     over `threads` threads (the per-tensor dynamic scale from the slices' amax)."""
+    if s.parts:
+        for p in s.parts:
+            _oracle_call(oracle, xf, p, threads, pool)
+        return
     fmt = oracle.FMT_MXFP4 if s.fmt == "mx" else s.scale_fmt
     rows = xf.shape[0]
     n = max(1, min(rows, 2 * threads))
@@ -780,7 +881,7 @@ def cpu_baseline(w, xs_host_sample):
         for xf, in_bytes in tensors:
             for s in specs:
                 _oracle_call(oracle, xf, s, nthreads, pool)
-                nbytes += xf.size * in_bytes
+                nbytes += xf.size * in_bytes * s.formats
         return nbytes, time.perf_counter() - t
 
     with ThreadPoolExecutor(threads) as pool:
@@ -834,16 +935,16 @@ def three_term_table(fq, run, sigmas):
 def launch_times(fq, torch, run):
     """Every call of one step replayed back to back on one stream, each kernel
     launch timed with HIP events on that stream (fp4q_profile_events).  Returns
-    {kind: [(us, algorithmic bytes, spec index, tensor shape)]} for kinds amax,
+    {kind: [(us, algorithmic bytes, format tag, tensor shape)]} for kinds amax,
     quantize and finalize."""
     seq = []
     for ti, x in enumerate(run.xs):
         for si, s in enumerate(run.specs):
             in_bytes = x.element_size()
-            for kind in s.launches():
-                nb = {"amax": x.numel() * in_bytes, "quantize": s.quantize_bytes(x.numel(), in_bytes),
-                      "finalize": 0}[kind]
-                seq.append((ti, si, kind, nb))
+            for kind, tag in s.launches():
+                nb = {"amax": x.numel() * in_bytes,
+                      "quantize": s.part(tag).quantize_bytes(x.numel(), in_bytes), "finalize": 0}[kind]
+                seq.append((ti, tag, kind, nb))
     run.step(given=False, one_stream=True)  # warm
     torch.cuda.synchronize()
     with fq.LaunchTimer(len(seq)) as t:
@@ -852,8 +953,8 @@ def launch_times(fq, torch, run):
     if len(us) != len(seq):
         raise RuntimeError(f"recorded {len(us)} launches, expected {len(seq)}")
     out = {}
-    for (ti, si, kind, nb), u in zip(seq, us):
-        out.setdefault(kind, []).append((u, nb, si, "x".join(map(str, run.xs[ti].shape))))
+    for (ti, tag, kind, nb), u in zip(seq, us):
+        out.setdefault(kind, []).append((u, nb, tag, "x".join(map(str, run.xs[ti].shape))))
     return out
 
 
@@ -887,6 +988,9 @@ def main():
     ap.add_argument("--workload", default="qwen14model", choices=sorted(WORKLOADS) + ["gemm"])
     ap.add_argument("--layers", type=int, default=None,
                     help="qwen14model: run only the first LAYERS layers (short counter runs)")
+    ap.add_argument("--separate", action="store_true",
+                    help="issue a combined MXFP4 + NVFP4 call as its two separate calls "
+                         "(NVFP4 with its own amax pass)")
     ap.add_argument("--streams", type=int, default=2,
                     help="HIP streams the step's independent calls are spread over")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -898,7 +1002,13 @@ def main():
     ap.add_argument("--write-counters", nargs="+", metavar="ARG",
                     help="OUT_MD BENCH_LINE DIR...: summarise rocprofv3 instruction/busy counter "
                          "runs of the workload into OUT_MD, then exit (no GPU needed)")
+    ap.add_argument("--write-trace", nargs=4, metavar=("OUT_MD", "BENCH_LINE", "TRACE_DIR", "COMMAND"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run of bench.py into OUT_MD, "
+                         "then exit (no GPU needed)")
     args = ap.parse_args()
+    if args.write_trace:
+        write_trace(args.workload, *args.write_trace)
+        return
     if args.write_traffic:
         write_traffic(args.workload, *args.write_traffic)
         return
@@ -920,6 +1030,10 @@ def main():
     global QWEN14_LAYERS_RUN
     QWEN14_LAYERS_RUN = args.layers
     w = WORKLOADS[args.workload]
+    if args.separate:
+        specs = [p for s in w.specs for p in (s.parts or [s])]
+        w = Workload(w.name, w.config, w.make_tensors, specs, w.steps, w.warmup,
+                     (w.sample[0], w.sample[1], list(range(len(specs)))), w.per_call)
     steps = args.steps if args.steps is not None else w.steps
     warmup = args.warmup if args.warmup is not None else w.warmup
 
@@ -936,7 +1050,7 @@ def main():
         del x
     in_bytes = xs[0].element_size()
     run = Runner(fq, torch, dev, xs, w.specs, max(1, args.streams))
-    n_elem_calls = sum(x.numel() for x in xs) * len(w.specs)
+    n_elem_calls = sum(x.numel() for x in xs) * sum(s.formats for s in w.specs)
     alg_bytes = sum(s.algorithmic_bytes(x.numel(), in_bytes) for x in xs for s in w.specs)
 
     for _ in range(warmup):
@@ -962,17 +1076,17 @@ def main():
     q_us, q_bytes = sum(e[0] for e in q), sum(e[1] for e in q)
     achieved = q_bytes / (q_us * 1e-6) / 1e9
     per_spec = {}
-    for si, s in enumerate(w.specs):
-        sel = [e for e in q if e[2] == si]
+    for tag in dict.fromkeys(e[2] for e in q):
+        sel = [e for e in q if e[2] == tag]
         su, sb = sum(e[0] for e in sel), sum(e[1] for e in sel)
         by_shape = {}
         for e in sel:
             by_shape.setdefault(e[3], []).append(e)
-        per_spec[s.tag] = {"launches": len(sel), "us_per_launch": round(su / len(sel), 3),
+        per_spec[tag] = {"launches": len(sel), "us_per_launch": round(su / len(sel), 3),
                            "GBps": round(sb / (su * 1e-6) / 1e9, 1),
                            "frac": round(sb / (su * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         if len(by_shape) > 1:
-            per_spec[s.tag]["by_shape"] = {
+            per_spec[tag]["by_shape"] = {
                 shp: {"launches": len(v), "us_per_launch": round(sum(e[0] for e in v) / len(v), 3),
                       "frac": round(sum(e[1] for e in v) / (sum(e[0] for e in v) * 1e-6) / 1e9
                                     / HBM_PEAK_GBS, 4)}
@@ -993,6 +1107,11 @@ def main():
             "launches": len(a), "us_per_launch": round(a_us / len(a), 3),
             "GBps": round(a_bytes / (a_us * 1e-6) / 1e9, 1),
             "frac": round(a_bytes / (a_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    elif any(s.parts for s in w.specs):
+        roofline["s0_amax_pass"] = {
+            "kernel": "none: the MXFP4 quantize launch of each fp4_quantize_mx_nv call also takes "
+                      "the tensor maximum (per-workgroup maxima, reduced to g by its stats reduction), "
+                      "so the NVFP4 pass needs no amax read"}
     if "finalize" in lt:
         f = lt["finalize"]
         roofline["stats_reduction_us_per_launch"] = round(sum(e[0] for e in f) / len(f), 3)
@@ -1030,6 +1149,7 @@ def main():
         torch.cuda.synchronize()
 
     config = {"workload": w.name, **w.config, "elements_per_step": n_elem_calls,
+              "calls": "; ".join(s.describe() for s in w.specs),
               "streams": max(1, args.streams),
               "arithmetic": "binary32 scales and codes, binary64 error sums"}
     if args.workload == "qwen14model":

@@ -161,6 +161,32 @@ fp4q_status nvfp4_quantize(const void* x, int32_t xt, int64_t rows, int64_t cols
                            fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * One tensor in both formats ("Diagnosing FP4 inference", technical summary
+ * section 2: each layer's tensors quantized to NVFP4 and to MXFP4 and their
+ * errors compared): mxfp4_quantize (no rotation) and nvfp4_quantize with UE4M3
+ * scales under the dynamic per-tensor scale (no rotation), as one call.  The
+ * MXFP4 pass reads every element anyway, so it also takes the tensor maximum,
+ * and the NVFP4 pass uses it: the tensor is read twice instead of three times
+ * (no separate amax pass).
+ *   mx_*       outputs of the MXFP4 pass, as for mxfp4_quantize (block 32)
+ *   nv_block   block of the NVFP4 pass (8 ... 256, dividing cols)
+ *   g          device out, one float: the per-tensor scale RN32(amax / 2688)
+ *              (1 when amax is 0), as nvfp4_quantize writes in the dynamic mode
+ *   nv_*       outputs of the NVFP4 pass, as for nvfp4_quantize
+ *   mse_kind   kind of both per-block MSE outputs
+ *   ws         fp4q_workspace_bytes() bytes, always needed
+ * Every output equals the two separate calls' outputs bit for bit, except the
+ * NVFP4 pass's sum_x2 term under FP4Q_MSE_ABS, which is summed in a different
+ * order (equal to rounding).  Errors as for the two calls; nothing is launched
+ * unless both calls' arguments are valid.
+ */
+fp4q_status fp4_quantize_mx_nv(const void* x, int32_t xt, int64_t rows, int64_t cols,
+                               uint8_t* mx_codes, uint8_t* mx_scales, float* mx_block_mse,
+                               fp4q_stats* mx_stats, int32_t nv_block, float* g, uint8_t* nv_codes,
+                               uint8_t* nv_scales, float* nv_block_mse, fp4q_stats* nv_stats,
+                               int32_t mse_kind, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Quantization with a per-block scale search ("Bridging the Gap...", Sommario
  * tecnico section 3 item 2: scales chosen to minimise the reconstruction MSE
  * rather than taken from the block maximum).  The page gives no procedure; this

@@ -33,7 +33,8 @@ G_NONE, G_DYNAMIC, G_GIVEN, G_ROW = 0, 1, 2, 3
 MSE_ABS, MSE_REL = 0, 1
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
 
-EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "nvfp4_quantize_noalloc", "fp4_quantize_search",
+EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "nvfp4_quantize_noalloc", "fp4_quantize_mx_nv",
+           "fp4_quantize_search",
            "fp4_dequantize",
            "fp4_block_mse", "hadamard_block_rotate", "fp4_gemm_mxfp4", "fp4_gemm_workspace_bytes",
            "fp4_gemm_nvfp4", "fp4_gemm_nvfp4_workspace_bytes",
@@ -68,6 +69,8 @@ def _bind(l):
     l.nvfp4_quantize.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, P, P, P, i32, P, P, sz, P]
     l.nvfp4_quantize_noalloc.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, P, P, P, i32, P, P]
     l.nvfp4_quantize_noalloc.restype = c.c_int
+    l.fp4_quantize_mx_nv.argtypes = [P, i32, i64, i64, P, P, P, P, i32, P, P, P, P, P, i32, P, sz, P]
+    l.fp4_quantize_mx_nv.restype = c.c_int
     l.fp4_dequantize.argtypes = [P, P, i32, i32, P, i64, i64, i32, P, i32, P]
     l.fp4_quantize_search.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, i32, P, P, P, i32,
                                       P, P, sz, P]
@@ -243,6 +246,31 @@ def nvfp4_quantize_noalloc(x: torch.Tensor, block: int = 16, scale_fmt: int = FM
     return Quantized(codes, scales, block_mse, stats, g)
 
 
+def fp4_quantize_mx_nv(x: torch.Tensor, nv_block: int = 16, *, mse_kind: int = MSE_ABS,
+                       block_mse=True, stats=True, mx=None, nv=None, g=None,
+                       ws: Optional[torch.Tensor] = None):
+    """MXFP4 and dynamic NVFP4 (UE4M3 scales) of one unrotated tensor in one call;
+    the NVFP4 per-tensor scale comes from the MXFP4 pass (no separate amax pass).
+
+    ``mx`` / ``nv``: optional dicts of preallocated outputs (keys ``codes``,
+    ``scales``, ``block_mse``, ``stats``).  Returns (Quantized MXFP4, Quantized
+    NVFP4); the NVFP4 one carries ``g``."""
+    x = _matrix(x)
+    mx, nv = dict(mx or {}), dict(nv or {})
+    m = _outputs(x, 32, mx.get("codes"), mx.get("scales"), mx.get("block_mse", block_mse),
+                 mx.get("stats", stats))
+    v = _outputs(x, nv_block, nv.get("codes"), nv.get("scales"), nv.get("block_mse", block_mse),
+                 nv.get("stats", stats))
+    if g is None:
+        g = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = ws if ws is not None else workspace(x.device)
+    _check(lib().fp4_quantize_mx_nv(_ptr(x), _dtype_code(x), x.shape[0], x.shape[1],
+                                    _ptr(m[0]), _ptr(m[1]), _ptr(m[2]), _ptr(m[3]), nv_block, _ptr(g),
+                                    _ptr(v[0]), _ptr(v[1]), _ptr(v[2]), _ptr(v[3]), mse_kind,
+                                    _ptr(ws), ws.numel(), _stream(x.device)))
+    return Quantized(*m, None), Quantized(*v, g)
+
+
 def fp4_quantize_search(x: torch.Tensor, fmt: int = FMT_UE4M3, block: int = 16,
                         gmode: int = G_DYNAMIC, g: Optional[torch.Tensor] = None, rotate: int = 0,
                         radius: int = 1, *, codes=None, scales=None, block_mse=True,
@@ -372,6 +400,24 @@ def hadamard_block_rotate(x: torch.Tensor, n: int, out: Optional[torch.Tensor] =
     return out
 
 
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hip_runtime_api.h
+
+
+def _hip_runtime():
+    """The HIP runtime torch has loaded (for fence-free timing events)."""
+    global _HIP
+    if _HIP is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _HIP = h
+    return _HIP
+
+
+_HIP = None
+
+
 class LaunchTimer:
     """Times the library's kernel launches with HIP events (fp4q_profile_events).
 
@@ -379,15 +425,28 @@ class LaunchTimer:
     this thread (up to ``n``) is bracketed by a pair of events on its stream;
     afterwards ``t.durations_us()`` (which synchronises) gives their durations
     in launch order.  A quantize call launches the amax pass (dynamic scale
-    only), the quantize kernel and the stats reduction (stats only)."""
+    only), the quantize kernel and the stats reduction (stats only).
+
+    The events are created without the system-scope fence a default HIP event
+    performs when it is recorded (hipEventDisableSystemFence): that fence
+    writes back and invalidates the caches after every kernel, which adds
+    several microseconds to each timed launch and to the next one's start."""
 
     def __init__(self, n: int, device=None):
         dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
-        stream = torch.cuda.current_stream(dev)
-        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
-        for e in self.events:  # torch creates the HIP event at its first record
-            e.record(stream)
-        self._handles = (ctypes.c_void_p * (2 * n))(*[e.cuda_event for e in self.events])
+        self.device = dev
+        hip = _hip_runtime()
+        with torch.cuda.device(dev):
+            evs = []
+            for _ in range(2 * n):
+                e = ctypes.c_void_p()
+                rc = hip.hipEventCreateWithFlags(ctypes.byref(e), _HIP_EVENT_DISABLE_SYSTEM_FENCE)
+                if rc != 0:
+                    for x in evs:
+                        hip.hipEventDestroy(x)
+                    raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+                evs.append(e.value)
+        self._handles = (ctypes.c_void_p * (2 * n))(*evs)
         self.n = n
         self.count = 0
 
@@ -401,6 +460,19 @@ class LaunchTimer:
         return False
 
     def durations_us(self):
-        torch.cuda.synchronize()
-        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) * 1e3
-                for i in range(self.count)]
+        torch.cuda.synchronize(self.device)
+        hip = _hip_runtime()
+        out, ms = [], ctypes.c_float()
+        for i in range(self.count):
+            rc = hip.hipEventElapsedTime(ctypes.byref(ms), self._handles[2 * i], self._handles[2 * i + 1])
+            if rc != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+            out.append(ms.value * 1e3)
+        return out
+
+    def __del__(self):
+        hip = _HIP
+        if hip is not None and getattr(self, "_handles", None) is not None:
+            for h in self._handles:
+                if h:
+                    hip.hipEventDestroy(h)

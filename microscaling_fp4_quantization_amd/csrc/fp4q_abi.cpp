@@ -74,11 +74,12 @@ fp4q_status launched(int rc, const char* msg) {
         if (st_ != FP4Q_OK) return st_;    \
     } while (0)
 
-fp4q_status quantize_common(const char* fn, const void* x, int32_t xt, int64_t rows, int64_t cols,
-                            int32_t block, int32_t fmt, int32_t gmode, float* g, int32_t rotate,
-                            uint8_t* codes, uint8_t* scales, float* block_mse, int32_t mse_kind,
-                            fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream,
-                            int32_t radius = -1, bool scratch = false) {
+// Validates one quantize call's arguments and fills its job.
+fp4q_status quant_job(const char* fn, const void* x, int32_t xt, int64_t rows, int64_t cols,
+                      int32_t block, int32_t fmt, int32_t gmode, float* g, int32_t rotate,
+                      uint8_t* codes, uint8_t* scales, float* block_mse, int32_t mse_kind,
+                      fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream, int32_t radius,
+                      bool scratch, fp4q::QuantJob& j) {
     TRY(check_dtype(fn, xt));
     TRY(check_shape(fn, rows, cols, block, rotate));
     TRY(check_mse(fn, block_mse, mse_kind));
@@ -105,7 +106,7 @@ fp4q_status quantize_common(const char* fn, const void* x, int32_t xt, int64_t r
             return fail(FP4Q_ERR_HIP, "%s: %s", fn, msg);
     }
     TRY(check_ws(fn, need_ws, ws, ws_bytes));
-    fp4q::QuantJob j{};
+    j = fp4q::QuantJob{};
     j.x = x;
     j.xt = xt;
     j.n = n;
@@ -124,6 +125,17 @@ fp4q_status quantize_common(const char* fn, const void* x, int32_t xt, int64_t r
     j.ws = ws;
     j.stream = stream;
     j.radius = radius;
+    return FP4Q_OK;
+}
+
+fp4q_status quantize_common(const char* fn, const void* x, int32_t xt, int64_t rows, int64_t cols,
+                            int32_t block, int32_t fmt, int32_t gmode, float* g, int32_t rotate,
+                            uint8_t* codes, uint8_t* scales, float* block_mse, int32_t mse_kind,
+                            fp4q_stats* stats, void* ws, size_t ws_bytes, void* stream,
+                            int32_t radius = -1, bool scratch = false) {
+    fp4q::QuantJob j;
+    TRY(quant_job(fn, x, xt, rows, cols, block, fmt, gmode, g, rotate, codes, scales, block_mse,
+                  mse_kind, stats, ws, ws_bytes, stream, radius, scratch, j));
     char msg[256] = {0};
     return launched(fp4q::launch_quantize(j, msg, sizeof msg), msg);
 }
@@ -167,6 +179,21 @@ fp4q_status nvfp4_quantize_noalloc(const void* x, int32_t xt, int64_t rows, int6
     return quantize_common("nvfp4_quantize_noalloc", x, xt, rows, cols, block, scale_fmt, gmode, g,
                            rotate, codes, scales, block_mse, mse_kind, stats, nullptr, 0, stream, -1,
                            true);
+}
+
+fp4q_status fp4_quantize_mx_nv(const void* x, int32_t xt, int64_t rows, int64_t cols,
+                               uint8_t* mx_codes, uint8_t* mx_scales, float* mx_block_mse,
+                               fp4q_stats* mx_stats, int32_t nv_block, float* g, uint8_t* nv_codes,
+                               uint8_t* nv_scales, float* nv_block_mse, fp4q_stats* nv_stats,
+                               int32_t mse_kind, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "fp4_quantize_mx_nv";
+    fp4q::QuantJob mx, nv;
+    TRY(quant_job(fn, x, xt, rows, cols, 32, FP4Q_FMT_MXFP4, FP4Q_G_NONE, nullptr, 0, mx_codes,
+                  mx_scales, mx_block_mse, mse_kind, mx_stats, ws, ws_bytes, stream, -1, false, mx));
+    TRY(quant_job(fn, x, xt, rows, cols, nv_block, FP4Q_FMT_UE4M3, FP4Q_G_DYNAMIC, g, 0, nv_codes,
+                  nv_scales, nv_block_mse, mse_kind, nv_stats, ws, ws_bytes, stream, -1, false, nv));
+    char msg[256] = {0};
+    return launched(fp4q::launch_quantize_mx_nv(mx, nv, msg, sizeof msg), msg);
 }
 
 fp4q_status fp4_quantize_search(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t fmt,

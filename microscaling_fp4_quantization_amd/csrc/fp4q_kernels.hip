@@ -83,7 +83,7 @@ constexpr int kAmaxUnroll = FP4Q_AUNROLL;   // ... of the amax pre-pass
 // Quantize and amax grids: at least this many chunks per wave, and at most
 // kGridRounds rounds of resident workgroups.
 #ifndef FP4Q_MIN_CHUNKS_PER_WAVE
-#define FP4Q_MIN_CHUNKS_PER_WAVE 8
+#define FP4Q_MIN_CHUNKS_PER_WAVE 4
 #endif
 #ifndef FP4Q_GRID_ROUNDS
 #define FP4Q_GRID_ROUNDS 1
@@ -110,6 +110,14 @@ constexpr int kMinChunksPerWave = FP4Q_MIN_CHUNKS_PER_WAVE;
 #ifndef FP4Q_ACPW
 #define FP4Q_ACPW 8
 #endif
+// Smaller tensors give the amax pass fewer chunks per wave, so that it runs as
+// one round of loads on more CUs (below this many chunks).
+#ifndef FP4Q_ACPW_SMALL
+#define FP4Q_ACPW_SMALL 4
+#endif
+#ifndef FP4Q_ACPW_SMALL_BELOW
+#define FP4Q_ACPW_SMALL_BELOW 32768
+#endif
 #ifndef FP4Q_SCPW
 #define FP4Q_SCPW 0
 #endif
@@ -117,6 +125,8 @@ constexpr int kMinChunksPerWave = FP4Q_MIN_CHUNKS_PER_WAVE;
 #define FP4Q_SCPW_LIGHT 4
 #endif
 constexpr int kQuantCpw = FP4Q_QCPW, kQuantCpwLight = FP4Q_QCPW_LIGHT, kAmaxCpw = FP4Q_ACPW;
+constexpr int kAmaxCpwSmall = FP4Q_ACPW_SMALL;
+constexpr int64_t kAmaxSmallBelow = FP4Q_ACPW_SMALL_BELOW;
 constexpr int kStreamCpw = FP4Q_SCPW, kStreamCpwLight = FP4Q_SCPW_LIGHT;
 // The amax pre-pass has no per-workgroup set-up, so it runs larger workgroups
 // of short-lived waves: fewer per-workgroup maxima for the quantize kernel to
@@ -548,6 +558,7 @@ struct Acc {
     double nonmax = 0.0, max = 0.0, zero = 0.0, sumsq = 0.0;
     uint32_t nzero = 0;  // per lane: at most one per chunk the wave processes
     uint32_t fixup = 0;  // wave-uniform: a block's separate non-max sum was deferred
+    uint32_t amax = 0;   // max |x| (binary32 bits) over the chunks quantized (k_quantize AMAX)
 };
 
 // How a chunk's blocks whose non-max term needs the separate sum
@@ -627,10 +638,15 @@ __device__ __forceinline__ void add_block(Acc& acc, bool zero, double sse, doubl
 // flight that cost more than the separate kernel.)
 struct StatsOut {
     double* partials;
-    void* stats;               // fp4q_stats
+    void* stats;               // fp4q_stats, or NULL (k_finalize then only forms g)
     long long n_blocks;
     const double* sumsq_part;  // sum x^2 of the amax pre-pass, or NULL
     int G_sumsq;
+    // k_finalize of an MXFP4 pass that feeds an NVFP4 pass (fp4_quantize_mx_nv):
+    // the per-tensor scale from the quantize kernel's per-workgroup maxima.
+    const uint32_t* amax_part;
+    int n_amax;
+    float* g_out;              // NULL: no scale to form
 };
 
 // Fixed-order sum of G partials into the fp4q_stats struct, by one workgroup:
@@ -723,8 +739,6 @@ __device__ void write_partial(const Acc& a, const StatsOut& so) {
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_finalize(StatsOut so, int G) { sum_partials(so, G); }
-
 // ------------------------------------------------------------ quantize
 struct QParams {
     const void* x;
@@ -743,6 +757,7 @@ struct QParams {
     const uint32_t* amax_part;
     int n_amax;
     float* g_out;
+    uint32_t* amax_out;  // k_quantize AMAX: per-workgroup max |x| bits (slot blockIdx.x)
     StatsOut so;
 };
 
@@ -836,16 +851,31 @@ __device__ __forceinline__ double nonmax_reread(Rsrc xin, int xoff, int lane, in
     return group_sum<L>(s);
 }
 
+// What a block's MSE and tensor terms need from its chunk (PAIR mode of
+// quantize_chunk): the block's SSE and sum of squares, its maximum |x| and that
+// maximum's dequantized value.  An absent chunk is all zeros, which stores
+// nothing (its offsets fall outside the group's output window) and adds 0.
+struct BlockRes {
+    double sse = 0.0, ss = 0.0;
+    float m = 0.0f, xh_m = 0.0f;
+};
+
 // One 512-element chunk: lane `lane` holds elements 8 lane .. 8 lane + 7 of it
 // and block lane / L of it (gl = lane % L).  Every lane of a block ends with the
 // block's results; the block's first lane stores its scale and MSE, and every
 // lane adds the block's terms to acc (the caller keeps only the first lanes').
 // The chunk's input starts xoff bytes into the window xin (read again only for
 // the separate non-max sum in kSepInline).  SEP: see kSepInline.
-template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ, int SEP = kSepInline>
+// PAIR (blocks of L >= 2 lanes, two-chunk groups): the chunk stores its codes
+// and scale bytes and hands its blocks' sums to `res`, and finish_pair then
+// forms the MSE and tensor terms of both chunks at once; in kSepFixup only
+// lane gl = u adds (the lane finish_pair gives chunk u's block).
+template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ, int SEP = kSepInline,
+          bool PAIR = false>
 __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const QOut& o,
                                                const QParams& p, const UeCtx& ue, int lane,
-                                               int gl, Acc& acc, Rsrc xin, int xoff) {
+                                               int gl, Acc& acc, Rsrc xin, int xoff,
+                                               BlockRes* res = nullptr) {
     constexpr int L = B / kLaneElems;
     constexpr int kBlocks = kChunk / B;
     constexpr int kSt = quant_store_policy<FMT>();
@@ -871,6 +901,7 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
     }
     const uint32_t mbits = group_max<L>(lane_max);
     const float m = __uint_as_float(mbits);
+    if constexpr (SEP != kSepFixup) acc.amax = max(acc.amax, mbits);  // read only by k_quantize AMAX
 
     uint32_t cw, sbyte;
     float xh[8];
@@ -929,6 +960,10 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
         }
         sse = group_sum<L>(sse);
         if constexpr (SUMSQ) ss = group_sum<L>(ss);
+        if constexpr (PAIR && SEP != kSepFixup) {
+            *res = BlockRes{sse, ss, m, xh_m};
+            return;
+        }
         if (SEP != kSepFixup && p.block_mse) {
             float mse;
             // Relative MSE always comes with the sum of squares (SUMSQ).
@@ -959,12 +994,52 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
             } else {
                 if (__builtin_amdgcn_ballot_w64(sep)) {
                     const double s2 = nonmax_sum<L>(v, xh, m, gl);
-                    if (sep) acc.nonmax += s2;
+                    if (sep && (!PAIR || gl == u)) acc.nonmax += s2;
                 }
                 return;
             }
             add_block(acc, zero, sse, mterm, nm, ss);
         }
+    }
+}
+
+// The block MSE and tensor terms of two chunks' blocks (PAIR mode), one block
+// per lane: lane gl = 0 of each block position takes the first chunk's block
+// and lane gl = 1 the second's.  The lanes gl >= 2 of wider blocks compute
+// copies whose stores are dropped and whose terms the caller discards.  This
+// runs the per-block arithmetic once per two chunks instead of once per chunk
+// on every lane of every block.  Non-max sums that need the separate sum are
+// deferred (kSepDefer).
+template <int FMT, int B, bool SUMSQ>
+__device__ __forceinline__ void finish_pair(const BlockRes (&r)[2], const QOut& o, const QParams& p,
+                                            int lane, int gl, Acc& acc) {
+    constexpr int L = B / kLaneElems;
+    constexpr int kBlocks = kChunk / B;
+    constexpr int kSt = quant_store_policy<FMT>();
+    static_assert(L >= 2, "one block per lane needs no pairing");
+    const bool second = (gl & 1) != 0;
+    const double sse = second ? r[1].sse : r[0].sse;
+    const float m = second ? r[1].m : r[0].m;
+    const float xh_m = second ? r[1].xh_m : r[0].xh_m;
+    double ss = 0.0;
+    if constexpr (SUMSQ) ss = second ? r[1].ss : r[0].ss;
+    if (p.block_mse) {
+        float mse;
+        if (SUMSQ && p.mse_kind == kMseRel) mse = rel_mse(sse, ss);
+        else mse = (float)(sse * (1.0 / B));
+        const int blk = (second ? kBlocks : 0) + lane / L;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mse), o.mse, gl < 2 ? blk * 4 : kDropped,
+                                              0, kSt);
+    }
+    if (p.so.stats) {
+        const double em = (double)(m - xh_m);
+        const double mterm = em * em;
+        const bool zero = (m > 0.0f) && (xh_m == 0.0f);
+        double nm = sse - mterm;
+        const bool sep = needs_separate_sum(zero, sse, nm);
+        if (sep) nm = 0.0;
+        if (__builtin_amdgcn_ballot_w64(sep)) acc.fixup = 1u;
+        add_block(acc, zero, sse, mterm, nm, ss);
     }
 }
 
@@ -1117,15 +1192,23 @@ __device__ float dynamic_g(const uint32_t* part, int n_part) {
     return g > 0.0f ? g : 1.0f;
 }
 
+// Sums a stats kernel's G partials (when so.stats is set) and, for an MXFP4
+// pass that feeds an NVFP4 pass, forms the per-tensor scale from its maxima.
+__global__ __launch_bounds__(kThreads) void k_finalize(StatsOut so, int G) {
+    if (so.g_out) {
+        const float g = dynamic_g(so.amax_part, so.n_amax);
+        if (threadIdx.x == 0) *so.g_out = g;
+    }
+    if (so.stats) sum_partials(so, G);
+}
+
 #ifndef FP4Q_QUANT_WPE
 #define FP4Q_QUANT_WPE 0
 #endif
-template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ, bool SEARCH = false>
-__global__ __launch_bounds__(kThreads)
-#if FP4Q_QUANT_WPE
-__attribute__((amdgpu_waves_per_eu(FP4Q_QUANT_WPE)))
-#endif
-FP4Q_SGPR_CAP void k_quantize(QParams p) {
+// The quantize kernel's body.  AMAX: also write the workgroup's max |x|
+// (binary32 bits) to p.amax_out.
+template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ, bool SEARCH, bool AMAX>
+__device__ __forceinline__ void quantize_body(const QParams& p) {
     constexpr int L = B / kLaneElems;
     const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
@@ -1153,6 +1236,8 @@ FP4Q_SGPR_CAP void k_quantize(QParams p) {
     }
     Acc acc;
     constexpr int E = XT == 0 ? 2 : 4;
+    // Blocks of two or more lanes finish a group's two chunks together.
+    constexpr bool kPair = ERR && !SEARCH && L >= 2 && kQuantUnroll == 2;
     for (int64_t i = 0, c = wr.c0; i < wr.n; ++i, c += wr.step) {
         const QOut o = group_outputs<B, kQuantUnroll>(p, c, wr.c1);
         const Rsrc xin = group_input<XT, kQuantUnroll>(p.x, p.n, c, wr.c1);
@@ -1161,15 +1246,26 @@ FP4Q_SGPR_CAP void k_quantize(QParams p) {
         Raw<XT> nxt[kQuantUnroll];
         if (i + 1 < wr.n) load_group<XT, kQuantUnroll>(nxt, p.x, p.n, c + wr.step, wr.c1, lane);
 #endif
+        if constexpr (kPair) {
+            BlockRes r[2];
+            quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer, true>(
+                cur[0], 0, o, p, ue, lane, gl, acc, xin, 0, &r[0]);
+            if (left > 1)
+                quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer, true>(
+                    cur[1], 1, o, p, ue, lane, gl, acc, xin, kChunk * E, &r[1]);
+            if (p.block_mse || p.so.stats) finish_pair<FMT, B, SUMSQ>(r, o, p, lane, gl, acc);
+        } else {
 #pragma unroll
-        for (int u = 0; u < kQuantUnroll; ++u)
-            if (u < left) {
-                if constexpr (SEARCH)
-                    search_chunk<XT, FMT, B, ROT, SUMSQ, kSepDefer>(cur[u], u, o, p, ue, lane, gl, acc);
-                else
-                    quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer>(
-                        cur[u], u, o, p, ue, lane, gl, acc, xin, u * kChunk * E);
-            }
+            for (int u = 0; u < kQuantUnroll; ++u)
+                if (u < left) {
+                    if constexpr (SEARCH)
+                        search_chunk<XT, FMT, B, ROT, SUMSQ, kSepDefer>(cur[u], u, o, p, ue, lane, gl,
+                                                                        acc);
+                    else
+                        quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer>(
+                            cur[u], u, o, p, ue, lane, gl, acc, xin, u * kChunk * E);
+                }
+        }
 #if FP4Q_PREFETCH
 #pragma unroll
         for (int u = 0; u < kQuantUnroll; ++u) cur[u] = nxt[u];
@@ -1194,16 +1290,48 @@ FP4Q_SGPR_CAP void k_quantize(QParams p) {
                             search_chunk<XT, FMT, B, ROT, SUMSQ, kSepFixup>(raw[u], u, o, p, ue, lane,
                                                                             gl, acc);
                         else
-                            quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepFixup>(
+                            quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepFixup, kPair>(
                                 raw[u], u, o, p, ue, lane, gl, acc, xin, u * kChunk * E);
                     }
             }
         }
     }
+    if constexpr (AMAX) {
+        __shared__ uint32_t s_amax[kWaves];
+        const uint32_t wm = wave_max(acc.amax);
+        if (lane == 0) s_amax[threadIdx.x / kWave] = wm;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t mm = s_amax[0];
+            for (int w = 1; w < kWaves; ++w) mm = max(mm, s_amax[w]);
+            p.amax_out[blockIdx.x] = mm;
+        }
+    }
     if (p.so.stats) {
-        if (gl != 0) acc = Acc{};  // every lane of a block holds its terms: keep one copy
+        // Every lane of a block holds its terms: keep one copy (with pairing,
+        // lanes 0 and 1 of each block position hold the two chunks' blocks).
+        if (kPair ? gl >= 2 : gl != 0) acc = Acc{};
         write_partial(acc, p.so);
     }
+}
+
+template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ, bool SEARCH = false>
+__global__ __launch_bounds__(kThreads)
+#if FP4Q_QUANT_WPE
+__attribute__((amdgpu_waves_per_eu(FP4Q_QUANT_WPE)))
+#endif
+FP4Q_SGPR_CAP void k_quantize(QParams p) {
+    quantize_body<XT, FMT, B, ROT, ERR, SUMSQ, SEARCH, false>(p);
+}
+
+// The MXFP4 pass of fp4_quantize_mx_nv (no rotation): k_quantize plus the
+// per-workgroup maxima.  Held to 8 waves per SIMD (64 VGPRs), the occupancy
+// of the plain MXFP4 kernel, whose grid it takes (so its tensor terms are
+// summed in the same order and match the plain call's bit for bit).
+template <int XT, bool ERR, bool SUMSQ>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
+FP4Q_SGPR_CAP void k_quantize_amax(QParams p) {
+    quantize_body<XT, kFmtMx, 32, 0, ERR, SUMSQ, false, true>(p);
 }
 
 
@@ -1897,7 +2025,13 @@ int launch_finalize(const StatsOut& so, int G, hipStream_t st, char* msg, size_t
 typedef void (*QuantKernel)(QParams);
 
 template <int XT, int FMT, int B, int ROT>
-QuantKernel pick_quant(bool err, bool sumsq, bool search) {
+QuantKernel pick_quant(bool err, bool sumsq, bool search, bool amax = false) {
+    if constexpr (FMT == kFmtMx && ROT == 0) {
+        if (amax) {
+            if (!err) return k_quantize_amax<XT, false, false>;
+            return sumsq ? k_quantize_amax<XT, true, true> : k_quantize_amax<XT, true, false>;
+        }
+    }
     if (search) return sumsq ? k_quantize<XT, FMT, B, ROT, true, true, true>
                              : k_quantize<XT, FMT, B, ROT, true, false, true>;
     if (!err) return k_quantize<XT, FMT, B, ROT, false, false>;
@@ -1906,10 +2040,11 @@ QuantKernel pick_quant(bool err, bool sumsq, bool search) {
 }
 
 template <int XT, int FMT>
-QuantKernel pick_quant_block(int block, int rotate, bool err, bool sumsq, bool search) {
+QuantKernel pick_quant_block(int block, int rotate, bool err, bool sumsq, bool search,
+                             bool amax = false) {
     if constexpr (FMT == kFmtMx) {
         return rotate ? pick_quant<XT, FMT, 32, 32>(err, sumsq, search)
-                      : pick_quant<XT, FMT, 32, 0>(err, sumsq, search);
+                      : pick_quant<XT, FMT, 32, 0>(err, sumsq, search, amax);
     } else {
         switch (block) {
             case 8: return pick_quant<XT, FMT, 8, 0>(err, sumsq, search);
@@ -2132,9 +2267,10 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     p.radius = search ? j.radius : 0;
     p.max_byte = j.fmt == kFmtMx ? 254 : (j.fmt == kFmtUe4m3 ? 0x7E : 0xF7);
     QuantKernel k;
+    const bool amax = j.amax_out != nullptr;  // MXFP4 pass of fp4_quantize_mx_nv (rotate 0)
     if (j.fmt == kFmtMx)
-        k = j.xt == 0 ? pick_quant_block<0, kFmtMx>(32, j.rotate, err, sumsq, search)
-                      : pick_quant_block<1, kFmtMx>(32, j.rotate, err, sumsq, search);
+        k = j.xt == 0 ? pick_quant_block<0, kFmtMx>(32, j.rotate, err, sumsq, search, amax)
+                      : pick_quant_block<1, kFmtMx>(32, j.rotate, err, sumsq, search, amax);
     else
         k = j.fmt == kFmtUe4m3
                 ? (j.xt == 0 ? pick_quant_block<0, kFmtUe4m3>(j.block, j.rotate, err, sumsq, search)
@@ -2142,14 +2278,21 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
                 : (j.xt == 0 ? pick_quant_block<0, kFmtUe5m3>(j.block, j.rotate, err, sumsq, search)
                              : pick_quant_block<1, kFmtUe5m3>(j.block, j.rotate, err, sumsq, search));
     const bool light = j.stats == nullptr && !dynamic && j.fmt != kFmtMx;
-    const Split sq = split_for(chunks, reinterpret_cast<const void*>(k), light ? kQuantCpwLight : kQuantCpw);
+    // The amax-writing MXFP4 kernel takes the plain kernel's grid (same occupancy).
+    const QuantKernel k_grid =
+        !amax ? k
+              : (j.xt == 0 ? pick_quant_block<0, kFmtMx>(32, j.rotate, err, sumsq, search)
+                           : pick_quant_block<1, kFmtMx>(32, j.rotate, err, sumsq, search));
+    const Split sq = split_for(chunks, reinterpret_cast<const void*>(k_grid),
+                               light ? kQuantCpwLight : kQuantCpw);
     const int G = sq.G;
     p.cpw = sq.cpw;
     int G_amax = 0;
     if (j.fmt != kFmtMx && j.gmode != 0) {
         if (dynamic) {
             const AmaxKernel ka = pick_amax(j.xt, j.rotate, sumsq_in_amax);
-            const Split sa = split_for(chunks, reinterpret_cast<const void*>(ka), kAmaxCpw, kAmaxWaves);
+            const Split sa = split_for(chunks, reinterpret_cast<const void*>(ka),
+                                       chunks < kAmaxSmallBelow ? kAmaxCpwSmall : kAmaxCpw, kAmaxWaves);
             AParams a{j.x, j.n, chunks, sa.cpw, reinterpret_cast<uint32_t*>(ws + kWsAmax),
                       sumsq_in_amax ? reinterpret_cast<double*>(ws + kWsAmaxSumsq) : nullptr};
             p.so.sumsq_part = a.sumsq;
@@ -2165,10 +2308,36 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
             p.g_in = j.g;
         }
     }
+    if (amax) {
+        p.amax_out = j.amax_out;
+        p.so.amax_part = j.amax_out;
+        p.so.n_amax = G;
+        p.so.g_out = j.g_from_amax;
+    }
     FP4Q_LAUNCH(k, dim3(G), dim3(kThreads), 0, st, p);
     int rc = report(hipGetLastError(), "quantize kernel launch", msg, msg_len);
-    if (rc || !j.stats) return rc;
+    if (rc || !(j.stats || amax)) return rc;
     return launch_finalize(p.so, G, st, msg, msg_len);
+}
+
+int launch_quantize_mx_nv(const QuantJob& mx, const QuantJob& nv, char* msg, size_t msg_len) {
+    if (mx.n == 0) {  // empty: zero stats and g = 1, as the separate calls give
+        const int rc = launch_quantize(mx, msg, msg_len);
+        return rc ? rc : launch_quantize(nv, msg, msg_len);
+    }
+    // The MXFP4 pass leaves its per-workgroup maxima in the amax slots of the
+    // workspace and its reduction writes g; the NVFP4 pass then reads g as a
+    // given scale.  Both reductions run before the next pass in stream order,
+    // so the two passes can share the workspace's partial slots.
+    QuantJob a = mx;
+    a.ws = nv.ws;
+    a.amax_out = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(nv.ws) + kWsAmax);
+    a.g_from_amax = nv.g;
+    int rc = launch_quantize(a, msg, msg_len);
+    if (rc) return rc;
+    QuantJob b = nv;
+    b.gmode = 2;
+    return launch_quantize(b, msg, msg_len);
 }
 
 int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len) {

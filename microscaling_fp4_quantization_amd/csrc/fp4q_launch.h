@@ -37,6 +37,11 @@ struct QuantJob {
     void* ws;
     void* stream;
     int radius = -1;   // >= 0: per-block scale search over this many neighbours
+    // MXFP4 pass of fp4_quantize_mx_nv: the quantize kernel also writes its
+    // per-workgroup max |x| (binary32 bits) to amax_out, and the reduction
+    // kernel turns them into the NVFP4 per-tensor scale at g_from_amax.
+    uint32_t* amax_out = nullptr;
+    float* g_from_amax = nullptr;
 };
 
 struct DequantJob {
@@ -131,6 +136,9 @@ int scratch_workspace(void** ptr, size_t* bytes, char* msg, size_t msg_len);
 
 // Each returns 0 on success, else a HIP error code; `msg` gets a description.
 int launch_quantize(const QuantJob& j, char* msg, size_t msg_len);
+// MXFP4 (mx) then dynamic NVFP4 (nv) of the same unrotated tensor, the NVFP4
+// per-tensor scale taken from the MXFP4 pass's maxima (no amax pass).
+int launch_quantize_mx_nv(const QuantJob& mx, const QuantJob& nv, char* msg, size_t msg_len);
 int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len);
 int launch_block_mse(const MseJob& j, char* msg, size_t msg_len);
 int launch_rotate(const RotateJob& j, char* msg, size_t msg_len);

@@ -257,3 +257,22 @@ def test_noalloc_validation(L):
     assert nva(gmode=2) == ARG and "g pointer" in err(L)
     assert nva(kind=3) == ARG
     assert nva(stats=A16 + 4) == ALIGN
+
+
+def test_mx_nv_validation(L):
+    """fp4_quantize_mx_nv checks both passes' arguments before launching anything."""
+    def pair(x=A16, xt=0, rows=4, cols=64, mxc=A16b, mxs=A16c, block=16, g=A16, nvc=A16b,
+             nvs=A16c, kind=0, mst=None, nst=None, ws=A16, wsb=WSB):
+        return L.fp4_quantize_mx_nv(x, xt, rows, cols, mxc, mxs, None, mst, block, g, nvc, nvs,
+                                    None, nst, kind, ws, wsb, None)
+    assert pair(xt=5) == ARG
+    assert pair(cols=48) == SHAPE                       # not a multiple of 32 (MXFP4)
+    assert pair(block=12) == SHAPE
+    assert pair(cols=96, block=64) == SHAPE             # 96 % 64
+    assert pair(g=None) == ARG and "g pointer" in err(L)  # the dynamic scale needs g
+    assert pair(ws=None) == WS                          # always needs a workspace
+    assert pair(wsb=16) == WS
+    assert pair(kind=2) == ARG
+    assert pair(nvc=None) == ARG
+    assert pair(mxc=A16b + 8) == ALIGN
+    assert pair(mst=A16 + 4) == ALIGN

@@ -1,0 +1,112 @@
+"""fp4_quantize_mx_nv (MXFP4 and dynamic NVFP4 of one tensor in one call, the
+NVFP4 per-tensor scale taken from the MXFP4 pass) against the two separate
+calls, bit for bit, and against the oracle.
+
+"Diagnosing FP4 inference", technical summary section 2: every layer's
+tensors quantized in both formats.  The separate calls are themselves held to
+the oracle elsewhere; here every output of the combined call must equal theirs
+exactly (codes, scale bytes, per-block MSE, g and the tensor terms), except the
+NVFP4 sum-of-squares term under the absolute MSE, which the combined call sums
+in its quantize kernel instead of the amax pass (same value to rounding: the
+oracle's bar applies)."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_workloads as wl
+import oracle
+import microscaling_fp4_quantization_amd as fq
+from parity_util import compare_quant, to_oracle_input
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def seeded(shape, seed, dtype=torch.bfloat16, sigma=0.02):
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma)
+    return torch.from_numpy(a).to(dtype).to(DEV)
+
+
+def same(a: torch.Tensor, b: torch.Tensor):
+    assert a.shape == b.shape and a.dtype == b.dtype
+    assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def check_against_separate(x, nv_block, kind, block_mse=True, stats=True):
+    m, v = fq.fp4_quantize_mx_nv(x, nv_block, mse_kind=kind, block_mse=block_mse, stats=stats)
+    a = fq.mxfp4_quantize(x, mse_kind=kind, block_mse=block_mse, stats=stats)
+    b = fq.nvfp4_quantize(x, nv_block, fq.FMT_UE4M3, fq.G_DYNAMIC, None, 0, mse_kind=kind,
+                          block_mse=block_mse, stats=stats)
+    torch.cuda.synchronize()
+    same(m.codes, a.codes)
+    same(m.scales, a.scales)
+    same(v.codes, b.codes)
+    same(v.scales, b.scales)
+    same(v.g, b.g)
+    if block_mse:
+        same(m.block_mse, a.block_mse)
+        same(v.block_mse, b.block_mse)
+    if stats:
+        same(m.stats, a.stats)
+        if kind == fq.MSE_REL:
+            same(v.stats, b.stats)
+        else:
+            sv, sb = fq.stats_dict(v.stats), fq.stats_dict(b.stats)
+            for k in ("sse_nonmax", "sse_max", "sse_zero", "n_blocks", "n_zero_blocks"):
+                assert sv[k] == sb[k], k
+            assert abs(sv["sum_x2"] - sb["sum_x2"]) <= 1e-12 * sb["sum_x2"]
+    return m, v
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("kind", [fq.MSE_ABS, fq.MSE_REL])
+@pytest.mark.parametrize("nv_block", [16, 32, 8])
+def test_matches_separate_calls_and_oracle(dtype, kind, nv_block):
+    x = seeded((67, 1536), [115, nv_block, kind], dtype)
+    print(f"  mx_nv dtype={dtype} kind={kind} nv_block={nv_block}", flush=True)
+    m, v = check_against_separate(x, nv_block, kind)
+    xf = to_oracle_input(x)
+    compare_quant(m, oracle.quantize(xf, oracle.FMT_MXFP4, 32, mse_kind=kind), xin=xf)
+    compare_quant(v, oracle.quantize(xf, oracle.FMT_UE4M3, nv_block, oracle.GMODE_DYNAMIC,
+                                     mse_kind=kind), xin=xf)
+
+
+@pytest.mark.parametrize("block_mse,stats", [(False, False), (True, False), (False, True)])
+def test_partial_outputs(block_mse, stats):
+    x = seeded((300, 2048), 116)
+    check_against_separate(x, 16, fq.MSE_REL, block_mse, stats)
+
+
+def test_empty_tensor():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    m, v = fq.fp4_quantize_mx_nv(x)
+    torch.cuda.synchronize()
+    assert v.g.item() == 1.0
+    for q in (m, v):
+        st = fq.stats_dict(q.stats)
+        assert st["n_blocks"] == 0 and st["sse_nonmax"] == 0.0 and st["sum_x2"] == 0.0
+
+
+def test_all_zero_tensor_gives_unit_scale():
+    x = torch.zeros((64, 512), dtype=torch.bfloat16, device=DEV)
+    m, v = check_against_separate(x, 16, fq.MSE_REL)
+    assert v.g.item() == 1.0
+
+
+@pytest.mark.parametrize("proj", range(len(wl.QWEN14_PROJ)))
+def test_qwen14_layer0_full_size(proj):
+    """Every projection of layer 0 of the 14B-shaped stack, as the benchmark
+    runs it (relative MSE, tensor terms), against the separate calls."""
+    x = wl.qwen14_layer_tensor(0, proj).to(DEV)
+    print(f"  mx_nv layer 0 {wl.QWEN14_PROJ[proj][0]}", flush=True)
+    check_against_separate(x, 16, fq.MSE_REL)
+
+
+def test_two_calls_in_a_row_reuse_the_workspace():
+    """A large call then a small one on the same workspace: nothing of the
+    first (maxima, partials) leaks into the second."""
+    big = seeded((4096, 4096), 117, sigma=0.5)
+    small = seeded((33, 512), 118)
+    fq.fp4_quantize_mx_nv(big, mse_kind=fq.MSE_REL)
+    check_against_separate(small, 16, fq.MSE_REL)
