@@ -237,13 +237,19 @@ def write_counters(workload, out_md, bench_line, dirs):
                 continue
             a = acc.setdefault(key, {})
             a.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-            a.setdefault("_vgpr", set()).add(int(r["VGPR_Count"]) + int(r["Accum_VGPR_Count"]))
-            a.setdefault("_sgpr", set()).add(int(r["SGPR_Count"]))
     rel = lambda d: os.path.relpath(os.path.abspath(d), ROOT)
     lines = [f"# Instruction and busy counters per launch: bench.py workload `{workload}`", "",
              "Counter runs (from the repository root on the MI355X box), one counter set per run, "
              "csv output under the directories named:", "", "```"]
-    lines += [f"rocprofv3 --pmc <set> --output-format csv -d {rel(d)} -o run -- {plan['run']}" for d in dirs]
+    sets = []
+    for d in dirs:
+        names = []
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if r["Counter_Name"] not in names:
+                names.append(r["Counter_Name"])
+        sets.append(" ".join(names))
+    lines += [f"rocprofv3 --pmc {c} --output-format csv -d {rel(d)} -o run -- {plan['run']}"
+              for c, d in zip(sets, dirs)]
     lines += ["```", "", f"then `python bench.py --workload {workload} --write-counters {out_md} "
               f"{rel(bench_line)} {' '.join(rel(d) for d in dirs)}`.  Launch times come from the untraced "
               f"bench line ({rel(bench_line)}: per-format mean over the step's launches).", "",
@@ -261,8 +267,8 @@ def write_counters(workload, out_md, bench_line, dirs):
         mean = {c: sum(v) / len(v) for c, v in a.items() if not c.startswith("_")}
         n_disp = max(len(v) for c, v in a.items() if not c.startswith("_"))
         lines += [f"## `{key}...>`: {label}", "",
-                  f"{n_disp} dispatches per counter; VGPRs {sorted(a['_vgpr'])}, SGPRs {sorted(a['_sgpr'])}; "
-                  f"launch time {us} us (untraced).", "", "| counter | mean per launch | per chunk |",
+                  f"{n_disp} dispatches per counter; launch time {us} us (untraced, mean over the "
+                  "format's launches in the bench line).", "", "| counter | mean per launch | per chunk |",
                   "|---|---|---|"]
         for c in sorted(mean):
             per = f"{mean[c] / chunks:.2f}" if c.startswith("SQ_INSTS") else ""
@@ -280,12 +286,14 @@ def _short_kernel(name):
     return name.split("(")[0] if "<" in name.split("(")[0] else name
 
 
-def write_trace(workload, out_md, bench_line, trace_dir, command):
+def write_trace(workload, out_md, bench_line, trace_dir, command, untraced_line=None):
     """Summarise a `rocprofv3 --kernel-trace --stats` run of bench.py (csv
     output, -o bench) into OUT_MD: every kernel's statistics, and the launches
     of the roofline leg (the step replayed on one stream after the warm-up
     and timed steps and one warm replay) set against the leg's own HIP-event
-    timing in the bench line the same run printed."""
+    timing in the bench line the same run printed, and, when given, in an
+    untraced run of the same command (the tracer adds work around every
+    dispatch, which the traced run's event pairs include)."""
     import csv
     line = json.loads(open(bench_line).read().strip().splitlines()[-1])
     r = line["roofline"]
@@ -301,10 +309,12 @@ def write_trace(workload, out_md, bench_line, trace_dir, command):
         raise SystemExit(f"trace holds {len(quant)} quantize launches; the leg needs {start + per_step_q}")
     dur = lambda t: (int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) / 1e3
     rel = lambda d: os.path.relpath(os.path.abspath(d), ROOT)
+    un = json.loads(open(untraced_line).read().strip().splitlines()[-1]) if untraced_line else None
     lines = [f"# Kernel trace: bench.py workload `{workload}`", "",
              "Command (from the repository root on the MI355X box), then "
              f"`python bench.py --workload {workload} --write-trace {out_md} {rel(bench_line)} "
-             f"{rel(trace_dir)} \"<command>\"` to write this file:", "", "```", command, "```", "",
+             f"{rel(trace_dir)} \"<command>\"" + (f" {rel(untraced_line)}" if un else "") +
+             "` to write this file:", "", "```", command, "```", "",
              "| kernel | calls | total us | avg us | min us | max us |", "|---|---|---|---|---|---|"]
     for s in stats:
         lines.append(f"| `{_short_kernel(s['Name'])[:100]}` | {s['Calls']} | "
@@ -315,18 +325,31 @@ def write_trace(workload, out_md, bench_line, trace_dir, command):
               f"The roofline leg is quantize launches {start} to {start + per_step_q - 1} in launch "
               f"order ({line['warmup']} warm-up and {line['steps']} timed steps, then one warm replay "
               "come before it): one step's calls replayed on one stream.", "",
-              "| roofline leg, per format | launches | trace avg us | bench events avg us | difference |",
-              "|---|---|---|---|---|"]
+              "| roofline leg, per format | launches | trace avg us | events, traced run | difference |"
+              + (" events, untraced run | difference |" if un else ""),
+              "|---|---|---|---|---|" + ("---|---|" if un else "")]
+
+    def row(tag, n, tr, ev, ev_un):
+        cells = f"| {tag} | {n} | {tr:.3f} | {ev:.3f} | {100 * (ev - tr) / tr:+.2f} % |"
+        if ev_un is not None:
+            cells += f" {ev_un:.3f} | {100 * (ev_un - tr) / tr:+.2f} % |"
+        return cells
     for si, tag in enumerate(specs):
         sel = [dur(t) for i, t in enumerate(leg) if i % len(specs) == si]
-        tr = sum(sel) / len(sel)
-        ev = r["per_spec"][tag]["us_per_launch"]
-        lines.append(f"| {tag} | {len(sel)} | {tr:.3f} | {ev:.3f} | {100 * (ev - tr) / tr:+.2f} % |")
-    tr_all = sum(dur(t) for t in leg) / len(leg)
-    lines.append(f"| all | {len(leg)} | {tr_all:.3f} | {r['us_per_launch']:.3f} | "
-                 f"{100 * (r['us_per_launch'] - tr_all) / tr_all:+.2f} % |")
-    lines += ["", f"Bench line of this run (under the tracer): value {line['value']} GB/s, "
-              f"{line['ms_per_step']} ms per step, roofline frac {r['frac']}.", ""]
+        lines.append(row(tag, len(sel), sum(sel) / len(sel), r["per_spec"][tag]["us_per_launch"],
+                         un["roofline"]["per_spec"][tag]["us_per_launch"] if un else None))
+    lines.append(row("all", len(leg), sum(dur(t) for t in leg) / len(leg), r["us_per_launch"],
+                     un["roofline"]["us_per_launch"] if un else None))
+    lines += ["", f"Bench line of the traced run: value {line['value']} GB/s, "
+              f"{line['ms_per_step']} ms per step, roofline frac {r['frac']}."]
+    if un:
+        lines += ["", f"Untraced bench.py run (the same workload and GPU legs; it also ran the CPU baseline leg) in the same session on the same box: value {un['value']} GB/s, "
+                  f"{un['ms_per_step']} ms per step, roofline frac {un['roofline']['frac']}.  Under "
+                  "the tracer every dispatch carries the tracer's own completion work, which the "
+                  "traced run's event pairs (recorded around each launch) include and the kernels' "
+                  "own start and end timestamps do not; the untraced run's events measure the "
+                  "launches without it."]
+    lines.append("")
     open(out_md, "w").write("\n".join(lines))
     print("\n".join(lines))
 
@@ -1002,11 +1025,13 @@ def main():
     ap.add_argument("--write-counters", nargs="+", metavar="ARG",
                     help="OUT_MD BENCH_LINE DIR...: summarise rocprofv3 instruction/busy counter "
                          "runs of the workload into OUT_MD, then exit (no GPU needed)")
-    ap.add_argument("--write-trace", nargs=4, metavar=("OUT_MD", "BENCH_LINE", "TRACE_DIR", "COMMAND"),
-                    help="summarise a rocprofv3 --kernel-trace --stats run of bench.py into OUT_MD, "
-                         "then exit (no GPU needed)")
+    ap.add_argument("--write-trace", nargs="+", metavar="ARG",
+                    help="OUT_MD BENCH_LINE TRACE_DIR COMMAND [UNTRACED_LINE]: summarise a rocprofv3 "
+                         "--kernel-trace --stats run of bench.py into OUT_MD, then exit (no GPU needed)")
     args = ap.parse_args()
     if args.write_trace:
+        if len(args.write_trace) not in (4, 5):
+            ap.error("--write-trace needs OUT_MD BENCH_LINE TRACE_DIR COMMAND [UNTRACED_LINE]")
         write_trace(args.workload, *args.write_trace)
         return
     if args.write_traffic:

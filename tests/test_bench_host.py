@@ -46,3 +46,61 @@ def test_traffic_record_scales_counters_by_the_calibration_copy(tmp_path, monkey
     json.dump(rec, open(out, "w"))
     assert bench.read_traffic("gemm") is None
 
+
+
+def test_trace_summary_takes_the_roofline_leg(tmp_path):
+    """write_trace picks the leg's quantize launches (after warm-up, timed steps
+    and one warm replay) and sets their kernel durations beside the events."""
+    n_q = 4  # quantize launches per step: 2 tensors x (MXFP4, NVFP4)
+    line = {"warmup": 1, "steps": 2, "value": 1.0, "ms_per_step": 1.0, "config": {"streams": 2},
+            "roofline": {"launches": n_q, "frac": 0.5, "us_per_launch": 11.0,
+                         "per_spec": {"mx32": {"us_per_launch": 10.5}, "nv16_dyn": {"us_per_launch": 11.5}}}}
+    bl = tmp_path / "line.json"
+    bl.write_text(json.dumps(line) + "\n")
+    d = tmp_path / "kt"
+    d.mkdir()
+    with open(d / "bench_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs"])
+        w.writerow(["void k_quantize<0, 1, 16>(QParams)", 10, 1000, 100.0, 50, 150])
+    rows, t = [], 0
+    names = ["void fp4q::k_quantize_amax<0, true, true>(QParams)", "void fp4q::k_quantize<0, 1, 16>(QParams)"]
+    for i in range(5 * n_q):  # warm-up, 2 timed steps, the warm replay, then the leg
+        dur = (10000 if i % 2 == 0 else 11000) if 4 * n_q <= i < 5 * n_q else 99000
+        rows.append([i + 1, names[i % 2], t, t + dur])
+        rows.append([1000 + i, "k_finalize(StatsOut, int)", t, t + 1])
+        t += dur + 10
+    with open(d / "bench_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writerows(rows)
+    out = tmp_path / "t.md"
+    bench.write_trace("qwen14model", str(out), str(bl), str(d), "cmd")
+    text = out.read_text()
+    assert "| mx32 | 2 | 10.000 | 10.500 | +5.00 % |" in text
+    assert "| nv16_dyn | 2 | 11.000 | 11.500 | +4.55 % |" in text
+
+
+def test_counter_summary_per_chunk(tmp_path):
+    """write_counters divides instruction counts by the layer's mean chunks per
+    launch and names the counter sets it was given."""
+    import fp4_workloads as wl
+    chunks = sum(r * c for _, (r, c) in wl.QWEN14_PROJ) / len(wl.QWEN14_PROJ) / 512
+    line = {"roofline": {"per_spec": {"mx32": {"us_per_launch": 20.0}, "nv16_dyn": {"us_per_launch": 25.0}}}}
+    bl = tmp_path / "line.json"
+    bl.write_text(json.dumps(line) + "\n")
+    d = tmp_path / "pa"
+    d.mkdir()
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writerow([1, "void k_quantize_amax<0, true, true>(QParams)", "SQ_INSTS_VALU", 100 * chunks])
+        w.writerow([2, "void k_quantize_amax<0, true, true>(QParams)", "SQ_INSTS_VALU", 140 * chunks])
+        w.writerow([3, "void k_quantize<0, 1, 16, 0, true, true, false>(QParams)", "SQ_INSTS_VALU",
+                    150 * chunks])
+    out = tmp_path / "c.md"
+    bench.write_counters("qwen14model", str(out), str(bl), [str(d)])
+    text = out.read_text()
+    assert "--pmc SQ_INSTS_VALU " in text
+    assert f"| SQ_INSTS_VALU | {120 * chunks:,.2f} | 120.00 |" in text
+    assert f"| SQ_INSTS_VALU | {150 * chunks:,.2f} | 150.00 |" in text
