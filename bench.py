@@ -997,19 +997,10 @@ def copy_ceiling(torch, xs):
     per = ms / len(src)
     nbytes = src[0].numel() * src[0].element_size()
     gbs = 2 * nbytes / (per * 1e-3) / 1e9
-    # Read-only: torch's max reduction of the same tensors (reads each once).
-    for x in src:
-        torch.amax(x)
-    ms_r = time_region(torch, stream, lambda: [torch.amax(x) for x in src], reps)
-    per_r = ms_r / len(src)
-    gbs_r = nbytes / (per_r * 1e-3) / 1e9
     return {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "us_per_copy": round(per * 1e3, 2),
             "what": f"device copy of a {'x'.join(map(str, shape))} {str(src[0].dtype)[6:]} tensor "
-                    f"(read + write), {len(src)} distinct tensors cycled",
-            "read_only": {"GBps": round(gbs_r, 1), "frac_of_peak": round(gbs_r / HBM_PEAK_GBS, 4),
-                          "us_per_read": round(per_r * 1e3, 2),
-                          "what": "torch.amax of the same tensors (each read once)"}}
+                    f"(read + write), {len(src)} distinct tensors cycled"}
 
 
 def main():
