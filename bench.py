@@ -4,13 +4,15 @@ Default workload (one step = the whole path over one batch): a random-init
 Qwen2.5-14B-shaped stack, 48 layers x {q 5120x5120, k and v 1024x5120, o
 5120x5120, gate and up 13824x5120, down 5120x13824}, bf16 N(0, 0.02) seeded
 per tensor (13.2e9 parameters, 26.4 GB resident in HBM before timing).  Every
-tensor is quantized twice per step, in one fp4_quantize_mx_nv call: MXFP4
-(block 32, E8M0) and NVFP4 (block 16, UE4M3 under the dynamic FP32 per-tensor
-scale, whose tensor maximum the MXFP4 pass takes on the way), each with packed
-codes, scale bytes, the relative per-block MSE and the three-term error split
-(--separate issues the two calls instead, NVFP4 with its own amax pass).  The
-step spreads its calls over two HIP streams (one workspace each; --streams 1
-runs them back to back).
+tensor is quantized twice per step: MXFP4 (block 32, E8M0) and NVFP4 (block
+16, UE4M3 under the dynamic FP32 per-tensor scale, whose tensor maximum the
+MXFP4 pass takes on the way), each with packed codes, scale bytes, the relative
+per-block MSE and the three-term error split.  Each layer's seven tensors go
+in one fp4_quantize_mx_nv_batch call (one launch per format for the layer;
+--no-batch issues one fp4_quantize_mx_nv call per tensor, --separate the two
+single-format calls, NVFP4 with its own amax pass).  The step spreads its
+calls over two HIP streams (one workspace each; --streams 1 runs them back to
+back).
 
 Prints one JSON line:
   value         GB/s of input quantized+packed+MSE'd over the whole step (every
@@ -103,13 +105,13 @@ def _traffic_plan(workload):
     if workload == "qwen14model":
         import fp4_workloads as wl
         ns = [r * c for _, (r, c) in wl.QWEN14_PROJ]
-        # mean algorithmic bytes of one layer's 14 quantize launches (MXFP4 b32
-        # and NVFP4 b16 of each projection, relative per-block MSE)
-        alg = sum(n * (2 + 0.5 + 1 / 32 + 4 / 32) + n * (2 + 0.5 + 1 / 16 + 4 / 16) for n in ns) / (2 * len(ns))
+        # mean algorithmic bytes of one layer's two batched quantize launches
+        # (MXFP4 b32 and NVFP4 b16 of all seven projections, relative MSE)
+        alg = sum(n * (2 + 0.5 + 1 / 32 + 4 / 32) + n * (2 + 0.5 + 1 / 16 + 4 / 16) for n in ns) / 2
         return {"parts": [("k_quantize", None)],
-                "label": "k_quantize_amax (MXFP4 b32) and k_quantize (NVFP4 b16 under the dynamic g), "
-                         "the step's launches, with relative per-block MSE and the three-term split: "
-                         "mean per launch over one layer's 14",
+                "label": "k_quantize_mx_batch (MXFP4 b32) and k_quantize_nv_batch (NVFP4 b16 under the "
+                         "per-tensor g), the step's launches, each over one layer's seven tensors, with "
+                         "relative per-block MSE and the three-term split: mean per launch",
                 "calib_bytes": 5120 * 5120 * 2, "alg_bytes": int(alg),
                 "run": "python -u bench.py --layers 1 --steps 1 --warmup 0 --no-cpu-baseline "
                        "--calibration-copy"}
@@ -220,9 +222,15 @@ def write_counters(workload, out_md, bench_line, dirs):
     line = json.loads(open(bench_line).read().strip().splitlines()[-1])
     spec_us = {k: v["us_per_launch"] for k, v in line["roofline"]["per_spec"].items()}
     amax_us = line["roofline"].get("s0_amax_pass", {}).get("us_per_launch")
-    mean_elems = sum(r * c for _, (r, c) in wl.QWEN14_PROJ) / len(wl.QWEN14_PROJ)
+    layer_elems = sum(r * c for _, (r, c) in wl.QWEN14_PROJ)
+    mean_elems = layer_elems / len(wl.QWEN14_PROJ)
     chunks = mean_elems / 512
-    kinds = {"k_quantize_amax<0": ("MXFP4 b32 quantize (relative MSE, three-term split, tensor maximum)",
+    kinds = {"k_quantize_mx_batch<0": ("MXFP4 b32 quantize of a layer's seven tensors in one launch "
+                                       "(relative MSE, three-term split, tensor maxima)", spec_us.get("mx32")),
+             "k_quantize_nv_batch<0, 16": ("NVFP4 b16 quantize of a layer's seven tensors in one launch "
+                                           "(given per-tensor g, relative MSE, three-term split)",
+                                           spec_us.get("nv16_dyn")),
+             "k_quantize_amax<0": ("MXFP4 b32 quantize (relative MSE, three-term split, tensor maximum)",
                                    spec_us.get("mx32")),
              "k_quantize<0, 0, 32": ("MXFP4 b32 quantize (relative MSE, three-term split)", spec_us.get("mx32")),
              "k_quantize<0, 1, 16": ("NVFP4 b16 quantize (dynamic g, relative MSE, three-term split)",
@@ -253,8 +261,9 @@ def write_counters(workload, out_md, bench_line, dirs):
     lines += ["```", "", f"then `python bench.py --workload {workload} --write-counters {out_md} "
               f"{rel(bench_line)} {' '.join(rel(d) for d in dirs)}`.  Launch times come from the untraced "
               f"bench line ({rel(bench_line)}: per-format mean over the step's launches).", "",
-              f"A chunk is 512 elements; one layer's seven projections average {mean_elems / 1e6:.2f} M "
-              f"elements ({chunks:,.0f} chunks) per launch.  VALU issue share = VALU wave-instructions / "
+              f"A chunk is 512 elements; one layer's seven projections hold {layer_elems / 1e6:.2f} M "
+              f"elements ({layer_elems / 512:,.0f} chunks: a batched launch's share) and average "
+              f"{mean_elems / 1e6:.2f} M ({chunks:,.0f} chunks: a single-tensor launch's).  VALU issue share = VALU wave-instructions / "
               f"(256 CUs x launch time x {COUNTER_CLOCK_GHZ} GHz), one wave-instruction per CU per cycle; "
               "the clock under load is lower than the peak, so the true share is higher.  VALUBusy, "
               "SALUBusy and MemUnitStalled are rocprofv3's derived metrics (percent of the counter "
@@ -264,6 +273,7 @@ def write_counters(workload, out_md, bench_line, dirs):
         if key not in acc:
             continue
         a = acc[key]
+        per_launch_chunks = layer_elems / 512 if "_batch<" in key else chunks
         mean = {c: sum(v) / len(v) for c, v in a.items() if not c.startswith("_")}
         n_disp = max(len(v) for c, v in a.items() if not c.startswith("_"))
         lines += [f"## `{key}...>`: {label}", "",
@@ -271,7 +281,7 @@ def write_counters(workload, out_md, bench_line, dirs):
                   "format's launches in the bench line).", "", "| counter | mean per launch | per chunk |",
                   "|---|---|---|"]
         for c in sorted(mean):
-            per = f"{mean[c] / chunks:.2f}" if c.startswith("SQ_INSTS") else ""
+            per = f"{mean[c] / per_launch_chunks:.2f}" if c.startswith("SQ_INSTS") else ""
             lines.append(f"| {c} | {mean[c]:,.2f} | {per} |")
         if "SQ_INSTS_VALU" in mean and us:
             share = mean["SQ_INSTS_VALU"] / (256 * us * 1e-6 * COUNTER_CLOCK_GHZ * 1e9)
@@ -302,7 +312,8 @@ def write_trace(workload, out_md, bench_line, trace_dir, command, untraced_line=
     stats = list(csv.DictReader(open(os.path.join(trace_dir, "bench_kernel_stats.csv"))))
     trace = sorted(csv.DictReader(open(os.path.join(trace_dir, "bench_kernel_trace.csv"))),
                    key=lambda t: int(t["Dispatch_Id"]))
-    quant = [t for t in trace if "k_quantize<" in t["Kernel_Name"] or "k_quantize_amax<" in t["Kernel_Name"]]
+    import re
+    quant = [t for t in trace if re.search(r"k_quantize(_amax|_mx_batch|_nv_batch)?<", t["Kernel_Name"])]
     start = (line["warmup"] + line["steps"] + 1) * per_step_q
     leg = quant[start:start + per_step_q]
     if len(leg) != per_step_q:
@@ -425,10 +436,14 @@ class Workload:
     bounded CPU sample.  `per_call` asks for a time per (tensor, spec) pair in
     the breakdown (latency-bound workloads)."""
 
-    def __init__(self, name, config, make_tensors, specs, steps, warmup, sample, per_call=False):
+    def __init__(self, name, config, make_tensors, specs, steps, warmup, sample, per_call=False,
+                 batch=0):
         self.name, self.config, self.make_tensors = name, config, make_tensors
         self.specs, self.steps, self.warmup, self.sample = specs, steps, warmup, sample
         self.per_call = per_call
+        # batch > 0: a "pair" spec is issued as fp4_quantize_mx_nv_batch calls over
+        # consecutive groups of `batch` tensors (one layer of the stack).
+        self.batch = batch
 
 
 def _qwen7_tensors():
@@ -533,7 +548,7 @@ WORKLOADS = {
          "outputs": "codes + scales + relative per-block MSE + per-tensor split"},
         _qwen14model_tensors,
         [Spec("mx32+nv16_dyn", "pair", 16, mse_kind=1)],
-        20, 3, ("layer 0's seven projections (q, k, v, o, gate, up, down), whole", 7, [0])),
+        20, 3, ("layer 0's seven projections (q, k, v, o, gate, up, down), whole", 7, [0]), batch=7),
 }
 
 
@@ -700,8 +715,13 @@ class Runner:
     tensor's memory-bound amax pass runs beside another's quantize pass.  The
     streams join the caller's stream at the start and end of every step."""
 
-    def __init__(self, fq, torch, dev, xs, specs, n_streams=1):
+    def __init__(self, fq, torch, dev, xs, specs, n_streams=1, batch=0):
         self.fq, self.torch, self.dev, self.xs, self.specs = fq, torch, dev, xs, specs
+        # With batch > 0 (a single "pair" spec), a call covers `batch` consecutive
+        # tensors; calls alternate over the streams.
+        self.batch = batch if (batch and len(specs) == 1 and specs[0].parts) else 0
+        self.groups = ([list(range(i, min(i + self.batch, len(xs)))) for i in range(0, len(xs), self.batch)]
+                       if self.batch else None)
         self.streams = [torch.cuda.current_stream(dev)] + [torch.cuda.Stream(dev)
                                                            for _ in range(n_streams - 1)]
         ws_bytes = fq.workspace_bytes()
@@ -714,8 +734,8 @@ class Runner:
         # replay can reuse the step's g.
         shared = {}
         k = 0
-        def outputs(r, c, block, stream):
-            key = (r, c, block, stream)
+        def outputs(r, c, block, stream, slot=0):
+            key = (r, c, block, stream, slot)
             if key not in shared:
                 shared[key] = dict(
                     codes=torch.empty((r, c // 2), dtype=torch.uint8, device=dev),
@@ -729,9 +749,12 @@ class Runner:
             r, c = x.shape
             for si, s in enumerate(specs):
                 stream = k % n_streams
+                slot = 0
+                if self.batch:  # distinct outputs within a call, one stream per call
+                    stream, slot = (ti // self.batch) % n_streams, ti % self.batch
                 k += 1
                 if s.parts:
-                    o = {p.tag: outputs(r, c, p.block, stream) for p in s.parts}
+                    o = {p.tag: outputs(r, c, p.block, stream, slot) for p in s.parts}
                 else:
                     o = outputs(r, c, s.block, stream)
                 o["g"] = torch.ones(r if s.gmode == 3 else 1, dtype=torch.float32, device=dev)
@@ -767,10 +790,38 @@ class Runner:
                               scales=o["scales"], block_mse=bm, mse_kind=s.mse_kind, stats=st,
                               ws=ws)
 
+    def call_batch(self, gi, ws=None):
+        """One fp4_quantize_mx_nv_batch call over tensor group gi."""
+        fq, s = self.fq, self.specs[0]
+        ws = self.ws if ws is None else ws
+        outs = []
+        for ti in self.groups[gi]:
+            o = self.out[(ti, 0)]
+            mx, nv = ({"codes": o[p.tag]["codes"], "scales": o[p.tag]["scales"],
+                       "block_mse": o[p.tag]["block_mse"] if s.block_mse else False,
+                       "stats": o[p.tag]["stats"] if s.stats else False} for p in s.parts)
+            outs.append((mx, nv, o["g"]))
+        fq.fp4_quantize_mx_nv_batch([self.xs[ti] for ti in self.groups[gi]], s.block,
+                                    mse_kind=s.mse_kind, outs=outs, ws=ws)
+
     def step(self, given=False, one_stream=False):
         """All calls of one step; with one_stream (or given, which also passes the
         dynamic per-tensor scale as given) they run back to back on the caller's
         stream."""
+        if self.batch:
+            one = one_stream or len(self.streams) == 1
+            main = self.streams[0]
+            if not one:
+                for st in self.streams[1:]:
+                    st.wait_stream(main)
+            for gi in range(len(self.groups)):
+                k = 0 if one else self.out[(self.groups[gi][0], 0)]["stream"]
+                with self.torch.cuda.stream(self.streams[k]):
+                    self.call_batch(gi, self.wss[k])
+            if not one:
+                for st in self.streams[1:]:
+                    main.wait_stream(st)
+            return
         if given or one_stream or len(self.streams) == 1:
             for ti in range(len(self.xs)):
                 for si in range(len(self.specs)):
@@ -961,13 +1012,22 @@ def launch_times(fq, torch, run):
     {kind: [(us, algorithmic bytes, format tag, tensor shape)]} for kinds amax,
     quantize and finalize."""
     seq = []
-    for ti, x in enumerate(run.xs):
+    if run.batch:  # one launch per pass covers a group of tensors
+        s = run.specs[0]
+        for grp in run.groups:
+            n_el = sum(run.xs[ti].numel() for ti in grp)
+            in_bytes = run.xs[grp[0]].element_size()
+            label = f"batch of {len(grp)}"
+            for kind, tag in s.launches():
+                nb = s.part(tag).quantize_bytes(n_el, in_bytes) if kind == "quantize" else 0
+                seq.append((label, tag, kind, nb))
+    for ti, x in enumerate(run.xs if not run.batch else []):
         for si, s in enumerate(run.specs):
             in_bytes = x.element_size()
             for kind, tag in s.launches():
                 nb = {"amax": x.numel() * in_bytes,
                       "quantize": s.part(tag).quantize_bytes(x.numel(), in_bytes), "finalize": 0}[kind]
-                seq.append((ti, tag, kind, nb))
+                seq.append(("x".join(map(str, x.shape)), tag, kind, nb))
     run.step(given=False, one_stream=True)  # warm
     torch.cuda.synchronize()
     with fq.LaunchTimer(len(seq)) as t:
@@ -976,8 +1036,8 @@ def launch_times(fq, torch, run):
     if len(us) != len(seq):
         raise RuntimeError(f"recorded {len(us)} launches, expected {len(seq)}")
     out = {}
-    for (ti, tag, kind, nb), u in zip(seq, us):
-        out.setdefault(kind, []).append((u, nb, tag, "x".join(map(str, run.xs[ti].shape))))
+    for (label, tag, kind, nb), u in zip(seq, us):
+        out.setdefault(kind, []).append((u, nb, tag, label))
     return out
 
 
@@ -1015,6 +1075,9 @@ def main():
     ap.add_argument("--separate", action="store_true",
                     help="issue a combined MXFP4 + NVFP4 call as its two separate calls "
                          "(NVFP4 with its own amax pass)")
+    ap.add_argument("--no-batch", action="store_true",
+                    help="issue the combined call tensor by tensor instead of one batched call "
+                         "per layer")
     ap.add_argument("--streams", type=int, default=2,
                     help="HIP streams the step's independent calls are spread over")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -1075,7 +1138,7 @@ def main():
         xs.append(x.to(dev))
         del x
     in_bytes = xs[0].element_size()
-    run = Runner(fq, torch, dev, xs, w.specs, max(1, args.streams))
+    run = Runner(fq, torch, dev, xs, w.specs, max(1, args.streams), 0 if args.no_batch else w.batch)
     n_elem_calls = sum(x.numel() for x in xs) * sum(s.formats for s in w.specs)
     alg_bytes = sum(s.algorithmic_bytes(x.numel(), in_bytes) for x in xs for s in w.specs)
 

@@ -186,6 +186,46 @@ fp4q_status fp4_quantize_mx_nv(const void* x, int32_t xt, int64_t rows, int64_t 
                                uint8_t* nv_scales, float* nv_block_mse, fp4q_stats* nv_stats,
                                int32_t mse_kind, void* ws, size_t ws_bytes, void* stream);
 
+/* One tensor of a batched fp4_quantize_mx_nv call: its device input and the
+ * outputs of both passes, laid out as for fp4_quantize_mx_nv. */
+typedef struct {
+    const void* x;             /* device, rows x cols, 16-byte aligned */
+    int64_t rows, cols;
+    uint8_t* mx_codes;         /* MXFP4 pass, as for mxfp4_quantize */
+    uint8_t* mx_scales;
+    float* mx_block_mse;
+    fp4q_stats* mx_stats;
+    float* g;                  /* device out: the NVFP4 per-tensor scale */
+    uint8_t* nv_codes;         /* NVFP4 pass, as for nvfp4_quantize */
+    uint8_t* nv_scales;
+    float* nv_block_mse;
+    fp4q_stats* nv_stats;
+} fp4q_mx_nv_tensor;
+
+#define FP4Q_MAX_BATCH 16
+
+/*
+ * fp4_quantize_mx_nv for up to FP4Q_MAX_BATCH tensors (say, one layer's
+ * projections) in one launch per pass: the grid is split between the tensors,
+ * each tensor's workgroups sweeping only its own elements, so small tensors
+ * share a launch instead of paying one each.
+ *   tensors    host array of n_tensors descriptors (1 <= n_tensors <= 16);
+ *              shapes may differ
+ *   xt         dtype of every tensor's x
+ *   nv_block   16 or 32
+ *   mse_kind   kind of every per-block MSE output
+ *   ws         fp4q_workspace_bytes() bytes, always needed
+ * Each format's block_mse must be given for every tensor or for none, and
+ * likewise its stats.  Every code byte, scale byte, per-block MSE and g equals
+ * the single-tensor call's; the tensor terms equal it to rounding (a tensor's
+ * partial sums follow its share of the grid).  Errors as for
+ * fp4_quantize_mx_nv, with the failing tensor's index in the message;
+ * nothing is launched unless every tensor's arguments are valid.
+ */
+fp4q_status fp4_quantize_mx_nv_batch(const fp4q_mx_nv_tensor* tensors, int32_t n_tensors,
+                                     int32_t xt, int32_t nv_block, int32_t mse_kind, void* ws,
+                                     size_t ws_bytes, void* stream);
+
 /*
  * Quantization with a per-block scale search ("Bridging the Gap...", Sommario
  * tecnico section 3 item 2: scales chosen to minimise the reconstruction MSE

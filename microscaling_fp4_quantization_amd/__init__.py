@@ -34,7 +34,7 @@ MSE_ABS, MSE_REL = 0, 1
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_WORKSPACE", 5: "ERR_HIP"}
 
 EXPORTS = ("mxfp4_quantize", "nvfp4_quantize", "nvfp4_quantize_noalloc", "fp4_quantize_mx_nv",
-           "fp4_quantize_search",
+           "fp4_quantize_mx_nv_batch", "fp4_quantize_search",
            "fp4_dequantize",
            "fp4_block_mse", "hadamard_block_rotate", "fp4_gemm_mxfp4", "fp4_gemm_workspace_bytes",
            "fp4_gemm_nvfp4", "fp4_gemm_nvfp4_workspace_bytes",
@@ -71,6 +71,8 @@ def _bind(l):
     l.nvfp4_quantize_noalloc.restype = c.c_int
     l.fp4_quantize_mx_nv.argtypes = [P, i32, i64, i64, P, P, P, P, i32, P, P, P, P, P, i32, P, sz, P]
     l.fp4_quantize_mx_nv.restype = c.c_int
+    l.fp4_quantize_mx_nv_batch.argtypes = [P, i32, i32, i32, i32, P, sz, P]
+    l.fp4_quantize_mx_nv_batch.restype = c.c_int
     l.fp4_dequantize.argtypes = [P, P, i32, i32, P, i64, i64, i32, P, i32, P]
     l.fp4_quantize_search.argtypes = [P, i32, i64, i64, i32, i32, i32, P, i32, i32, P, P, P, i32,
                                       P, P, sz, P]
@@ -269,6 +271,49 @@ def fp4_quantize_mx_nv(x: torch.Tensor, nv_block: int = 16, *, mse_kind: int = M
                                     _ptr(v[0]), _ptr(v[1]), _ptr(v[2]), _ptr(v[3]), mse_kind,
                                     _ptr(ws), ws.numel(), _stream(x.device)))
     return Quantized(*m, None), Quantized(*v, g)
+
+
+class MxNvTensor(ctypes.Structure):
+    """fp4q_mx_nv_tensor: one tensor of a batched fp4_quantize_mx_nv call."""
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("mx_codes", ctypes.c_void_p), ("mx_scales", ctypes.c_void_p),
+                ("mx_block_mse", ctypes.c_void_p), ("mx_stats", ctypes.c_void_p),
+                ("g", ctypes.c_void_p), ("nv_codes", ctypes.c_void_p), ("nv_scales", ctypes.c_void_p),
+                ("nv_block_mse", ctypes.c_void_p), ("nv_stats", ctypes.c_void_p)]
+
+
+MAX_BATCH = 16
+
+
+def fp4_quantize_mx_nv_batch(xs, nv_block: int = 16, *, mse_kind: int = MSE_ABS, block_mse=True,
+                             stats=True, outs=None, ws: Optional[torch.Tensor] = None):
+    """fp4_quantize_mx_nv for up to MAX_BATCH tensors (same dtype, same device) in
+    one launch per pass.  ``outs``: optional list of (mx dict, nv dict, g) of
+    preallocated outputs per tensor.  Returns a list of (Quantized MXFP4,
+    Quantized NVFP4 with g) per tensor."""
+    xs = [_matrix(x) for x in xs]
+    if not xs:
+        raise ValueError("xs is empty")
+    if any(x.dtype != xs[0].dtype or x.device != xs[0].device for x in xs):
+        raise ValueError("every tensor of a batch must have the same dtype and device")
+    res = []
+    arr = (MxNvTensor * len(xs))()
+    for i, x in enumerate(xs):
+        mx, nv, g = outs[i] if outs is not None else ({}, {}, None)
+        m = _outputs(x, 32, mx.get("codes"), mx.get("scales"), mx.get("block_mse", block_mse),
+                     mx.get("stats", stats))
+        v = _outputs(x, nv_block, nv.get("codes"), nv.get("scales"), nv.get("block_mse", block_mse),
+                     nv.get("stats", stats))
+        if g is None:
+            g = torch.empty(1, dtype=torch.float32, device=x.device)
+        ptr = lambda t: None if t is None else t.data_ptr()
+        arr[i] = MxNvTensor(ptr(x), x.shape[0], x.shape[1], ptr(m[0]), ptr(m[1]), ptr(m[2]), ptr(m[3]),
+                            ptr(g), ptr(v[0]), ptr(v[1]), ptr(v[2]), ptr(v[3]))
+        res.append((Quantized(*m, None), Quantized(*v, g)))
+    ws = ws if ws is not None else workspace(xs[0].device)
+    _check(lib().fp4_quantize_mx_nv_batch(arr, len(xs), _dtype_code(xs[0]), nv_block, mse_kind,
+                                          _ptr(ws), ws.numel(), _stream(xs[0].device)))
+    return res
 
 
 def fp4_quantize_search(x: torch.Tensor, fmt: int = FMT_UE4M3, block: int = 16,

@@ -196,6 +196,44 @@ fp4q_status fp4_quantize_mx_nv(const void* x, int32_t xt, int64_t rows, int64_t 
     return launched(fp4q::launch_quantize_mx_nv(mx, nv, msg, sizeof msg), msg);
 }
 
+fp4q_status fp4_quantize_mx_nv_batch(const fp4q_mx_nv_tensor* tensors, int32_t n_tensors,
+                                     int32_t xt, int32_t nv_block, int32_t mse_kind, void* ws,
+                                     size_t ws_bytes, void* stream) {
+    static_assert(FP4Q_MAX_BATCH == fp4q::kMaxBatchTensors, "batch limit");
+    const char* fn = "fp4_quantize_mx_nv_batch";
+    if (n_tensors < 1 || n_tensors > FP4Q_MAX_BATCH)
+        return fail(FP4Q_ERR_ARG, "%s: n_tensors %d is not in 1..%d", fn, n_tensors, FP4Q_MAX_BATCH);
+    if (!tensors) return fail(FP4Q_ERR_ARG, "%s: tensors is NULL", fn);
+    if (nv_block != 16 && nv_block != 32)
+        return fail(FP4Q_ERR_SHAPE, "%s: nv_block %d is not 16 or 32", fn, nv_block);
+    fp4q::QuantJob mx[FP4Q_MAX_BATCH], nv[FP4Q_MAX_BATCH];
+    char where[96];
+    // Outputs wanted: as the first non-empty tensor gives them (an empty
+    // tensor's zero-size outputs may be NULL).
+    int ref = 0;
+    while (ref + 1 < n_tensors && tensors[ref].rows * tensors[ref].cols == 0) ++ref;
+    for (int i = 0; i < n_tensors; ++i) {
+        const fp4q_mx_nv_tensor& t = tensors[i];
+        snprintf(where, sizeof where, "%s tensor %d", fn, i);
+        TRY(quant_job(where, t.x, xt, t.rows, t.cols, 32, FP4Q_FMT_MXFP4, FP4Q_G_NONE, nullptr, 0,
+                      t.mx_codes, t.mx_scales, t.mx_block_mse, mse_kind, t.mx_stats, ws, ws_bytes,
+                      stream, -1, false, mx[i]));
+        TRY(quant_job(where, t.x, xt, t.rows, t.cols, nv_block, FP4Q_FMT_UE4M3, FP4Q_G_DYNAMIC, t.g,
+                      0, t.nv_codes, t.nv_scales, t.nv_block_mse, mse_kind, t.nv_stats, ws, ws_bytes,
+                      stream, -1, false, nv[i]));
+        const fp4q_mx_nv_tensor& r = tensors[ref];
+        const bool empty = t.rows * t.cols == 0;
+        if ((!empty && ((t.mx_block_mse == nullptr) != (r.mx_block_mse == nullptr) ||
+                        (t.nv_block_mse == nullptr) != (r.nv_block_mse == nullptr))) ||
+            (t.mx_stats == nullptr) != (r.mx_stats == nullptr) ||
+            (t.nv_stats == nullptr) != (r.nv_stats == nullptr))
+            return fail(FP4Q_ERR_ARG, "%s: block_mse and stats must be given for every tensor or for none",
+                        where);
+    }
+    char msg[256] = {0};
+    return launched(fp4q::launch_quantize_mx_nv_batch(mx, nv, n_tensors, msg, sizeof msg), msg);
+}
+
 fp4q_status fp4_quantize_search(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t fmt,
                                 int32_t block, int32_t gmode, float* g, int32_t rotate,
                                 int32_t radius, uint8_t* codes, uint8_t* scales, float* block_mse,

@@ -294,15 +294,21 @@ struct WaveRange {
     int64_t c0, step, n, c1;
 };
 
+// The workgroups working on the tensor are wg_first .. wg_first + wg_count - 1
+// of the grid (wg_count <= 0: the whole grid; a batched launch gives each
+// tensor its own run of workgroups).
 template <int WAVES = kWaves, int U = kUnroll>
-__device__ __forceinline__ WaveRange wave_range(int64_t n_chunks, int64_t cpw) {
+__device__ __forceinline__ WaveRange wave_range(int64_t n_chunks, int64_t cpw, int wg_first = 0,
+                                                int wg_count = 0) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t W = (int64_t)gridDim.x * WAVES;
+    const int bid = (int)blockIdx.x - wg_first;
+    const int G = wg_count > 0 ? wg_count : (int)gridDim.x;
+    const int64_t W = (int64_t)G * WAVES;
     // Short-lived workgroups (cpw > 0) and the sweep (cpw < 0) keep the
     // dispatch order, so that the waves working at one time on all eight XCDs
     // cover one compact window of the tensor; the balanced split gives each
     // XCD a contiguous part.
-    const int64_t slot = cpw != 0 ? (int64_t)blockIdx.x : (int64_t)xcd_slice(blockIdx.x, gridDim.x);
+    const int64_t slot = cpw != 0 ? (int64_t)bid : (int64_t)xcd_slice(bid, G);
     const int64_t wid = slot * WAVES + wave;
     if (cpw < 0) {
         const int64_t groups = (n_chunks + U - 1) / U;
@@ -758,6 +764,8 @@ struct QParams {
     int n_amax;
     float* g_out;
     uint32_t* amax_out;  // k_quantize AMAX: per-workgroup max |x| bits (slot blockIdx.x)
+    // The tensor's workgroups within the grid (see wave_range); 0, 0 = all.
+    int wg_first, wg_count;
     StatsOut so;
 };
 
@@ -1212,7 +1220,7 @@ __device__ __forceinline__ void quantize_body(const QParams& p) {
     constexpr int L = B / kLaneElems;
     const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
-    const WaveRange wr = wave_range<kWaves, kQuantUnroll>(p.n_chunks, p.cpw);
+    const WaveRange wr = wave_range<kWaves, kQuantUnroll>(p.n_chunks, p.cpw, p.wg_first, p.wg_count);
     // The first group's loads go out before the per-workgroup set-up below, so
     // that set-up overlaps their latency.
     Raw<XT> cur[kQuantUnroll];
@@ -1223,7 +1231,7 @@ __device__ __forceinline__ void quantize_body(const QParams& p) {
         float g = 1.0f;
         if (p.amax_part) {
             g = dynamic_g(p.amax_part, p.n_amax);
-            if (blockIdx.x == 0 && threadIdx.x == 0) *p.g_out = g;
+            if ((int)blockIdx.x == p.wg_first && threadIdx.x == 0) *p.g_out = g;
         } else if (p.g_in) {
             g = *p.g_in;
         }
@@ -1332,6 +1340,90 @@ template <int XT, bool ERR, bool SUMSQ>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
 FP4Q_SGPR_CAP void k_quantize_amax(QParams p) {
     quantize_body<XT, kFmtMx, 32, 0, ERR, SUMSQ, false, true>(p);
+}
+
+// ------------------------------------------------------------ batched launches
+// Several tensors in one launch (fp4_quantize_mx_nv_batch): tensor i gets
+// workgroups wg_first .. wg_first + wg_count - 1 of the grid and sweeps its
+// own chunks with them, exactly as a launch of its own with that grid would.
+// Per-workgroup partials and maxima keep their grid-wide slots.
+constexpr int kMaxBatch = kMaxBatchTensors;
+
+struct TensorSlot {
+    const void* x;
+    int64_t n, n_chunks;
+    uint8_t* codes;
+    uint8_t* scales;
+    float* block_mse;
+    const float* g_in;  // NVFP4 pass: the tensor's per-tensor scale (device)
+    int wg_first, wg_count;
+};
+
+struct BatchParams {
+    QParams base;  // what the tensors share: format, MSE kind, outputs wanted, slots
+    int n;
+    TensorSlot t[kMaxBatch];
+};
+
+template <int XT, int FMT, int B, bool ERR, bool SUMSQ>
+__device__ __forceinline__ void batch_body(const BatchParams& bp) {
+    int t = 0;
+    while (t + 1 < bp.n && (int)blockIdx.x >= bp.t[t + 1].wg_first) ++t;
+    const TensorSlot& s = bp.t[t];
+    QParams p = bp.base;
+    p.x = s.x;
+    p.n = s.n;
+    p.n_chunks = s.n_chunks;
+    p.n_blocks = s.n / B;
+    p.codes = s.codes;
+    p.scales = s.scales;
+    p.block_mse = s.block_mse;
+    p.g_in = s.g_in;
+    p.wg_first = s.wg_first;
+    p.wg_count = s.wg_count;
+    quantize_body<XT, FMT, B, 0, ERR, SUMSQ, false, FMT == kFmtMx>(p);
+}
+
+// The MXFP4 pass of a batch (per-workgroup maxima for the NVFP4 scales).
+template <int XT, bool ERR, bool SUMSQ>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
+FP4Q_SGPR_CAP void k_quantize_mx_batch(BatchParams bp) {
+    batch_body<XT, kFmtMx, 32, ERR, SUMSQ>(bp);
+}
+
+// The NVFP4 pass of a batch (UE4M3 scales under each tensor's given g).
+template <int XT, int B, bool ERR, bool SUMSQ>
+__global__ __launch_bounds__(kThreads) FP4Q_SGPR_CAP void k_quantize_nv_batch(BatchParams bp) {
+    batch_body<XT, kFmtUe4m3, B, ERR, SUMSQ>(bp);
+}
+
+// The reductions of a batch, one workgroup per tensor: its tensor terms from
+// its workgroups' partials, and (MXFP4 pass) its per-tensor scale from their
+// maxima.
+struct BatchStats {
+    double* partials;
+    const uint32_t* amax_part;
+    struct {
+        void* stats;  // fp4q_stats or NULL
+        long long n_blocks;
+        float* g_out;  // NULL: no scale to form
+        int wg_first, wg_count;
+    } t[kMaxBatch];
+};
+
+__global__ __launch_bounds__(kThreads) void k_finalize_batch(BatchStats bs) {
+    const auto& s = bs.t[blockIdx.x];
+    if (s.g_out) {
+        const float g = dynamic_g(bs.amax_part + s.wg_first, s.wg_count);
+        if (threadIdx.x == 0) *s.g_out = g;
+    }
+    if (s.stats) {
+        StatsOut so{};
+        so.partials = bs.partials + s.wg_first;
+        so.stats = s.stats;
+        so.n_blocks = s.n_blocks;
+        sum_partials(so, s.wg_count);
+    }
 }
 
 
@@ -2318,6 +2410,134 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
     int rc = report(hipGetLastError(), "quantize kernel launch", msg, msg_len);
     if (rc || !(j.stats || amax)) return rc;
     return launch_finalize(p.so, G, st, msg, msg_len);
+}
+
+typedef void (*BatchKernel)(BatchParams);
+
+template <int XT>
+BatchKernel pick_mx_batch(bool err, bool sumsq) {
+    if (!err) return k_quantize_mx_batch<XT, false, false>;
+    return sumsq ? k_quantize_mx_batch<XT, true, true> : k_quantize_mx_batch<XT, true, false>;
+}
+
+template <int XT, int B>
+BatchKernel pick_nv_batch(bool err, bool sumsq) {
+    if (!err) return k_quantize_nv_batch<XT, B, false, false>;
+    return sumsq ? k_quantize_nv_batch<XT, B, true, true> : k_quantize_nv_batch<XT, B, true, false>;
+}
+
+// Splits one pass's grid between the tensors of a batch: each tensor gets the
+// workgroups a launch of its own would want (at least kMinChunksPerWave chunks
+// per wave), and when their sum exceeds the kernel's resident capacity, that
+// capacity in proportion to the tensors' chunks (at least one workgroup for a
+// non-empty tensor).  Returns the grid size.
+int split_batch(const int64_t* chunks, int n, const void* kernel, TensorSlot* t) {
+    const int64_t cap = (int64_t)resident_groups(kernel, kThreads) * kGridRounds;
+    int64_t want[kMaxBatch], total_want = 0, total_chunks = 0;
+    for (int i = 0; i < n; ++i) {
+        want[i] = (chunks[i] + (int64_t)kWaves * kMinChunksPerWave - 1) / ((int64_t)kWaves * kMinChunksPerWave);
+        total_want += want[i];
+        total_chunks += chunks[i];
+    }
+    int first = 0;
+    for (int i = 0; i < n; ++i) {
+        int64_t g = want[i];
+        if (total_want > cap && chunks[i] > 0) {
+            g = cap * chunks[i] / total_chunks;
+            if (g < 1) g = 1;
+            if (g > want[i]) g = want[i];
+        }
+        t[i].wg_first = first;
+        t[i].wg_count = (int)g;
+        first += (int)g;
+    }
+    return first;
+}
+
+int launch_quantize_mx_nv_batch(const QuantJob* mx, const QuantJob* nv, int n, char* msg,
+                                size_t msg_len) {
+    hipStream_t st = static_cast<hipStream_t>(nv[0].stream);
+    uint8_t* ws = static_cast<uint8_t*>(nv[0].ws);
+    const int xt = nv[0].xt, block = nv[0].block;
+    // Outputs wanted by any tensor (an empty tensor's block MSE pointer may be NULL).
+    bool mx_bm = false, nv_bm = false;
+    for (int i = 0; i < n; ++i) {
+        mx_bm = mx_bm || mx[i].block_mse != nullptr;
+        nv_bm = nv_bm || nv[i].block_mse != nullptr;
+    }
+    const bool mx_stats = mx[0].stats != nullptr, nv_stats = nv[0].stats != nullptr;
+    const bool rel = nv[0].mse_kind == kMseRel;
+    const bool mx_err = mx_bm || mx_stats, mx_sumsq = mx_stats || (mx_bm && rel);
+    const bool nv_err = nv_bm || nv_stats, nv_sumsq = nv_stats || (nv_bm && rel);
+    const BatchKernel kmx = xt == 0 ? pick_mx_batch<0>(mx_err, mx_sumsq) : pick_mx_batch<1>(mx_err, mx_sumsq);
+    const BatchKernel knv =
+        block == 16 ? (xt == 0 ? pick_nv_batch<0, 16>(nv_err, nv_sumsq) : pick_nv_batch<1, 16>(nv_err, nv_sumsq))
+                    : (xt == 0 ? pick_nv_batch<0, 32>(nv_err, nv_sumsq) : pick_nv_batch<1, 32>(nv_err, nv_sumsq));
+    int64_t chunks[kMaxBatch];
+    for (int i = 0; i < n; ++i) chunks[i] = chunks_of(mx[i].n);
+
+    // MXFP4 pass: quantize, write per-workgroup maxima and partials.
+    BatchParams bm{};
+    bm.n = n;
+    bm.base.mse_kind = mx[0].mse_kind;
+    bm.base.fmt = kFmtMx;
+    bm.base.max_byte = 254;
+    bm.base.cpw = kQuantCpw;
+    bm.base.amax_out = reinterpret_cast<uint32_t*>(ws + kWsAmax);
+    bm.base.so.partials = reinterpret_cast<double*>(ws + kWsPartials);
+    bm.base.so.stats = mx[0].stats;  // a flag here: the per-tensor sums go to each tensor's stats
+    for (int i = 0; i < n; ++i)
+        bm.t[i] = TensorSlot{mx[i].x, mx[i].n, chunks[i], mx[i].codes, mx[i].scales, mx[i].block_mse,
+                             nullptr, 0, 0};
+    const int Gm = split_batch(chunks, n, reinterpret_cast<const void*>(kmx), bm.t);
+    if (Gm > 0) {
+        FP4Q_LAUNCH(kmx, dim3(Gm), dim3(kThreads), 0, st, bm);
+        int rc = report(hipGetLastError(), "batched MXFP4 quantize launch", msg, msg_len);
+        if (rc) return rc;
+    }
+    BatchStats fm{};
+    fm.partials = bm.base.so.partials;
+    fm.amax_part = bm.base.amax_out;
+    for (int i = 0; i < n; ++i) {
+        fm.t[i].stats = mx[i].stats;
+        fm.t[i].n_blocks = mx[i].n / 32;
+        fm.t[i].g_out = nv[i].g;
+        fm.t[i].wg_first = bm.t[i].wg_first;
+        fm.t[i].wg_count = bm.t[i].wg_count;
+    }
+    FP4Q_LAUNCH(k_finalize_batch, dim3(n), dim3(kThreads), 0, st, fm);
+    int rc = report(hipGetLastError(), "batched reduction launch", msg, msg_len);
+    if (rc) return rc;
+
+    // NVFP4 pass under the scales the reduction just wrote.
+    BatchParams bn{};
+    bn.n = n;
+    bn.base.mse_kind = nv[0].mse_kind;
+    bn.base.fmt = kFmtUe4m3;
+    bn.base.max_byte = 0x7E;
+    bn.base.cpw = kQuantCpw;
+    bn.base.so.partials = reinterpret_cast<double*>(ws + kWsPartials);
+    bn.base.so.stats = nv[0].stats;
+    for (int i = 0; i < n; ++i)
+        bn.t[i] = TensorSlot{nv[i].x, nv[i].n, chunks[i], nv[i].codes, nv[i].scales, nv[i].block_mse,
+                             nv[i].g, 0, 0};
+    const int Gn = split_batch(chunks, n, reinterpret_cast<const void*>(knv), bn.t);
+    if (Gn > 0) {
+        FP4Q_LAUNCH(knv, dim3(Gn), dim3(kThreads), 0, st, bn);
+        rc = report(hipGetLastError(), "batched NVFP4 quantize launch", msg, msg_len);
+        if (rc) return rc;
+    }
+    if (!nv[0].stats) return 0;
+    BatchStats fn{};
+    fn.partials = bn.base.so.partials;
+    for (int i = 0; i < n; ++i) {
+        fn.t[i].stats = nv[i].stats;
+        fn.t[i].n_blocks = nv[i].n / block;
+        fn.t[i].wg_first = bn.t[i].wg_first;
+        fn.t[i].wg_count = bn.t[i].wg_count;
+    }
+    FP4Q_LAUNCH(k_finalize_batch, dim3(n), dim3(kThreads), 0, st, fn);
+    return report(hipGetLastError(), "batched reduction launch", msg, msg_len);
 }
 
 int launch_quantize_mx_nv(const QuantJob& mx, const QuantJob& nv, char* msg, size_t msg_len) {

@@ -139,6 +139,12 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len);
 // MXFP4 (mx) then dynamic NVFP4 (nv) of the same unrotated tensor, the NVFP4
 // per-tensor scale taken from the MXFP4 pass's maxima (no amax pass).
 int launch_quantize_mx_nv(const QuantJob& mx, const QuantJob& nv, char* msg, size_t msg_len);
+// The same for n <= kMaxBatchTensors tensors in one launch per pass: mx[i] and
+// nv[i] describe tensor i (same dtype, NVFP4 block 16 or 32, and the same
+// outputs wanted for every tensor); one reduction launch per pass.
+constexpr int kMaxBatchTensors = 16;
+int launch_quantize_mx_nv_batch(const QuantJob* mx, const QuantJob* nv, int n, char* msg,
+                                size_t msg_len);
 int launch_dequantize(const DequantJob& j, char* msg, size_t msg_len);
 int launch_block_mse(const MseJob& j, char* msg, size_t msg_len);
 int launch_rotate(const RotateJob& j, char* msg, size_t msg_len);

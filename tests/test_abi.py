@@ -276,3 +276,21 @@ def test_mx_nv_validation(L):
     assert pair(nvc=None) == ARG
     assert pair(mxc=A16b + 8) == ALIGN
     assert pair(mst=A16 + 4) == ALIGN
+
+
+def test_mx_nv_batch_validation(L):
+    """fp4_quantize_mx_nv_batch validates every tensor (naming it) before launching."""
+    def t(cols=64, bm=None, x=A16):
+        return fq.MxNvTensor(x, 4, cols, A16b, A16c, bm, None, A16, A16b, A16c, bm, None)
+
+    def batch(ts, n=None, block=16, ws=A16, kind=0):
+        arr = (fq.MxNvTensor * max(1, len(ts)))(*ts)
+        return L.fp4_quantize_mx_nv_batch(arr, len(ts) if n is None else n, 0, block, kind, ws, WSB, None)
+    assert batch([t()], n=0) == ARG
+    assert batch([t()] * 17) == ARG and "n_tensors" in err(L)
+    assert L.fp4_quantize_mx_nv_batch(None, 1, 0, 16, 0, A16, WSB, None) == ARG
+    assert batch([t()], block=8) == SHAPE
+    assert batch([t(), t(cols=48)]) == SHAPE and "tensor 1" in err(L)
+    assert batch([t(), t(bm=A16)]) == ARG and "every tensor" in err(L)
+    assert batch([t()], ws=None) == WS
+    assert batch([t(x=A16 + 8)]) == ALIGN
