@@ -34,7 +34,14 @@
 //   by element, leaving out the lowest-index element attaining m (see
 //   needs_separate_sum).
 //   Tensor terms: per-workgroup binary64 partials, summed in a fixed order by a
-//   one-workgroup finalize kernel, so results are bit-reproducible.
+//   one-workgroup finalize kernel (one workgroup per tensor for a batch), so
+//   results are bit-reproducible.
+//
+// Launch forms.  k_quantize covers one tensor with the whole grid;
+// k_quantize_amax is its MXFP4 form that also leaves per-workgroup maxima (the
+// NVFP4 per-tensor scale of fp4_quantize_mx_nv without an amax pass);
+// k_quantize_mx_batch / k_quantize_nv_batch cover up to 16 tensors in one
+// launch, each tensor on its own run of workgroups.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -871,7 +878,8 @@ struct BlockRes {
 // One 512-element chunk: lane `lane` holds elements 8 lane .. 8 lane + 7 of it
 // and block lane / L of it (gl = lane % L).  Every lane of a block ends with the
 // block's results; the block's first lane stores its scale and MSE, and every
-// lane adds the block's terms to acc (the caller keeps only the first lanes').
+// lane adds the block's terms to acc (the caller keeps one lane's copy per
+// block: gl = 0, or gl = 0 and 1 in PAIR mode).
 // The chunk's input starts xoff bytes into the window xin (read again only for
 // the separate non-max sum in kSepInline).  SEP: see kSepInline.
 // PAIR (blocks of L >= 2 lanes, two-chunk groups): the chunk stores its codes
