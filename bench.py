@@ -1078,8 +1078,10 @@ def main():
     ap.add_argument("--no-batch", action="store_true",
                     help="issue the combined call tensor by tensor instead of one batched call "
                          "per layer")
-    ap.add_argument("--streams", type=int, default=2,
-                    help="HIP streams the step's independent calls are spread over")
+    ap.add_argument("--streams", type=int, default=None,
+                    help="HIP streams the step's independent calls are spread over (default 2, "
+                         "or 1 when a step is a single call: the cross-stream joins would cost "
+                         "more than a lone call takes)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain device copy of the first tensor (a kernel of "
                          "known traffic, for scaling rocprofv3 byte counters)")
@@ -1138,7 +1140,9 @@ def main():
         xs.append(x.to(dev))
         del x
     in_bytes = xs[0].element_size()
-    run = Runner(fq, torch, dev, xs, w.specs, max(1, args.streams), 0 if args.no_batch else w.batch)
+    n_calls = len(xs) * len(w.specs)
+    streams = args.streams if args.streams is not None else (1 if n_calls == 1 else 2)
+    run = Runner(fq, torch, dev, xs, w.specs, max(1, streams), 0 if args.no_batch else w.batch)
     n_elem_calls = sum(x.numel() for x in xs) * sum(s.formats for s in w.specs)
     alg_bytes = sum(s.algorithmic_bytes(x.numel(), in_bytes) for x in xs for s in w.specs)
 
@@ -1239,7 +1243,7 @@ def main():
 
     config = {"workload": w.name, **w.config, "elements_per_step": n_elem_calls,
               "calls": "; ".join(s.describe() for s in w.specs),
-              "streams": max(1, args.streams),
+              "streams": max(1, streams),
               "arithmetic": "binary32 scales and codes, binary64 error sums"}
     if args.workload == "qwen14model":
         config["layers"] = QWEN14_LAYERS_RUN or 48
