@@ -61,3 +61,53 @@ def test_graph_replays_match_eager():
             assert torch.equal(a, b), f"replay {rep}"
         x.mul_(0.5)  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_batched_mx_nv_in_a_graph():
+    """fp4_quantize_mx_nv_batch (four launches, the per-tensor scales passed
+    from the MXFP4 reduction to the NVFP4 pass through device memory) captured
+    once and replayed on changing inputs: every replay equals the eager call."""
+    rng = np.random.default_rng(98)
+    shapes = [(64, 1024), (8, 512), (200, 2048)]
+    srcs = [[torch.from_numpy((rng.standard_normal(s) * (0.01 + 0.02 * k)).astype(np.float32))
+             .to(torch.bfloat16).to(DEV) for s in shapes] for k in range(2)]
+    xs = [t.clone() for t in srcs[0]]
+    ws = torch.zeros(fq.workspace_bytes(), dtype=torch.uint8, device=DEV)
+    outs = []
+    for (r, c) in shapes:
+        mx = dict(codes=torch.empty((r, c // 2), dtype=torch.uint8, device=DEV),
+                  scales=torch.empty((r, c // 32), dtype=torch.uint8, device=DEV),
+                  block_mse=torch.empty((r, c // 32), dtype=torch.float32, device=DEV),
+                  stats=fq.new_stats(DEV))
+        nv = dict(codes=torch.empty((r, c // 2), dtype=torch.uint8, device=DEV),
+                  scales=torch.empty((r, c // 16), dtype=torch.uint8, device=DEV),
+                  block_mse=torch.empty((r, c // 16), dtype=torch.float32, device=DEV),
+                  stats=fq.new_stats(DEV))
+        outs.append((mx, nv, torch.empty(1, dtype=torch.float32, device=DEV)))
+
+    def call():
+        fq.fp4_quantize_mx_nv_batch(xs, 16, mse_kind=fq.MSE_REL, outs=outs, ws=ws)
+
+    def flat():
+        return [t for mx, nv, g in outs for t in list(mx.values()) + list(nv.values()) + [g]]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(4):
+        for x, s in zip(xs, srcs[rep % 2]):
+            x.copy_(s)
+        call()  # eager
+        torch.cuda.synchronize()
+        want = [t.clone() for t in flat()]
+        for t in flat():
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(flat(), want):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
