@@ -7,12 +7,13 @@ per tensor (13.2e9 parameters, 26.4 GB resident in HBM before timing).  Every
 tensor is quantized twice per step: MXFP4 (block 32, E8M0) and NVFP4 (block
 16, UE4M3 under the dynamic FP32 per-tensor scale, whose tensor maximum the
 MXFP4 pass takes on the way), each with packed codes, scale bytes, the relative
-per-block MSE and the three-term error split.  Each layer's seven tensors go
-in one fp4_quantize_mx_nv_batch call (one launch per format for the layer;
---no-batch issues one fp4_quantize_mx_nv call per tensor, --separate the two
-single-format calls, NVFP4 with its own amax pass).  The step spreads its
-calls over two HIP streams (one workspace each; --streams 1 runs them back to
-back).
+per-block MSE and the three-term error split.  Every five consecutive tensors
+of the stack go in one fp4_quantize_mx_nv_batch call (one launch per format;
+--batch N for N per call, --no-batch for one fp4_quantize_mx_nv call per
+tensor, --separate for the two single-format calls, NVFP4 with its own amax
+pass).  The step spreads its calls over two HIP streams (one workspace each;
+--streams 1 runs them back to back): while one call's VALU-heavy NVFP4 pass
+runs, the other stream's MXFP4 pass overlaps it.
 
 Prints one JSON line:
   value         GB/s of input quantized+packed+MSE'd over the whole step (every
@@ -101,19 +102,28 @@ def read_traffic(workload="qwen7"):
 # What one roofline "launch" is in each workload's counter runs: the kernels
 # of one call (name fragment, grid size in work items or None for any), the
 # bytes of the calibration copy, and the call's algorithmic bytes.
+QWEN14_BATCH = 5    # tensors per batched call in the 48-layer step
+COUNTER_LAYERS = 5  # layers the counter runs of that step cover (seven calls)
+
+
 def _traffic_plan(workload):
     if workload == "qwen14model":
         import fp4_workloads as wl
-        ns = [r * c for _, (r, c) in wl.QWEN14_PROJ]
-        # mean algorithmic bytes of one layer's two batched quantize launches
-        # (MXFP4 b32 and NVFP4 b16 of all seven projections, relative MSE)
-        alg = sum(n * (2 + 0.5 + 1 / 32 + 4 / 32) + n * (2 + 0.5 + 1 / 16 + 4 / 16) for n in ns) / 2
+        # The counter runs cover the first COUNTER_LAYERS layers in the default
+        # grouping (QWEN14_BATCH consecutive tensors per call): the mean
+        # algorithmic bytes and elements of one batched quantize launch there
+        # (MXFP4 b32 and NVFP4 b16, relative per-block MSE).
+        ns = [r * c for _, (r, c) in wl.QWEN14_PROJ] * COUNTER_LAYERS
+        groups = -(-len(ns) // QWEN14_BATCH)
+        alg = sum(n * (2 + 0.5 + 1 / 32 + 4 / 32) + n * (2 + 0.5 + 1 / 16 + 4 / 16) for n in ns) / (2 * groups)
         return {"parts": [("k_quantize", None)],
-                "label": "k_quantize_mx_batch (MXFP4 b32) and k_quantize_nv_batch (NVFP4 b16 under the "
-                         "per-tensor g), the step's launches, each over one layer's seven tensors, with "
-                         "relative per-block MSE and the three-term split: mean per launch",
+                "label": f"k_quantize_mx_batch (MXFP4 b32) and k_quantize_nv_batch (NVFP4 b16 under the "
+                         f"per-tensor g), the step's launches, each over {QWEN14_BATCH} consecutive tensors "
+                         "of the stack, with relative per-block MSE and the three-term split: mean per "
+                         f"launch over the first {COUNTER_LAYERS} layers",
                 "calib_bytes": 5120 * 5120 * 2, "alg_bytes": int(alg),
-                "run": "python -u bench.py --layers 1 --steps 1 --warmup 0 --no-cpu-baseline "
+                "elems_per_batch_launch": sum(ns) / groups,
+                "run": f"python -u bench.py --layers {COUNTER_LAYERS} --steps 1 --warmup 0 --no-cpu-baseline "
                        "--calibration-copy"}
     if workload == "qwen7":
         n = 18944 * 3584
@@ -224,10 +234,11 @@ def write_counters(workload, out_md, bench_line, dirs):
     amax_us = line["roofline"].get("s0_amax_pass", {}).get("us_per_launch")
     layer_elems = sum(r * c for _, (r, c) in wl.QWEN14_PROJ)
     mean_elems = layer_elems / len(wl.QWEN14_PROJ)
+    batch_elems = plan["elems_per_batch_launch"]
     chunks = mean_elems / 512
-    kinds = {"k_quantize_mx_batch<0": ("MXFP4 b32 quantize of a layer's seven tensors in one launch "
+    kinds = {"k_quantize_mx_batch<0": ("MXFP4 b32 quantize of a batch of tensors in one launch "
                                        "(relative MSE, three-term split, tensor maxima)", spec_us.get("mx32")),
-             "k_quantize_nv_batch<0, 16": ("NVFP4 b16 quantize of a layer's seven tensors in one launch "
+             "k_quantize_nv_batch<0, 16": ("NVFP4 b16 quantize of a batch of tensors in one launch "
                                            "(given per-tensor g, relative MSE, three-term split)",
                                            spec_us.get("nv16_dyn")),
              "k_quantize_amax<0": ("MXFP4 b32 quantize (relative MSE, three-term split, tensor maximum)",
@@ -261,9 +272,9 @@ def write_counters(workload, out_md, bench_line, dirs):
     lines += ["```", "", f"then `python bench.py --workload {workload} --write-counters {out_md} "
               f"{rel(bench_line)} {' '.join(rel(d) for d in dirs)}`.  Launch times come from the untraced "
               f"bench line ({rel(bench_line)}: per-format mean over the step's launches).", "",
-              f"A chunk is 512 elements; one layer's seven projections hold {layer_elems / 1e6:.2f} M "
-              f"elements ({layer_elems / 512:,.0f} chunks: a batched launch's share) and average "
-              f"{mean_elems / 1e6:.2f} M ({chunks:,.0f} chunks: a single-tensor launch's).  VALU issue share = VALU wave-instructions / "
+              f"A chunk is 512 elements; a batched launch of the counter runs covers {batch_elems / 1e6:.2f} M "
+              f"elements on average ({batch_elems / 512:,.0f} chunks), a single-tensor launch "
+              f"{mean_elems / 1e6:.2f} M ({chunks:,.0f} chunks).  VALU issue share = VALU wave-instructions / "
               f"(256 CUs x launch time x {COUNTER_CLOCK_GHZ} GHz), one wave-instruction per CU per cycle; "
               "the clock under load is lower than the peak, so the true share is higher.  VALUBusy, "
               "SALUBusy and MemUnitStalled are rocprofv3's derived metrics (percent of the counter "
@@ -273,7 +284,7 @@ def write_counters(workload, out_md, bench_line, dirs):
         if key not in acc:
             continue
         a = acc[key]
-        per_launch_chunks = layer_elems / 512 if "_batch<" in key else chunks
+        per_launch_chunks = batch_elems / 512 if "_batch<" in key else chunks
         mean = {c: sum(v) / len(v) for c, v in a.items() if not c.startswith("_")}
         n_disp = max(len(v) for c, v in a.items() if not c.startswith("_"))
         lines += [f"## `{key}...>`: {label}", "",
@@ -548,7 +559,8 @@ WORKLOADS = {
          "outputs": "codes + scales + relative per-block MSE + per-tensor split"},
         _qwen14model_tensors,
         [Spec("mx32+nv16_dyn", "pair", 16, mse_kind=1)],
-        20, 3, ("layer 0's seven projections (q, k, v, o, gate, up, down), whole", 7, [0]), batch=7),
+        20, 3, ("layer 0's seven projections (q, k, v, o, gate, up, down), whole", 7, [0]),
+        batch=QWEN14_BATCH),
 }
 
 
@@ -1078,6 +1090,8 @@ def main():
     ap.add_argument("--no-batch", action="store_true",
                     help="issue the combined call tensor by tensor instead of one batched call "
                          "per layer")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="tensors per batched call (default: the workload's; 5 for the 48-layer stack)")
     ap.add_argument("--streams", type=int, default=None,
                     help="HIP streams the step's independent calls are spread over (default 2, "
                          "or 1 when a step is a single call: the cross-stream joins would cost "
@@ -1142,7 +1156,8 @@ def main():
     in_bytes = xs[0].element_size()
     n_calls = len(xs) * len(w.specs)
     streams = args.streams if args.streams is not None else (1 if n_calls == 1 else 2)
-    run = Runner(fq, torch, dev, xs, w.specs, max(1, streams), 0 if args.no_batch else w.batch)
+    batch = 0 if args.no_batch else (args.batch if args.batch is not None else w.batch)
+    run = Runner(fq, torch, dev, xs, w.specs, max(1, streams), batch)
     n_elem_calls = sum(x.numel() for x in xs) * sum(s.formats for s in w.specs)
     alg_bytes = sum(s.algorithmic_bytes(x.numel(), in_bytes) for x in xs for s in w.specs)
 
@@ -1247,6 +1262,8 @@ def main():
               "arithmetic": "binary32 scales and codes, binary64 error sums"}
     if args.workload == "qwen14model":
         config["layers"] = QWEN14_LAYERS_RUN or 48
+    if run.batch:
+        config["tensors_per_call"] = run.batch
     line = {
         "metric": METRIC,
         "value": round(value, 2),
