@@ -240,3 +240,29 @@ def test_gemm_full_down_projection_sampled():
     print("  case 8192x3584x18944 bf16", flush=True)
     w = wl.qwen7_mlp(1, 1).float().numpy()
     sampled(8192, 3584, 18944, (60, None, 61), 16, torch.bfloat16, w=w)
+
+
+# The bf16 epilogue of the tile kernel converts the very binary32 accumulators
+# the binary32 epilogue stores (two at a time, in hardware), so with one K
+# range bf16 C must be binary32 C rounded to nearest even, bit for bit, at any
+# magnitude.  Each row's scale bytes are a base in 60 .. 175 plus 0 .. 3, so
+# results range from about 2^-130 to 2^110.  Shapes: rows of C in whole
+# 16-byte units (the epilogue through LDS) and not (the element-wise one), one
+# K range each.
+@pytest.mark.parametrize("m,n,k", [(8192, 4096, 1024), (4100, 4500, 544)])
+def test_gemm_bf16_is_the_rounded_f32_result(m, n, k):
+    print(f"  case bf16 vs f32 {m}x{n}x{k}", flush=True)
+    rng = np.random.default_rng([63, m, n, k])
+    ac = t_dev(rng.integers(0, 256, (m, k // 2), dtype=np.uint8))
+    bc = t_dev(rng.integers(0, 256, (n, k // 2), dtype=np.uint8))
+    row_scales = lambda r: (rng.integers(60, 176, (r, 1)) + rng.integers(0, 4, (r, k // 32))).astype(np.uint8)
+    asc, bsc = t_dev(row_scales(m)), t_dev(row_scales(n))
+    f32 = fq.fp4_gemm_mxfp4(ac, asc, bc, bsc, torch.float32)
+    b16 = fq.fp4_gemm_mxfp4(ac, asc, bc, bsc, torch.bfloat16)
+    assert torch.equal(b16.view(torch.int16), f32.bfloat16().view(torch.int16))
+    mag = f32.abs()
+    assert bool(((mag > 0) & (mag < 2.0 ** -60)).any()) and bool((mag > 2.0 ** 60).any())
+
+
+def t_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)

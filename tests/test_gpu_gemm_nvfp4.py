@@ -189,3 +189,21 @@ def test_nv_gemm_full_up_projection_sampled():
     err = np.abs(got[:, cols] - want)
     i = np.unravel_index(np.argmax(err - tol), err.shape)
     assert np.all(err <= tol), f"at {i}: got {got[:, cols][i]!r} want {want[i]!r} tol {tol[i]!r}"
+
+
+# As for the MXFP4 GEMM: with one K range the bf16 epilogue rounds the
+# binary32 result to nearest even, bit for bit (UE4M3 scale bytes over their
+# whole range, given per-tensor scales; K a multiple of 64, as this GEMM takes).
+@pytest.mark.parametrize("m,n,k", [(8192, 4096, 1024), (4100, 4500, 576)])
+def test_nv_gemm_bf16_is_the_rounded_f32_result(m, n, k):
+    print(f"  case nv bf16 vs f32 {m}x{n}x{k}", flush=True)
+    rng = np.random.default_rng([75, m, n, k])
+    ac = t(rng.integers(0, 256, (m, k // 2), dtype=np.uint8))
+    bc = t(rng.integers(0, 256, (n, k // 2), dtype=np.uint8))
+    asc = t(rng.integers(1, 0x7F, (m, k // 16), dtype=np.uint8))
+    bsc = t(rng.integers(1, 0x7F, (n, k // 16), dtype=np.uint8))
+    ga = torch.tensor([0.3], dtype=torch.float32, device=DEV)
+    gb = torch.tensor([1.7], dtype=torch.float32, device=DEV)
+    f32 = fq.fp4_gemm_nvfp4(ac, asc, ga, bc, bsc, gb, torch.float32)
+    b16 = fq.fp4_gemm_nvfp4(ac, asc, ga, bc, bsc, gb, torch.bfloat16)
+    assert torch.equal(b16.view(torch.int16), f32.bfloat16().view(torch.int16))
