@@ -121,7 +121,11 @@ typedef struct {
     double sse_nonmax;     /* sum of squared errors of non-maximum elements */
     double sse_max;        /* sum of squared errors of the block maxima */
     double sse_zero;       /* squared error of zero-rounded blocks (whole blocks) */
-    double sum_x2;         /* sum of x^2 (rotated values when rotating) */
+    double sum_x2;         /* sum of x^2 (rotated values when rotating); within
+                              (4 + log2(b / 8)) 2^-24 of its exact value,
+                              relatively (a quantize pass sums the exact squares
+                              of bf16 input without rotation per block in
+                              binary32) */
     int64_t n_blocks;      /* rows * cols / block */
     int64_t n_zero_blocks; /* number of zero-rounded blocks */
 } fp4q_stats;
@@ -176,8 +180,11 @@ fp4q_status nvfp4_quantize(const void* x, int32_t xt, int64_t rows, int64_t cols
  *   mse_kind   kind of both per-block MSE outputs
  *   ws         fp4q_workspace_bytes() bytes, always needed
  * Every output equals the two separate calls' outputs bit for bit, except the
- * NVFP4 pass's sum_x2 term under FP4Q_MSE_ABS, which is summed in a different
- * order (equal to rounding).  Errors as for the two calls; nothing is launched
+ * NVFP4 pass's sum_x2 term when nv_block_mse is NULL or mse_kind is
+ * FP4Q_MSE_ABS: the separate dynamic call sums it in its amax pass (binary64),
+ * this call in its NVFP4 pass (per block in binary32 for bf16 input, within
+ * (4 + log2(nv_block / 8)) 2^-24 relatively; else binary64, equal to rounding).
+ * Errors as for the two calls; nothing is launched
  * unless both calls' arguments are valid.
  */
 fp4q_status fp4_quantize_mx_nv(const void* x, int32_t xt, int64_t rows, int64_t cols,

@@ -26,7 +26,10 @@
 //   range (the negated remainder keeps the sign of a zero quotient); blocks
 //   whose d or x / d leave the safe range use a plain division.  y is then coded with the same cvt instruction at scale 1.
 //   Errors: e = x - x_hat in binary32 (exact for MXFP4 and for unsaturated
-//   UE4M3 blocks), squared and summed in binary64.  The max-element term is
+//   UE4M3 blocks), squared and summed in binary64.  The sum of squares of x
+//   (relative MSE, tensor term) is binary64 too, except for bf16 values
+//   without rotation: their squares are exact in binary32 and the block's sum
+//   is formed there, within (4 + log2 L) 2^-24 relatively (see sumsq_b32).  The max-element term is
 //   computed from the block maximum m itself (every element attaining m has
 //   the same error).  The non-max term is block SSE minus it when that
 //   difference keeps at least 2^-12 of the SSE (then it is within b 2^-41 of
@@ -168,9 +171,13 @@ constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i within 16
 constexpr uint32_t kRsqrt32Bits = 0x3E3504F3u;  // RN32(2^-2.5)
 
 // ------------------------------------------------------------ lane helpers
+// Every control used here reads a lane of the same row, so the row/bank masks
+// and bound_ctrl never take effect; written as an update with old = 0 and
+// bound_ctrl set, the move folds into the ALU instruction that uses it
+// (v_max_u32_dpp, v_add_f32_dpp) instead of costing one of its own.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 
 template <int CTRL>
@@ -216,6 +223,71 @@ __device__ __forceinline__ double group_sum(double v) {
     if constexpr (L >= 16) v = v + dpp_f64<kRowMirror>(v);
     if constexpr (L >= 32) v = v + __shfl_xor(v, 16);
     return v;
+}
+
+template <int L>
+__device__ __forceinline__ float group_sum_f32(float v) {
+    if constexpr (L >= 2) v = v + dpp_f32<kQuadXor1>(v);
+    if constexpr (L >= 4) v = v + dpp_f32<kQuadXor2>(v);
+    if constexpr (L >= 8) v = v + dpp_f32<kRowHalfMirror>(v);
+    if constexpr (L >= 16) v = v + dpp_f32<kRowMirror>(v);
+    if constexpr (L >= 32) v = v + __shfl_xor(v, 16);
+    return v;
+}
+
+// A block's sum of squares (every lane of the block gets it), in binary64:
+// exact squares, rounded only by the sum (relative error about b 2^-53).
+template <int L>
+__device__ __forceinline__ double sumsq_b64(const float (&v)[8]) {
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const double xv = (double)v[i];
+        ss = fma(xv, xv, ss);
+    }
+    return group_sum<L>(ss);
+}
+
+// The same sum for values of 8 significant bits (bf16 inputs, no rotation)
+// whose block maximum m passes sumsq_b32_ok, in binary32 at a third of the
+// instructions.  Each square has at most 16 significant bits, so the products
+// are exact; the lane's two interleaved chains of four (3 roundings each),
+// their sum (1) and the log2 L cross-lane levels round every term at most
+// 4 + log2 L times, so the result is within (4 + log2 L) 2^-24 of the exact
+// sum, relatively (non-negative terms): at most 9 2^-24 = 5.4e-7 for b = 256.
+// The window for m keeps m^2 and the block's sum normal and finite; smaller
+// elements of the block whose squares fall below the normal range add an
+// absolute error of at most 2^-150 each against a sum of at least 2^-100.
+template <int L>
+__device__ __forceinline__ double sumsq_b32(const float (&v)[8]) {
+    float a = v[0] * v[0], b = v[1] * v[1];
+    a = fmaf(v[2], v[2], a);
+    b = fmaf(v[3], v[3], b);
+    a = fmaf(v[4], v[4], a);
+    b = fmaf(v[5], v[5], b);
+    a = fmaf(v[6], v[6], a);
+    b = fmaf(v[7], v[7], b);
+    return (double)group_sum_f32<L>(a + b);
+}
+
+// Block maximum bits (binary32 of |x|) inside [2^-50, 2^60): the binary32 sum
+// of squares applies (zero blocks and every other block take binary64).
+__device__ __forceinline__ bool sumsq_b32_ok(uint32_t mbits) {
+    constexpr uint32_t kLo = 77u << 23, kHi = 187u << 23;  // 2^-50, 2^60
+    return mbits - kLo < kHi - kLo;
+}
+
+// A block's sum of squares as every kernel that forms one takes it (quantize,
+// block MSE, scale search), so that their per-block results agree bit for bit:
+// binary32 (sumsq_b32) for bf16 values without rotation (B32) whose block
+// maximum, with binary32 bits mbits, passes sumsq_b32_ok; binary64 otherwise.
+// The choice is the same on every lane of a block.
+template <int L, bool B32>
+__device__ __forceinline__ double block_sumsq(const float (&v)[8], uint32_t mbits) {
+    if constexpr (B32) {
+        if (sumsq_b32_ok(mbits)) return sumsq_b32<L>(v);
+    }
+    return sumsq_b64<L>(v);
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
@@ -969,13 +1041,9 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
         for (int i = 0; i < 8; ++i) {
             const double e = (double)(v[i] - xh[i]);
             sse = fma(e, e, sse);
-            if constexpr (SUMSQ) {
-                const double xv = (double)v[i];
-                ss = fma(xv, xv, ss);
-            }
         }
         sse = group_sum<L>(sse);
-        if constexpr (SUMSQ) ss = group_sum<L>(ss);
+        if constexpr (SUMSQ) ss = block_sumsq<L, kPackedBf16>(v, mbits);
         if constexpr (PAIR && SEP != kSepFixup) {
             *res = BlockRes{sse, ss, m, xh_m};
             return;
@@ -1144,11 +1212,7 @@ __device__ __forceinline__ void search_chunk(const Raw<XT>& raw, int u, const QO
         }
     }
     double ss = 0.0;
-    if constexpr (SUMSQ) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ss = fma((double)v[i], (double)v[i], ss);
-        ss = group_sum<L>(ss);
-    }
+    if constexpr (SUMSQ) ss = block_sumsq<L, XT == 0 && ROT == 0>(v, __float_as_uint(m));
     const int blk = u * kBlocks + lane / L;
     if constexpr (SEP != kSepFixup) {
         __builtin_amdgcn_raw_buffer_store_b32(best_cw, o.codes, (u * kChunk + lane * kLaneElems) / 2,
@@ -1258,10 +1322,8 @@ __device__ __forceinline__ void quantize_body(const QParams& p) {
         const QOut o = group_outputs<B, kQuantUnroll>(p, c, wr.c1);
         const Rsrc xin = group_input<XT, kQuantUnroll>(p.x, p.n, c, wr.c1);
         const int64_t left = wr.c1 - c;  // wave-uniform
-#if FP4Q_PREFETCH
         Raw<XT> nxt[kQuantUnroll];
         if (i + 1 < wr.n) load_group<XT, kQuantUnroll>(nxt, p.x, p.n, c + wr.step, wr.c1, lane);
-#endif
         if constexpr (kPair) {
             BlockRes r[2];
             quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer, true>(
@@ -1282,12 +1344,8 @@ __device__ __forceinline__ void quantize_body(const QParams& p) {
                             cur[u], u, o, p, ue, lane, gl, acc, xin, u * kChunk * E);
                 }
         }
-#if FP4Q_PREFETCH
 #pragma unroll
         for (int u = 0; u < kQuantUnroll; ++u) cur[u] = nxt[u];
-#else
-        if (i + 1 < wr.n) load_group<XT, kQuantUnroll>(cur, p.x, p.n, c + wr.step, wr.c1, lane);
-#endif
     }
     if constexpr (ERR) {
         // Fix-up pass: only waves that deferred a block's separate non-max sum
@@ -1910,13 +1968,9 @@ __device__ __forceinline__ void mse_chunk(const Raw<XT>& raw, uint32_t cw, uint3
     for (int i = 0; i < 8; ++i) {
         const double e = (double)(v[i] - xh[i]);
         sse = fma(e, e, sse);
-        if constexpr (SUMSQ) {
-            const double xv = (double)v[i];
-            ss = fma(xv, xv, ss);
-        }
     }
     sse = group_sum<L>(sse);
-    if constexpr (SUMSQ) ss = group_sum<L>(ss);
+    if constexpr (SUMSQ) ss = block_sumsq<L, XT == 0 && ROT == 0>(v, __float_as_uint(m));
     any_nz = group_max<L>(any_nz);
 #pragma unroll
     for (int s = 1; s < L; s <<= 1) {

@@ -49,13 +49,19 @@ def check_against_separate(x, nv_block, kind, block_mse=True, stats=True):
         same(v.block_mse, b.block_mse)
     if stats:
         same(m.stats, a.stats)
-        if kind == fq.MSE_REL:
+        if kind == fq.MSE_REL and block_mse:
             same(v.stats, b.stats)
         else:
             sv, sb = fq.stats_dict(v.stats), fq.stats_dict(b.stats)
             for k in ("sse_nonmax", "sse_max", "sse_zero", "n_blocks", "n_zero_blocks"):
                 assert sv[k] == sb[k], k
-            assert abs(sv["sum_x2"] - sb["sum_x2"]) <= 1e-12 * sb["sum_x2"]
+            # Without the relative per-block MSE, the separate dynamic call
+            # sums x^2 in its amax pass (binary64) and the combined call in its
+            # NVFP4 quantize pass.  For bf16 values the quantize pass sums each
+            # block in binary32 (within (4 + log2(b / 8)) 2^-24 of the exact
+            # sum, relatively), else in binary64 like the amax pass.
+            tol = 1e-6 if x.dtype == torch.bfloat16 else 1e-12
+            assert abs(sv["sum_x2"] - sb["sum_x2"]) <= tol * sb["sum_x2"]
     return m, v
 
 
