@@ -89,7 +89,8 @@ extern "C" {
 typedef enum {
     FP4Q_OK = 0,
     FP4Q_ERR_ARG = 1,       /* a required pointer is NULL or an enum is out of range */
-    FP4Q_ERR_SHAPE = 2,     /* negative size, cols % block != 0, bad block/rotation */
+    FP4Q_ERR_SHAPE = 2,     /* negative size, cols % block != 0, bad block/rotation,
+                               more than (2^31 - 1) * 512 elements */
     FP4Q_ERR_ALIGN = 3,     /* a pointer violates the alignment stated below */
     FP4Q_ERR_WORKSPACE = 4, /* ws missing or smaller than fp4q_workspace_bytes() */
     FP4Q_ERR_HIP = 5        /* the HIP runtime reported an error at launch */

@@ -35,6 +35,10 @@ bool valid_block(int32_t b) { return b == 8 || b == 16 || b == 32 || b == 64 || 
 fp4q_status check_shape(const char* fn, int64_t rows, int64_t cols, int32_t block, int32_t rotate) {
     if (rows < 0 || cols < 0) return fail(FP4Q_ERR_SHAPE, "%s: negative size %lld x %lld", fn, (long long)rows, (long long)cols);
     if (rows > 0 && cols > INT64_MAX / rows) return fail(FP4Q_ERR_SHAPE, "%s: rows * cols overflows", fn);
+    // The streaming kernels index 512-element chunks with 32-bit integers.
+    if (rows * cols > (int64_t)INT32_MAX * 512)
+        return fail(FP4Q_ERR_SHAPE, "%s: %lld elements exceed the limit of (2^31 - 1) * 512", fn,
+                    (long long)(rows * cols));
     if (!valid_block(block)) return fail(FP4Q_ERR_SHAPE, "%s: block %d is not one of 8, 16, 32, 64, 128, 256", fn, block);
     if (cols % block != 0) return fail(FP4Q_ERR_SHAPE, "%s: cols %lld is not a multiple of the block %d", fn, (long long)cols, block);
     if (rotate != 0) {

@@ -862,16 +862,58 @@ struct QOut {
     Rsrc codes, scales, mse;
 };
 
+// The quantize loop's chunk arithmetic in 32 bits.  Chunk indices fit 31 bits
+// (the library rejects tensors of more chunks), and the scalar unit has no
+// ordered 64-bit comparison: with 64-bit indices every clip of a group window
+// became VALU compares and moves.  Only a group that reaches the tensor's last
+// chunk (index n_chunks - 1, holding `tail` elements) is short of whole
+// chunks; c < c1 <= n_chunks.
+struct Chunks32 {
+    int n_chunks, tail;
+};
+
+__device__ __forceinline__ Chunks32 chunks32(int64_t n, int64_t n_chunks) {
+    return {(int)n_chunks, (int)(n - (n_chunks - 1) * kChunk)};
+}
+
+template <int U>
+__device__ __forceinline__ int group_elems(int c, int c1, const Chunks32& k) {
+    const int cl = c1 - c < U ? c1 - c : U;
+    return cl * kChunk - (c + cl == k.n_chunks ? kChunk - k.tail : 0);
+}
+
 template <int B, int U>
-__device__ __forceinline__ QOut group_outputs(const QParams& p, int64_t c, int64_t c1) {
-    const int64_t first = c * kChunk;
-    int64_t avail = (c1 - c < U ? c1 - c : U) * kChunk;
-    if (avail > p.n - first) avail = p.n - first;
+__device__ __forceinline__ QOut group_outputs32(const QParams& p, int c, int c1, const Chunks32& k) {
+    const int64_t first = (int64_t)c * kChunk;
+    const int avail = group_elems<U>(c, c1, k);
     QOut o;
     o.codes = make_rsrc(p.codes + first / 2, avail / 2);
     o.scales = make_rsrc(p.scales + first / B, avail / B);
     o.mse = make_rsrc(p.block_mse + first / B, p.block_mse ? avail / B * 4 : 0);
     return o;
+}
+
+template <int XT, int U>
+__device__ __forceinline__ Rsrc group_input32(const void* x, int c, int c1, const Chunks32& k) {
+    constexpr int E = XT == 0 ? 2 : 4;
+    return make_rsrc(static_cast<const char*>(x) + (int64_t)c * kChunk * E,
+                     group_elems<U>(c, c1, k) * E);
+}
+
+template <int XT, int U>
+__device__ __forceinline__ void load_group32(Raw<XT> (&raw)[U], const void* x, int c, int c1,
+                                             const Chunks32& k, int lane) {
+    constexpr int E = XT == 0 ? 2 : 4;
+    const Rsrc r = group_input32<XT, U>(x, c, c1, k);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if constexpr (XT == 0) {
+            raw[u].w = buf_load16(r, u * kChunk * E + lane * 16);
+        } else {
+            raw[u].a = buf_load16(r, u * kChunk * E + lane * 32);
+            raw[u].b = buf_load16(r, u * kChunk * E + lane * 32 + 16);
+        }
+    }
 }
 
 // One lane's raw values of the chunk that starts xoff bytes into window r.
@@ -995,9 +1037,10 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
     float xh[8];
     float xh_m = 0.0f;
     if constexpr (FMT == kFmtMx) {
-        const uint32_t F = mbits >> 23;
-        sbyte = F > 2u ? F - 2u : 0u;
-        const float sc = __uint_as_float(sbyte << 23);
+        // The scale's bits: the exponent field of m, less 2, clamped at 0.
+        const uint32_t sc_bits = __builtin_elementwise_sub_sat(mbits & 0x7F800000u, 2u << 23);
+        sbyte = sc_bits >> 23;
+        const float sc = __uint_as_float(sc_bits);
         if constexpr (kPackedBf16) cw = code_word_bf16(raw.w, sc);
         else cw = code_word_f32(v, sc);
         if constexpr (ERR) {
@@ -1293,10 +1336,12 @@ __device__ __forceinline__ void quantize_body(const QParams& p) {
     const int lane = threadIdx.x % kWave;
     const int gl = lane & (L - 1);
     const WaveRange wr = wave_range<kWaves, kQuantUnroll>(p.n_chunks, p.cpw, p.wg_first, p.wg_count);
+    const Chunks32 ck = chunks32(p.n, p.n_chunks);
+    const int c0 = (int)wr.c0, cstep = (int)wr.step, n_groups = (int)wr.n, c1 = (int)wr.c1;
     // The first group's loads go out before the per-workgroup set-up below, so
     // that set-up overlaps their latency.
     Raw<XT> cur[kQuantUnroll];
-    if (wr.n > 0) load_group<XT, kQuantUnroll>(cur, p.x, p.n, wr.c0, wr.c1, lane);
+    if (n_groups > 0) load_group32<XT, kQuantUnroll>(cur, p.x, c0, c1, ck, lane);
     UeCtx ue{1.0f, 6.0f, 0.0f, 4096.0f, nullptr};
     if constexpr (FMT != kFmtMx) {
         __shared__ float4 s_tab[kUeCodes];
@@ -1318,12 +1363,12 @@ __device__ __forceinline__ void quantize_body(const QParams& p) {
     constexpr int E = XT == 0 ? 2 : 4;
     // Blocks of two or more lanes finish a group's two chunks together.
     constexpr bool kPair = ERR && !SEARCH && L >= 2 && kQuantUnroll == 2;
-    for (int64_t i = 0, c = wr.c0; i < wr.n; ++i, c += wr.step) {
-        const QOut o = group_outputs<B, kQuantUnroll>(p, c, wr.c1);
-        const Rsrc xin = group_input<XT, kQuantUnroll>(p.x, p.n, c, wr.c1);
-        const int64_t left = wr.c1 - c;  // wave-uniform
+    for (int i = 0, c = c0; i < n_groups; ++i, c += cstep) {
+        const QOut o = group_outputs32<B, kQuantUnroll>(p, c, c1, ck);
+        const Rsrc xin = group_input32<XT, kQuantUnroll>(p.x, c, c1, ck);
+        const int left = c1 - c;  // wave-uniform
         Raw<XT> nxt[kQuantUnroll];
-        if (i + 1 < wr.n) load_group<XT, kQuantUnroll>(nxt, p.x, p.n, c + wr.step, wr.c1, lane);
+        if (i + 1 < n_groups) load_group32<XT, kQuantUnroll>(nxt, p.x, c + cstep, c1, ck, lane);
         if constexpr (kPair) {
             BlockRes r[2];
             quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer, true>(
@@ -1351,12 +1396,12 @@ __device__ __forceinline__ void quantize_body(const QParams& p) {
         // Fix-up pass: only waves that deferred a block's separate non-max sum
         // (rare) read their range again.
         if (p.so.stats && __builtin_amdgcn_readfirstlane(acc.fixup)) {
-            for (int64_t i = 0, c = wr.c0; i < wr.n; ++i, c += wr.step) {
+            for (int i = 0, c = c0; i < n_groups; ++i, c += cstep) {
                 Raw<XT> raw[kQuantUnroll];
-                load_group<XT, kQuantUnroll>(raw, p.x, p.n, c, wr.c1, lane);
-                const QOut o = group_outputs<B, kQuantUnroll>(p, c, wr.c1);
-                const Rsrc xin = group_input<XT, kQuantUnroll>(p.x, p.n, c, wr.c1);
-                const int64_t left = wr.c1 - c;
+                load_group32<XT, kQuantUnroll>(raw, p.x, c, c1, ck, lane);
+                const QOut o = group_outputs32<B, kQuantUnroll>(p, c, c1, ck);
+                const Rsrc xin = group_input32<XT, kQuantUnroll>(p.x, c, c1, ck);
+                const int left = c1 - c;
 #pragma unroll
                 for (int u = 0; u < kQuantUnroll; ++u)
                     if (u < left) {

@@ -69,6 +69,7 @@ def test_mxfp4_validation(L):
     assert mx(L, cols=48) == SHAPE and "multiple" in err(L)
     assert mx(L, rows=-1) == SHAPE
     assert mx(L, rows=1 << 62, cols=1 << 10) == SHAPE and "overflow" in err(L)
+    assert mx(L, rows=1 << 31, cols=512) == SHAPE and "limit" in err(L)
     assert mx(L, rot=16) == SHAPE
     assert mx(L, x=A16 + 8) == ALIGN
     assert mx(L, codes=A16b + 4) == ALIGN
