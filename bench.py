@@ -1259,7 +1259,7 @@ def main():
     config = {"workload": w.name, **w.config, "elements_per_step": n_elem_calls,
               "calls": "; ".join(s.describe() for s in w.specs),
               "streams": max(1, streams),
-              "arithmetic": "binary32 scales and codes, binary64 error sums"}
+              "arithmetic": "binary32 scales and codes, binary64 error sums, binary32 block sums of exact squares of x"}
     if args.workload == "qwen14model":
         config["layers"] = QWEN14_LAYERS_RUN or 48
     if run.batch:
