@@ -336,6 +336,20 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;       // raw (stride 0) buffer, 32-bit data format
 constexpr int kDropped = (int)0x80000000;    // an offset past every range: access dropped
 constexpr int kNt = FP4Q_LOAD_NT ? 2 : 0;    // cache policy: nontemporal (read-once data)
+// The NVFP4 pass of a batched combined call sweeps each tensor from its end
+// to its start: the MXFP4 pass before it swept forward, so the part of the
+// tensors still in the last-level cache is their end, which the NVFP4 pass
+// then reads first, before its own output stores can evict it (one box, two
+// interleaved rounds of the 48-layer step: NVFP4 launches 97.7 -> 92.7 us
+// in the one-stream replay, the step 3736 -> 3743 GB/s).
+#ifndef FP4Q_NV_BATCH_CPW
+#define FP4Q_NV_BATCH_CPW -2
+#endif
+// Load policy of the combined calls' MXFP4 pass (see quantize_body): any
+// policy without the nontemporal bit measured the same (SC0, SC1, both).
+#ifndef FP4Q_MX_IN_POL
+#define FP4Q_MX_IN_POL 0
+#endif
 constexpr int kStNt = FP4Q_STORE_NT ? 2 : 0;
 // Store policy of the quantize outputs: UE-scale formats store with the SC1
 // scope bit (interleaved medians on 67.9 M-element NVFP4 launches: 0.6-1.5 us
@@ -1349,7 +1363,7 @@ __device__ __forceinline__ void quantize_body(const QParams& p) {
     // 3662 -> 3733 GB/s; in the one-stream replay the NVFP4 launches went
     // 117 -> 97 us and the MXFP4 ones 110.5 -> 125 us.  (Both passes on the
     // default policy: 3719 GB/s, NVFP4 116 us.)
-    constexpr int kInPol = AMAX ? 0 : kNt;
+    constexpr int kInPol = AMAX ? FP4Q_MX_IN_POL : kNt;
     if (n_groups > 0) load_group32<XT, kQuantUnroll, kInPol>(cur, p.x, c0, c1, ck, lane);
     UeCtx ue{1.0f, 6.0f, 0.0f, 4096.0f, nullptr};
     if constexpr (FMT != kFmtMx) {
@@ -2632,7 +2646,7 @@ int launch_quantize_mx_nv_batch(const QuantJob* mx, const QuantJob* nv, int n, c
     bn.base.mse_kind = nv[0].mse_kind;
     bn.base.fmt = kFmtUe4m3;
     bn.base.max_byte = 0x7E;
-    bn.base.cpw = kQuantCpw;
+    bn.base.cpw = FP4Q_NV_BATCH_CPW;
     bn.base.so.partials = reinterpret_cast<double*>(ws + kWsPartials);
     bn.base.so.stats = nv[0].stats;
     for (int i = 0; i < n; ++i)
