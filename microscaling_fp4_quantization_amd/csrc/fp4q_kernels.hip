@@ -356,6 +356,17 @@ constexpr int kStNt = FP4Q_STORE_NT ? 2 : 0;
 // faster in all three modes); MXFP4 keeps the default (0.5 us slower with it).
 template <int FMT>
 constexpr int quant_store_policy() { return FMT == kFmtMx ? kStNt : 16; }
+// Store policy of the NVFP4 pass of a batched combined call: nontemporal.
+// With SC1 its outputs stayed in the last-level cache and the next call's
+// MXFP4 pass, which reads with the caching policy, ran slower (48-layer step,
+// two interleaved rounds on one box: 3814 -> 4072 GB/s; in the one-stream
+// replay MXFP4 launches 122.6 -> 106.1 us, NVFP4 94.1 -> 96.6 us).  SC1 with
+// NT measured 1.4% below NT alone, SC0 with NT the same, and NT on the MXFP4
+// pass's stores as well 0.6% below.
+#ifndef FP4Q_BATCH_NV_STORE_POL
+#define FP4Q_BATCH_NV_STORE_POL 2
+#endif
+constexpr int kBatchNvStore = FP4Q_BATCH_NV_STORE_POL;
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
@@ -1016,14 +1027,14 @@ struct BlockRes {
 // forms the MSE and tensor terms of both chunks at once; in kSepFixup only
 // lane gl = u adds (the lane finish_pair gives chunk u's block).
 template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ, int SEP = kSepInline,
-          bool PAIR = false>
+          bool PAIR = false, int ST = quant_store_policy<FMT>()>
 __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const QOut& o,
                                                const QParams& p, const UeCtx& ue, int lane,
                                                int gl, Acc& acc, Rsrc xin, int xoff,
                                                BlockRes* res = nullptr) {
     constexpr int L = B / kLaneElems;
     constexpr int kBlocks = kChunk / B;
-    constexpr int kSt = quant_store_policy<FMT>();
+    constexpr int kSt = ST;
     constexpr bool kPackedBf16 = (XT == 0) && (ROT == 0);
     float v[8];
     uint32_t lane_max;
@@ -1152,12 +1163,12 @@ __device__ __forceinline__ void quantize_chunk(const Raw<XT>& raw, int u, const 
 // runs the per-block arithmetic once per two chunks instead of once per chunk
 // on every lane of every block.  Non-max sums that need the separate sum are
 // deferred (kSepDefer).
-template <int FMT, int B, bool SUMSQ>
+template <int FMT, int B, bool SUMSQ, int ST = quant_store_policy<FMT>()>
 __device__ __forceinline__ void finish_pair(const BlockRes (&r)[2], const QOut& o, const QParams& p,
                                             int lane, int gl, Acc& acc) {
     constexpr int L = B / kLaneElems;
     constexpr int kBlocks = kChunk / B;
-    constexpr int kSt = quant_store_policy<FMT>();
+    constexpr int kSt = ST;
     static_assert(L >= 2, "one block per lane needs no pairing");
     const bool second = (gl & 1) != 0;
     const double sse = second ? r[1].sse : r[0].sse;
@@ -1345,7 +1356,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(StatsOut so, int G) {
 #endif
 // The quantize kernel's body.  AMAX: also write the workgroup's max |x|
 // (binary32 bits) to p.amax_out.
-template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ, bool SEARCH, bool AMAX>
+template <int XT, int FMT, int B, int ROT, bool ERR, bool SUMSQ, bool SEARCH, bool AMAX,
+          int ST = quant_store_policy<FMT>()>
 __device__ __forceinline__ void quantize_body(const QParams& p) {
     constexpr int L = B / kLaneElems;
     const int lane = threadIdx.x % kWave;
@@ -1395,12 +1407,12 @@ __device__ __forceinline__ void quantize_body(const QParams& p) {
             load_group32<XT, kQuantUnroll, kInPol>(nxt, p.x, c + cstep, c1, ck, lane);
         if constexpr (kPair) {
             BlockRes r[2];
-            quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer, true>(
+            quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer, true, ST>(
                 cur[0], 0, o, p, ue, lane, gl, acc, xin, 0, &r[0]);
             if (left > 1)
-                quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer, true>(
+                quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer, true, ST>(
                     cur[1], 1, o, p, ue, lane, gl, acc, xin, kChunk * E, &r[1]);
-            if (p.block_mse || p.so.stats) finish_pair<FMT, B, SUMSQ>(r, o, p, lane, gl, acc);
+            if (p.block_mse || p.so.stats) finish_pair<FMT, B, SUMSQ, ST>(r, o, p, lane, gl, acc);
         } else {
 #pragma unroll
             for (int u = 0; u < kQuantUnroll; ++u)
@@ -1409,7 +1421,7 @@ __device__ __forceinline__ void quantize_body(const QParams& p) {
                         search_chunk<XT, FMT, B, ROT, SUMSQ, kSepDefer>(cur[u], u, o, p, ue, lane, gl,
                                                                         acc);
                     else
-                        quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer>(
+                        quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepDefer, false, ST>(
                             cur[u], u, o, p, ue, lane, gl, acc, xin, u * kChunk * E);
                 }
         }
@@ -1433,7 +1445,7 @@ __device__ __forceinline__ void quantize_body(const QParams& p) {
                             search_chunk<XT, FMT, B, ROT, SUMSQ, kSepFixup>(raw[u], u, o, p, ue, lane,
                                                                             gl, acc);
                         else
-                            quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepFixup, kPair>(
+                            quantize_chunk<XT, FMT, B, ROT, ERR, SUMSQ, kSepFixup, kPair, ST>(
                                 raw[u], u, o, p, ue, lane, gl, acc, xin, u * kChunk * E);
                     }
             }
@@ -1516,7 +1528,10 @@ __device__ __forceinline__ void batch_body(const BatchParams& bp) {
     p.g_in = s.g_in;
     p.wg_first = s.wg_first;
     p.wg_count = s.wg_count;
-    quantize_body<XT, FMT, B, 0, ERR, SUMSQ, false, FMT == kFmtMx>(p);
+    // The NVFP4 pass of a batched combined call stores its outputs with the
+    // nontemporal bit (see kBatchNvStore).
+    quantize_body<XT, FMT, B, 0, ERR, SUMSQ, false, FMT == kFmtMx,
+                  FMT == kFmtMx ? quant_store_policy<FMT>() : kBatchNvStore>(p);
 }
 
 // The MXFP4 pass of a batch (per-workgroup maxima for the NVFP4 scales).
