@@ -1479,6 +1479,19 @@ FP4Q_SGPR_CAP void k_quantize(QParams p) {
     quantize_body<XT, FMT, B, ROT, ERR, SUMSQ, SEARCH, false>(p);
 }
 
+// The NVFP4 pass of fp4_quantize_mx_nv (UE4M3, no rotation): k_quantize with
+// the nontemporal stores of the batched NVFP4 pass (kBatchNvStore), launched on
+// the plain kernel's grid so that its tensor terms are summed in the same
+// order as a separate nvfp4_quantize call's.
+template <int XT, int B, bool ERR, bool SUMSQ>
+__global__ __launch_bounds__(kThreads)
+#if FP4Q_QUANT_WPE
+__attribute__((amdgpu_waves_per_eu(FP4Q_QUANT_WPE)))
+#endif
+FP4Q_SGPR_CAP void k_quantize_nv_pair(QParams p) {
+    quantize_body<XT, kFmtUe4m3, B, 0, ERR, SUMSQ, false, false, kBatchNvStore>(p);
+}
+
 // The MXFP4 pass of fp4_quantize_mx_nv (no rotation): k_quantize plus the
 // per-workgroup maxima.  Held to 8 waves per SIMD (64 VGPRs), the occupancy
 // of the plain MXFP4 kernel, whose grid it takes (so its tensor terms are
@@ -2297,6 +2310,24 @@ QuantKernel pick_quant_block(int block, int rotate, bool err, bool sumsq, bool s
     }
 }
 
+template <int XT, int B>
+QuantKernel pick_nv_pair(bool err, bool sumsq) {
+    if (!err) return k_quantize_nv_pair<XT, B, false, false>;
+    return sumsq ? k_quantize_nv_pair<XT, B, true, true> : k_quantize_nv_pair<XT, B, true, false>;
+}
+
+template <int XT>
+QuantKernel pick_nv_pair_block(int block, bool err, bool sumsq) {
+    switch (block) {
+        case 8: return pick_nv_pair<XT, 8>(err, sumsq);
+        case 16: return pick_nv_pair<XT, 16>(err, sumsq);
+        case 32: return pick_nv_pair<XT, 32>(err, sumsq);
+        case 64: return pick_nv_pair<XT, 64>(err, sumsq);
+        case 128: return pick_nv_pair<XT, 128>(err, sumsq);
+        default: return pick_nv_pair<XT, 256>(err, sumsq);
+    }
+}
+
 typedef void (*RowKernel)(RowParams);
 
 template <int XT, int B, int ROT>
@@ -2521,6 +2552,9 @@ int launch_quantize(const QuantJob& j, char* msg, size_t msg_len) {
         !amax ? k
               : (j.xt == 0 ? pick_quant_block<0, kFmtMx>(32, j.rotate, err, sumsq, search)
                            : pick_quant_block<1, kFmtMx>(32, j.rotate, err, sumsq, search));
+    if (j.nv_of_pair && j.fmt == kFmtUe4m3 && j.rotate == 0 && !search)
+        k = j.xt == 0 ? pick_nv_pair_block<0>(j.block, err, sumsq)
+                      : pick_nv_pair_block<1>(j.block, err, sumsq);
     const Split sq = split_for(chunks, reinterpret_cast<const void*>(k_grid),
                                light ? kQuantCpwLight : kQuantCpw);
     const int G = sq.G;
@@ -2703,6 +2737,7 @@ int launch_quantize_mx_nv(const QuantJob& mx, const QuantJob& nv, char* msg, siz
     if (rc) return rc;
     QuantJob b = nv;
     b.gmode = 2;
+    b.nv_of_pair = true;
     return launch_quantize(b, msg, msg_len);
 }
 

@@ -42,6 +42,8 @@ struct QuantJob {
     // kernel turns them into the NVFP4 per-tensor scale at g_from_amax.
     uint32_t* amax_out = nullptr;
     float* g_from_amax = nullptr;
+    // NVFP4 pass of fp4_quantize_mx_nv: stores with the nontemporal bit.
+    bool nv_of_pair = false;
 };
 
 struct DequantJob {
